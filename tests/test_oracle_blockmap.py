@@ -1,0 +1,116 @@
+"""Pins for the brute-force block map and visible-pair counts (CPU only)."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle.attention import CAUSAL, WINDOW, DOCUMENT
+from oracle.blockmap import EMPTY, PARTIAL, FULL
+
+
+def _loop_blockmap(N, flags, W, doc, block):
+    """Scalar re-derivation with explicit per-position loops (tiny sizes only)."""
+    def vis(q, k):
+        ok = True
+        if flags & CAUSAL:
+            ok &= k <= q
+        if flags & WINDOW:
+            ok &= abs(q - k) < W
+        if flags & DOCUMENT:
+            ok &= doc[q] == doc[k]
+        return ok
+    nb = -(-N // block)
+    cls = np.zeros((nb, nb), np.uint8)
+    for qb in range(nb):
+        for kb in range(nb):
+            seen = [vis(q, k) for q in range(qb * block, min(N, qb * block + block))
+                    for k in range(kb * block, min(N, kb * block + block))]
+            inside = len(seen) == block * block
+            cls[qb, kb] = EMPTY if not any(seen) else (FULL if all(seen) and inside else PARTIAL)
+    return cls
+
+
+@pytest.mark.parametrize("N,flags,W", [(10, CAUSAL, 0), (9, 0, 0), (13, CAUSAL | WINDOW, 3), (12, WINDOW, 2),
+                                       (11, DOCUMENT, 0), (16, CAUSAL | DOCUMENT, 0),
+                                       (17, CAUSAL | WINDOW | DOCUMENT, 4)])
+def test_blockmap_matches_scalar_loops(N, flags, W):
+    doc = np.repeat(np.arange(4), [3, 5, 1, 100])[:N].astype(np.int32)
+    m = O.blockmap_ref(1, N, flags, W, doc[None], block=4)
+    cls = _loop_blockmap(N, flags, W, doc, 4)
+    np.testing.assert_array_equal(m["cls"][0], cls)
+    for qb in range(cls.shape[0]):
+        full = [kb for kb in range(cls.shape[1]) if cls[qb, kb] == FULL]
+        part = [kb for kb in range(cls.shape[1]) if cls[qb, kb] == PARTIAL]
+        assert list(m["counts"][0, qb]) == [len(full), len(part)]
+        row = m["idx"][0, qb]
+        assert list(row[0]) == full + [-1] * (cls.shape[1] - len(full))
+        assert list(row[1]) == part + [-1] * (cls.shape[1] - len(part))
+
+
+@pytest.mark.parametrize("nqb", [1, 2, 5, 16])
+def test_causal_closed_form_counts(nqb):
+    N = 128 * nqb
+    m = O.blockmap_ref(2, N, CAUSAL)
+    for b in range(2):
+        assert (m["cls"][b] == PARTIAL).sum() == nqb
+        assert (m["cls"][b] == FULL).sum() == nqb * (nqb - 1) // 2
+        assert np.array_equal(np.diag(m["cls"][b]), np.full(nqb, PARTIAL))
+    assert m["visible_pairs"] == 2 * N * (N + 1) // 2
+
+
+def test_causal_window_closed_form_counts():
+    """Causal + window 1024 over 8192 tokens: per batch row 420 FULL and 120
+    PARTIAL blocks; visible pairs W(W+1)/2 + (N-W)W."""
+    N, W = 8192, 1024
+    m = O.blockmap_ref(1, N, CAUSAL | WINDOW, W)
+    assert (m["cls"] == FULL).sum() == 420
+    assert (m["cls"] == PARTIAL).sum() == 120
+    assert m["visible_pairs"] == W * (W + 1) // 2 + (N - W) * W
+
+
+def test_noncausal_all_full_and_tail_partial():
+    m = O.blockmap_ref(1, 1024, 0)
+    assert (m["cls"] == FULL).all()
+    m = O.blockmap_ref(1, 300, 0)
+    assert m["cls"][0, 0, 0] == FULL and m["cls"][0, 0, 2] == PARTIAL and m["cls"][0, 2, 0] == PARTIAL
+    assert m["visible_pairs"] == 300 * 300
+
+
+def test_pair_count_consistent_with_classes():
+    """#visible = 128*128*#FULL + visible pairs inside PARTIAL blocks."""
+    rng = np.random.default_rng(0)
+    N = 1000
+    lengths = [137, 300, 1, 262, 300]
+    doc = np.repeat(np.arange(5), lengths).astype(np.int32)[None]
+    for flags, W in ((CAUSAL, 0), (CAUSAL | WINDOW, 200), (CAUSAL | DOCUMENT, 0), (DOCUMENT, 0), (WINDOW, 77)):
+        m = O.blockmap_ref(1, N, flags, W, doc)
+        vis = O.visible(np.arange(N), np.arange(N), flags, W, doc[0])
+        part = 0
+        for qb, kb in zip(*np.nonzero(m["cls"][0] == PARTIAL)):
+            part += vis[qb * 128:(qb + 1) * 128, kb * 128:(kb + 1) * 128].sum()
+        assert m["visible_pairs"] == 128 * 128 * (m["cls"] == FULL).sum() + part
+        assert m["visible_pairs"] == O.visible_pairs_ref(1, N, flags, W, doc)
+
+
+def test_row_intervals_closed_forms():
+    N, W = 500, 64
+    m = O.blockmap_ref(1, N, CAUSAL)
+    assert np.array_equal(m["row_lo"][0], np.zeros(N)) and np.array_equal(m["row_hi"][0], np.arange(N))
+    m = O.blockmap_ref(1, N, CAUSAL | WINDOW, W)
+    assert np.array_equal(m["row_lo"][0], np.maximum(0, np.arange(N) - W + 1))
+    m = O.blockmap_ref(1, N, WINDOW, W)
+    assert np.array_equal(m["row_hi"][0], np.minimum(N - 1, np.arange(N) + W - 1))
+    lengths = [100, 250, 150]
+    starts = np.repeat(np.cumsum([0] + lengths[:-1]), lengths)
+    ends = np.repeat(np.cumsum(lengths) - 1, lengths)
+    doc = np.repeat(np.arange(3), lengths).astype(np.int32)[None]
+    m = O.blockmap_ref(1, N, DOCUMENT, 0, doc)
+    assert np.array_equal(m["row_lo"][0], starts) and np.array_equal(m["row_hi"][0], ends)
+    m = O.blockmap_ref(1, N, DOCUMENT | CAUSAL, 0, doc)
+    assert np.array_equal(m["row_lo"][0], starts) and np.array_equal(m["row_hi"][0], np.arange(N))
+    lo, hi, contiguous = O.row_intervals_ref(N, DOCUMENT | CAUSAL | WINDOW, 30, doc[0])
+    assert contiguous
+    assert np.array_equal(lo, np.maximum(starts, np.arange(N) - 29)) and np.array_equal(hi, np.arange(N))
+    # non-contiguous documents are not intervals
+    _, _, contiguous = O.row_intervals_ref(6, DOCUMENT, 0, np.array([0, 1, 0, 1, 0, 1]))
+    assert not contiguous
