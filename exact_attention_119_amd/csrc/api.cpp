@@ -1,0 +1,218 @@
+// C ABI of libattn119.so: argument validation, block-map entry points and the
+// dispatch of the forward pass to its compiled variants.  Declarations and the
+// full contract are in include/attn119.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn119.h"
+#include "common.hpp"
+#include "fwd_args.hpp"
+
+namespace attn119 {
+hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
+                           const int32_t* doc_id, hipStream_t stream);
+template <int D, int IN>
+hipError_t launch_fwd_family(const FwdArgs& a, bool masked, bool alibi, bool softcap, hipStream_t st);
+constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
+}  // namespace attn119
+
+using namespace attn119;
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr uint32_t kAllFlags = ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT | ATTN_ALIBI | ATTN_SOFTCAP;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool positional(const attn_mask* m) { return m && (m->flags & (ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT)); }
+
+attn_status check_mask(const attn_mask* m) {
+  if (!m) return ATTN_OK;
+  if (m->flags & ~kAllFlags) return ATTN_ERR_UNSUPPORTED;
+  if ((m->flags & ATTN_WINDOW) && m->window < 1) return ATTN_ERR_INVALID_ARG;
+  if (m->flags & ATTN_SOFTCAP) {
+    if (!(m->softcap > 0.f) || !std::isfinite(m->softcap)) return ATTN_ERR_INVALID_ARG;
+  }
+  if ((m->flags & ATTN_DOCUMENT) && !m->doc_id) return ATTN_ERR_INVALID_ARG;
+  if (m->doc_id && !aligned16(m->doc_id) && (m->flags & ATTN_DOCUMENT)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn_status check_shape(int32_t B, int32_t N) {
+  if (B < 1 || N < 1) return ATTN_ERR_INVALID_ARG;
+  // every int offset the kernels form must stay below 2^31
+  const int64_t nb = (N + 127) / 128;
+  if ((int64_t)B * N > (int64_t)INT32_MAX || (int64_t)B * nb * nb > (int64_t)INT32_MAX)
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int32_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype, flag or pv mode";
+    case ATTN_ERR_BAD_BLOCKMAP: return "block map missing or of the wrong size";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_BAD_DOC_ID: return "doc_id decreases (documents must be contiguous)";
+    default: return "unknown status";
+  }
+}
+
+attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* layout) {
+  if (!layout) return ATTN_ERR_INVALID_ARG;
+  const attn_status st = check_shape(B, N);
+  if (st != ATTN_OK) return st;
+  const MapLayout m = map_layout(B, N);
+  layout->cls = m.cls;
+  layout->counts = m.counts;
+  layout->idx = m.idx;
+  layout->row_lo = m.row_lo;
+  layout->row_hi = m.row_hi;
+  layout->pairs = m.pairs;
+  layout->status = m.status;
+  layout->total = m.total;
+  return ATTN_OK;
+}
+
+attn_status attn_blockmap_bytes(int32_t B, int32_t N, const attn_mask* mask, size_t* bytes) {
+  if (!bytes) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_shape(B, N);
+  if (st != ATTN_OK) return st;
+  st = check_mask(mask);
+  if (st != ATTN_OK) return st;
+  *bytes = map_layout(B, N).total;
+  return ATTN_OK;
+}
+
+attn_status attn_blockmap_build(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes,
+                                void* stream) {
+  size_t need = 0;
+  attn_status st = attn_blockmap_bytes(B, N, mask, &need);
+  if (st != ATTN_OK) return st;
+  if (!map || !aligned16(map)) return ATTN_ERR_INVALID_ARG;
+  if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
+  const uint32_t flags = mask ? mask->flags : 0u;
+  const int window = (mask && (flags & ATTN_WINDOW)) ? mask->window : 0;
+  const int32_t* doc = (mask && (flags & ATTN_DOCUMENT)) ? mask->doc_id : nullptr;
+  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
+  if (!map || bytes < 256) return ATTN_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
+  MapHeader hd;
+  if (hipMemcpy(&hd, map, sizeof(hd), hipMemcpyDeviceToHost) != hipSuccess) return ATTN_ERR_HIP;
+  if (hd.magic != kMapMagic || check_shape(hd.B, hd.N) != ATTN_OK) return ATTN_ERR_BAD_BLOCKMAP;
+  const MapLayout m = map_layout(hd.B, hd.N);
+  if (bytes != m.total) return ATTN_ERR_BAD_BLOCKMAP;
+  const size_t n = (size_t)hd.B * hd.nqb;
+  int32_t* st = new int32_t[n];
+  const hipError_t e = hipMemcpy(st, (const unsigned char*)map + m.status, n * 4, hipMemcpyDeviceToHost);
+  int bad = 0;
+  for (size_t i = 0; i < n; ++i) bad |= st[i];
+  delete[] st;
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  return bad ? ATTN_ERR_BAD_DOC_ID : ATTN_OK;
+}
+
+attn_status attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                            int32_t H, int32_t N, int32_t d, float scale, int32_t dtype,
+                            const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                            const attn_fp8* fp8, float rescale_tau) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (H < 1) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_shape(B, N);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)B * H > (int64_t)INT32_MAX / ((N + 127) / 128) ||
+      (int64_t)B * H * N > (int64_t)INT32_MAX * 8)
+    return ATTN_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!(rescale_tau >= 0.f && rescale_tau <= 8.f)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  st = check_mask(mask);
+  if (st != ATTN_OK) return st;
+  if (mask && (mask->flags & ATTN_ALIBI) && mask->alibi_slopes && !aligned16(mask->alibi_slopes))
+    return ATTN_ERR_INVALID_ARG;
+  if (dtype == ATTN_FP8_E4M3) {
+    if (!fp8 || !fp8->q_scale || !fp8->k_scale || !fp8->v_scale) return ATTN_ERR_INVALID_ARG;
+    if (fp8->pv_mode != ATTN_PV_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (fp8->qk_mode != ATTN_QK_BF16 && fp8->qk_mode != ATTN_QK_E4M3) return ATTN_ERR_UNSUPPORTED;
+  }
+  if (positional(mask)) {
+    if (!blockmap || !aligned16(blockmap)) return ATTN_ERR_BAD_BLOCKMAP;
+    if (blockmap_bytes != map_layout(B, N).total) return ATTN_ERR_BAD_BLOCKMAP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
+                     int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
+                     const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
+                     void* stream) {
+  const attn_status st = attn_check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, mask, blockmap,
+                                         blockmap_bytes, fp8, rescale_tau);
+  if (st != ATTN_OK) return st;
+  const uint32_t flags = mask ? mask->flags : 0u;
+  const bool masked = positional(mask);
+  const bool alibi = flags & ATTN_ALIBI;
+  const bool softcap = flags & ATTN_SOFTCAP;
+
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.nqb = (N + 127) / 128;
+  a.c = (float)((double)scale * kLog2e);
+  if (softcap) {
+    a.sc2 = (float)(2.0 * (double)scale * kLog2e / (double)mask->softcap);
+    a.cap2 = (float)((double)mask->softcap * kLog2e);
+  }
+  a.tau = rescale_tau;
+  a.alibi_exp = (float)(-8.0 / (double)H);
+  a.alibi_slopes = (alibi && mask) ? mask->alibi_slopes : nullptr;
+  if (dtype == ATTN_FP8_E4M3) {
+    a.q_scale = fp8->q_scale;
+    a.k_scale = fp8->k_scale;
+    a.v_scale = fp8->v_scale;
+  }
+  if (masked) {
+    a.map = (const unsigned char*)blockmap;
+    a.lay = map_layout(B, N);
+    a.mflags = flags & (ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT);
+    a.window = (flags & ATTN_WINDOW) ? mask->window : 0;
+  }
+  hipError_t e;
+  const hipStream_t s = (hipStream_t)stream;
+  if (dtype == ATTN_BF16)
+    e = d == 128 ? launch_fwd_family<128, kInBf16>(a, masked, alibi, softcap, s)
+                 : launch_fwd_family<64, kInBf16>(a, masked, alibi, softcap, s);
+  else if (fp8->qk_mode == ATTN_QK_BF16)
+    e = d == 128 ? launch_fwd_family<128, kInFp8>(a, masked, alibi, softcap, s)
+                 : launch_fwd_family<64, kInFp8>(a, masked, alibi, softcap, s);
+  else
+    e = d == 128 ? launch_fwd_family<128, kInFp8Qk8>(a, masked, alibi, softcap, s)
+                 : launch_fwd_family<64, kInFp8Qk8>(a, masked, alibi, softcap, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Block-map builder for the fused attention forward pass (gfx950).
+//
+// Block sparsity -- skipping blocks the mask hides completely -- is named in
+// "PyTorchs FlexAttention mit FlashAttention-4 ist ein Game-Changer" (liora.io),
+// section "Aktuelle Einschränkungen".  Every mask this library supports (causal,
+// sliding window, document with contiguous documents, and their conjunctions)
+// leaves each query row a single interval of visible keys [row_lo, row_hi], so
+// the map is built from those intervals:
+//   pass 1 (one thread per query row): the interval, and a flag for any place
+//          where doc_id decreases (documents must be contiguous runs);
+//          and per query block a status word: 1 if doc_id decreases at one of
+//          its rows (a batch row with any such word is invalid);
+//   pass 2 (one workgroup per 128-query block): the class of every 128x128
+//          block, the ascending lists of FULL and PARTIAL key blocks and the
+//          visible-pair count of the query block.
+// No atomics, no memset: every byte of every section is written, so the result is
+// byte-identical for equal inputs and the calls are safe to capture in a graph.
+#include "common.hpp"
+
+namespace attn119 {
+
+struct MapArgs {
+  unsigned char* map;
+  MapLayout lay;
+  const int32_t* doc_id;
+  int B, N, nb;
+  uint32_t flags;  // positional flags only
+  int window;
+};
+
+// First index i in [0, N) with row[i] >= v (row non-decreasing).
+__device__ inline int lower_bound_i32(const int32_t* row, int N, int v) {
+  int lo = 0, hi = N;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(256) blockmap_rows_kernel(MapArgs a) {
+  const int b = blockIdx.y;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  const int N = a.N;
+  int32_t* row_lo = (int32_t*)(a.map + a.lay.row_lo) + (size_t)b * N;
+  int32_t* row_hi = (int32_t*)(a.map + a.lay.row_hi) + (size_t)b * N;
+  int bad = 0;
+  if (q < N) {
+    int lo = 0, hi = N - 1;
+    if (a.flags & kCausal) hi = q;
+    if (a.flags & kWindow) {
+      lo = max(lo, q - (a.window - 1));
+      if (!(a.flags & kCausal)) hi = min(hi, q + (a.window - 1));
+    }
+    if (a.flags & kDocument) {
+      const int32_t* drow = a.doc_id + (size_t)b * N;
+      const int dq = drow[q];
+      if (q + 1 < N && drow[q + 1] < dq) bad = 1;
+      const int first = lower_bound_i32(drow, N, dq);
+      const int last = (dq == INT32_MAX) ? N - 1 : lower_bound_i32(drow, N, dq + 1) - 1;
+      lo = max(lo, first);
+      hi = min(hi, last);
+    }
+    if (hi < lo) { lo = 0; hi = -1; }
+    row_lo[q] = lo;
+    row_hi[q] = hi;
+  }
+  // Status word of each of the (up to) two query blocks this workgroup covers:
+  // 1 if doc_id decreases between one of its rows and the next row.
+  const int bad0 = __syncthreads_or(bad && threadIdx.x < kBlock);
+  const int bad1 = __syncthreads_or(bad && threadIdx.x >= kBlock);
+  if (threadIdx.x == 0) {
+    int32_t* st = (int32_t*)(a.map + a.lay.status) + (size_t)b * a.nb;
+    const int qb = 2 * blockIdx.x;
+    st[qb] = bad0 ? 1 : 0;
+    if (qb + 1 < a.nb) st[qb + 1] = bad1 ? 1 : 0;
+  }
+}
+
+// One workgroup (256 threads, 4 waves) per (query block, batch row).
+__global__ void __launch_bounds__(256) blockmap_blocks_kernel(MapArgs a) {
+  const int qb = blockIdx.x, b = blockIdx.y;
+  const int N = a.N, nb = a.nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* row_lo = (const int32_t*)(a.map + a.lay.row_lo) + (size_t)b * N;
+  const int32_t* row_hi = (const int32_t*)(a.map + a.lay.row_hi) + (size_t)b * N;
+  const int q0 = qb * kBlock, q1 = min(N, q0 + kBlock);
+  const int nrows = q1 - q0;
+
+  __shared__ int s_lo[kBlock], s_hi[kBlock];
+  __shared__ int s_wave_full[4], s_wave_part[4];
+  __shared__ long long s_pairs[4];
+  if (tid < kBlock) {
+    s_lo[tid] = tid < nrows ? row_lo[q0 + tid] : 0;
+    s_hi[tid] = tid < nrows ? row_hi[q0 + tid] : -1;
+  }
+  __syncthreads();
+
+  // visible pairs of this query block
+  long long my_pairs = 0;
+  if (tid < kBlock) my_pairs = (long long)max(0, s_hi[tid] - s_lo[tid] + 1);
+  for (int off = 32; off > 0; off >>= 1) my_pairs += __shfl_xor(my_pairs, off);
+  if (lane == 0) s_pairs[wave] = my_pairs;
+  __syncthreads();
+
+  unsigned char* cls = a.map + a.lay.cls + ((size_t)b * nb + qb) * nb;
+  int32_t* idx_full = (int32_t*)(a.map + a.lay.idx) + ((size_t)b * nb + qb) * 2 * nb;
+  int32_t* idx_part = idx_full + nb;
+
+  // classes and ascending CSR lists, 256 key blocks per round (64 per wave)
+  int full_base = 0, part_base = 0;
+  for (int kb0 = 0; kb0 < nb; kb0 += 256) {
+    const int kb = kb0 + tid;
+    int c = 0;
+    if (kb < nb) {
+      const int k0 = kb * kBlock, k1 = min(N, k0 + kBlock) - 1;
+      const bool whole = (nrows == kBlock) && (k1 - k0 + 1 == kBlock);
+      bool any = false, all = whole;
+      for (int r = 0; r < nrows; ++r) {
+        const int lo = s_lo[r], hi = s_hi[r];
+        any |= (max(lo, k0) <= min(hi, k1));
+        all &= (lo <= k0) && (hi >= k1);
+      }
+      c = !any ? 0 : (all ? 2 : 1);
+      cls[kb] = (unsigned char)c;
+    }
+    const uint64_t mfull = __ballot(c == 2);
+    const uint64_t mpart = __ballot(c == 1);
+    if (lane == 0) {
+      s_wave_full[wave] = __popcll(mfull);
+      s_wave_part[wave] = __popcll(mpart);
+    }
+    __syncthreads();
+    int fb = full_base, pbase = part_base;
+    for (int w = 0; w < wave; ++w) { fb += s_wave_full[w]; pbase += s_wave_part[w]; }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (c == 2) idx_full[fb + __popcll(mfull & below)] = kb;
+    if (c == 1) idx_part[pbase + __popcll(mpart & below)] = kb;
+    for (int w = 0; w < 4; ++w) { full_base += s_wave_full[w]; part_base += s_wave_part[w]; }
+    __syncthreads();
+  }
+  for (int i = full_base + tid; i < nb; i += 256) idx_full[i] = -1;
+  for (int i = part_base + tid; i < nb; i += 256) idx_part[i] = -1;
+  if (tid == 0 && b == 0 && qb == 0) {
+    MapHeader* hd = (MapHeader*)a.map;
+    hd->magic = kMapMagic;
+    hd->B = a.B;
+    hd->N = a.N;
+    hd->nqb = nb;
+    hd->nkb = nb;
+    hd->flags = a.flags;
+    hd->window = a.window;
+    for (int i = 0; i < 9; ++i) hd->reserved[i] = 0;
+  }
+  if (tid == 0) {
+    int32_t* counts = (int32_t*)(a.map + a.lay.counts) + ((size_t)b * nb + qb) * 2;
+    counts[0] = full_base;
+    counts[1] = part_base;
+    long long* pairs = (long long*)(a.map + a.lay.pairs) + (size_t)b * nb + qb;
+    *pairs = s_pairs[0] + s_pairs[1] + s_pairs[2] + s_pairs[3];
+  }
+}
+
+hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
+                           const int32_t* doc_id, hipStream_t stream) {
+  MapArgs a;
+  a.map = map;
+  a.lay = map_layout(B, N);
+  a.doc_id = doc_id;
+  a.B = B;
+  a.N = N;
+  a.nb = (N + kBlock - 1) / kBlock;
+  a.flags = flags & kPositional;
+  a.window = window;
+  hipLaunchKernelGGL(blockmap_rows_kernel, dim3((N + 255) / 256, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(blockmap_blocks_kernel, dim3(a.nb, B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn119

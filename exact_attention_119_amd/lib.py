@@ -1,0 +1,194 @@
+"""ctypes binding of libattn119.so -- argument marshalling only.
+
+The functions carry the C names of include/attn119.h.  Tensors are torch tensors
+on the current HIP device (torch supplies device memory and streams); every step
+of the computation runs in the library's HIP kernels.  There is no fallback: if
+the library is not built, load() raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn119.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_BAD_BLOCKMAP = -3
+ATTN_ERR_HIP = -4
+ATTN_ERR_BAD_DOC_ID = -5
+
+ATTN_BF16 = 0
+ATTN_FP8_E4M3 = 1
+
+ATTN_CAUSAL = 1
+ATTN_WINDOW = 2
+ATTN_DOCUMENT = 4
+ATTN_ALIBI = 8
+ATTN_SOFTCAP = 16
+POSITIONAL = ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT
+
+ATTN_PV_BF16 = 0
+ATTN_PV_E4M3 = 1
+
+ATTN_QK_BF16 = 0
+ATTN_QK_E4M3 = 1
+
+EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
+           "attn_blockmap_status", "attn_check_args", "attn_fwd", "attn_status_str")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class attn_mask(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("window", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("doc_id", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p)]
+
+
+class attn_fp8(ctypes.Structure):
+    _fields_ = [("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("pv_mode", ctypes.c_int32), ("qk_mode", ctypes.c_int32)]
+
+
+class attn_blockmap_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status",
+                                               "total")]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the built library (once) and declares its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m exact_attention_119_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.attn_status_str.argtypes = [i32]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_blockmap_bytes.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(sz)]
+    lib.attn_blockmap_bytes.restype = i32
+    lib.attn_blockmap_layout_of.argtypes = [i32, i32, ctypes.POINTER(attn_blockmap_layout)]
+    lib.attn_blockmap_layout_of.restype = i32
+    lib.attn_blockmap_build.argtypes = [i32, i32, ctypes.POINTER(attn_mask), vp, sz, vp]
+    lib.attn_blockmap_build.restype = i32
+    lib.attn_blockmap_status.argtypes = [vp, sz, vp]
+    lib.attn_blockmap_status.restype = i32
+    lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
+                                    vp, sz, ctypes.POINTER(attn_fp8), f32]
+    lib.attn_check_args.restype = i32
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask), vp, sz,
+                             ctypes.POINTER(attn_fp8), f32, vp]
+    lib.attn_fwd.restype = i32
+    _LIB = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().attn_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_mask(flags: int = 0, window: int = 0, softcap: float = 0.0, doc_id=None, alibi_slopes=None):
+    return attn_mask(int(flags), int(window), float(softcap), _ptr(doc_id), _ptr(alibi_slopes))
+
+
+def make_fp8(q_scale, k_scale, v_scale, pv_mode: int = ATTN_PV_BF16, qk_mode: int = ATTN_QK_BF16):
+    return attn_fp8(_ptr(q_scale), _ptr(k_scale), _ptr(v_scale), int(pv_mode), int(qk_mode))
+
+
+def attn_blockmap_bytes(B: int, N: int, mask: Optional[attn_mask] = None) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().attn_blockmap_bytes(B, N, ctypes.byref(mask) if mask else None, ctypes.byref(out)),
+           "attn_blockmap_bytes")
+    return out.value
+
+
+def attn_blockmap_layout_of(B: int, N: int) -> dict:
+    lay = attn_blockmap_layout()
+    _check(load().attn_blockmap_layout_of(B, N, ctypes.byref(lay)), "attn_blockmap_layout_of")
+    return {n: getattr(lay, n) for n, _ in attn_blockmap_layout._fields_}
+
+
+def attn_blockmap_build(B: int, N: int, mask: Optional[attn_mask], blockmap, stream=None) -> None:
+    """Builds the block map into the uint8 device tensor `blockmap`."""
+    _check(load().attn_blockmap_build(B, N, ctypes.byref(mask) if mask else None, _ptr(blockmap),
+                                      blockmap.numel() * blockmap.element_size(), _stream(stream)),
+           "attn_blockmap_build")
+
+
+def attn_blockmap_status(blockmap, stream=None) -> int:
+    return load().attn_blockmap_status(_ptr(blockmap), blockmap.numel() * blockmap.element_size(),
+                                       _stream(stream))
+
+
+def attn_check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, mask=None, blockmap=None, blockmap_bytes=0,
+                    fp8=None, rescale_tau=8.0) -> int:
+    """Host-side validation; pointers may be plain integers (no GPU needed)."""
+    return load().attn_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                  int(dtype), ctypes.byref(mask) if mask else None, _ptr(blockmap),
+                                  int(blockmap_bytes), ctypes.byref(fp8) if fp8 else None, float(rescale_tau))
+
+
+def attn_fwd(q, k, v, o, lse, *, scale: float, dtype: int = ATTN_BF16, mask: Optional[attn_mask] = None,
+             blockmap=None, fp8: Optional[attn_fp8] = None, rescale_tau: float = 8.0, stream=None) -> None:
+    """Enqueues the forward pass.  q, k, v, o: [B][H][N][d] device tensors; lse: [B][H][N] fp32."""
+    B, H, N, d = (int(x) for x in q.shape)
+    mbytes = 0 if blockmap is None else blockmap.numel() * blockmap.element_size()
+    _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(dtype),
+                           ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes,
+                           ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
+           "attn_fwd")
+
+
+def read_blockmap(blockmap, B: int, N: int) -> dict:
+    """Splits a block map copied back to the host into its sections (numpy)."""
+    raw = blockmap.detach().cpu().numpy() if hasattr(blockmap, "detach") else np.asarray(blockmap)
+    raw = raw.view(np.uint8)
+    lay = attn_blockmap_layout_of(B, N)
+    nb = (N + 127) // 128
+    hdr = raw[:64].view(np.int32)
+
+    def sec(name, dtype, shape):
+        n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+        return raw[lay[name]:lay[name] + n].view(dtype).reshape(shape)
+
+    return dict(header=dict(magic=int(hdr.view(np.uint32)[0]), B=int(hdr[1]), N=int(hdr[2]), nqb=int(hdr[3]),
+                            nkb=int(hdr[4]), flags=int(hdr.view(np.uint32)[5]), window=int(hdr[6])),
+                cls=sec("cls", np.uint8, (B, nb, nb)), counts=sec("counts", np.int32, (B, nb, 2)),
+                idx=sec("idx", np.int32, (B, nb, 2, nb)), row_lo=sec("row_lo", np.int32, (B, N)),
+                row_hi=sec("row_hi", np.int32, (B, N)), pairs=sec("pairs", np.int64, (B, nb)),
+                status=sec("status", np.int32, (B, nb)))

@@ -1,0 +1,204 @@
+/*
+ * attn119 -- fused exact-attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn119.so.  Plain pointers and sizes only; every device pointer is
+ * memory the caller allocated (hipMalloc or a framework allocator) on the current
+ * HIP device.  The library allocates nothing and keeps no state between calls.
+ *
+ * The operation (pages, cited by title and section):
+ *   "FlashAttention 4: Γρηγορότερη και Αποδοτική σε Μνήμη Προσοχή για LLMs"
+ *   (el.linux-konsole.com), section "Εισαγωγή": attention multiplies the queries
+ *   by the keys, normalises with a softmax, multiplies by the values; section
+ *   "Γιατί οι πυρήνες προσοχής ...": the score matrix is processed in tiles on
+ *   chip and only a running maximum and sum are kept per query row; section
+ *   "Έξυπνος επανακανονισμός Softmax ...": the accumulator is rescaled only when
+ *   the running maximum grows by a significant amount.
+ *   "PyTorchs FlexAttention mit FlashAttention-4 ist ein Game-Changer" (liora.io),
+ *   opening section: the ALiBi, sliding-window, document-mask and soft-capping
+ *   variants; section "Aktuelle Einschränkungen": block sparsity.
+ *   "FlashAttention-3: Rekordverdächtige Geschwindigkeit und Präzision bei
+ *   AI-Modellen" (ctol-digital.de), section "Analyse": FP8 inputs with block
+ *   quantisation.
+ *
+ * For every batch b, head h and query row q (0-based), with s = (Q[q].K[k])*scale:
+ *   ATTN_SOFTCAP:  s <- softcap * tanh(s / softcap)          (on the scaled score)
+ *   ATTN_ALIBI:    s <- s - slope[h] * |q - k|               (= slope*(k - q) for k <= q)
+ *   visible(q,k) = [k <= q if ATTN_CAUSAL] and [|q - k| <= window-1 if ATTN_WINDOW]
+ *                  and [doc_id[b][q] == doc_id[b][k] if ATTN_DOCUMENT]
+ *   O[q]   = sum_k softmax_k(s) V[k] over visible k          (bf16 output)
+ *   LSE[q] = ln sum_k exp(s) over visible k                  (fp32 output)
+ * Every valid mask keeps the diagonal, so no row is ever empty.
+ *
+ * Layouts (all contiguous, row-major, innermost index last):
+ *   q, k, v : [B][H][N][d] of bf16, or of OCP E4M3FN bytes (ATTN_FP8_E4M3)
+ *   o       : [B][H][N][d] bf16 (round to nearest even)
+ *   lse     : [B][H][N] fp32, natural log
+ *   doc_id  : [B][N] int32, non-decreasing along N (documents are contiguous runs)
+ *   alibi_slopes : [H] fp32, or NULL for 2^(-8(h+1)/H), h = 0..H-1
+ *   fp8 scales   : [B][H][ceil(N/128)] fp32; value = code * scale of its 128-row block
+ * d must be 64 or 128; any N >= 1 is accepted.  Device pointers must be 16-byte
+ * aligned.
+ *
+ * Errors: every entry point validates its host-visible arguments and returns a
+ * negative attn_status *before* launching anything.  Launch failures are reported
+ * as ATTN_ERR_HIP.  Faults inside kernels surface at the caller's next
+ * synchronisation.  No exception crosses the ABI.  All calls are thread-safe.
+ */
+#ifndef ATTN119_H_
+#define ATTN119_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad scalar */
+  ATTN_ERR_UNSUPPORTED = -2,   /* d not in {64,128}, unknown dtype / flag / pv mode */
+  ATTN_ERR_BAD_BLOCKMAP = -3,  /* blockmap missing or of the wrong size for (B, N, mask) */
+  ATTN_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
+  ATTN_ERR_BAD_DOC_ID = -5     /* doc_id decreases somewhere (attn_blockmap_status) */
+} attn_status;
+
+typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP8_E4M3 = 1 } attn_dtype;
+
+/* attn_mask.flags bits */
+enum {
+  ATTN_CAUSAL = 1,
+  ATTN_WINDOW = 2,
+  ATTN_DOCUMENT = 4,
+  ATTN_ALIBI = 8,
+  ATTN_SOFTCAP = 16
+};
+
+/* attn_fp8.pv_mode */
+enum {
+  ATTN_PV_BF16 = 0, /* P rounded to bf16, V codes widened exactly to bf16, bf16 MFMA */
+  ATTN_PV_E4M3 = 1  /* P rounded to e4m3 (saturating), fp8 MFMA on the V codes (not built yet:
+                       ATTN_ERR_UNSUPPORTED) */
+};
+
+/* attn_fp8.qk_mode */
+enum {
+  ATTN_QK_BF16 = 0, /* Q and K codes widened exactly to bf16, bf16 MFMA with fp32 accumulation:
+                       scores exact to fp32 rounding (the accurate mode) */
+  ATTN_QK_E4M3 = 1  /* Q.K^T on the e4m3 MFMA (twice the bf16 rate).  gfx950 sums the products
+                       of one fp8 MFMA to about 2^-13 of the largest product, so a score
+                       dominated by a few large channels (outlier features) carries an error
+                       of that size */
+};
+
+/*
+ * Mask and score modifiers.  The struct is read during the call only; the device
+ * arrays it points to must stay valid until the enqueued work completes.
+ *   window : visible keys per query side including itself (>= 1) when ATTN_WINDOW;
+ *            with ATTN_CAUSAL exactly `window` keys q-window+1 .. q are visible.
+ *   softcap: cap > 0 when ATTN_SOFTCAP.
+ */
+typedef struct attn_mask {
+  uint32_t flags;
+  int32_t window;
+  float softcap;
+  const int32_t* doc_id;     /* device [B][N], required iff ATTN_DOCUMENT */
+  const float* alibi_slopes; /* device [H] or NULL (default slopes) */
+} attn_mask;
+
+/* FP8 inputs: per (b, h, 128-row block) scales of q, k and v (device, > 0). */
+typedef struct attn_fp8 {
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t pv_mode; /* ATTN_PV_* */
+  int32_t qk_mode; /* ATTN_QK_* */
+} attn_fp8;
+
+/*
+ * Block map (block sparsity).  A workspace in caller-owned device memory that
+ * classifies every 128-query x 128-key block as EMPTY (0), PARTIAL (1) or FULL (2)
+ * and lists the non-empty key blocks of each query block, so that the forward pass
+ * never touches an EMPTY block and evaluates the mask only inside PARTIAL ones.
+ * Needed whenever flags contain ATTN_CAUSAL, ATTN_WINDOW or ATTN_DOCUMENT.
+ *
+ * Byte layout (nqb = nkb = ceil(N/128); every section starts 256-byte aligned,
+ * offsets as returned by attn_blockmap_layout_of):
+ *   header   : attn_blockmap_header
+ *   cls      : uint8  [B][nqb][nkb]     block class
+ *   counts   : int32  [B][nqb][2]       number of FULL, number of PARTIAL blocks
+ *   idx      : int32  [B][nqb][2][nkb]  ascending FULL kb, then -1; ascending PARTIAL kb, then -1
+ *   row_lo   : int32  [B][N]            smallest visible key of each query
+ *   row_hi   : int32  [B][N]            largest visible key of each query
+ *   pairs    : int64  [B][nqb]          visible (q, k) pairs of each query block
+ *   status   : int32  [B][nqb]          1 if doc_id[b] decreases from a row of this block to
+ *                                       the next row, else 0 (a batch row with any 1 is invalid)
+ */
+typedef struct attn_blockmap_header {
+  uint32_t magic; /* 0x39313141 */
+  int32_t B, N, nqb, nkb;
+  uint32_t flags; /* mask flags restricted to CAUSAL|WINDOW|DOCUMENT */
+  int32_t window;
+  int32_t reserved[9];
+} attn_blockmap_header;
+
+typedef struct attn_blockmap_layout {
+  size_t cls, counts, idx, row_lo, row_hi, pairs, status, total;
+} attn_blockmap_layout;
+
+/* Size in bytes of the block-map workspace for (B, N, mask).  Host only. */
+attn_status attn_blockmap_bytes(int32_t B, int32_t N, const attn_mask* mask, size_t* bytes);
+
+/* Byte offset of every section of the block-map workspace.  Host only. */
+attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* layout);
+
+/*
+ * Builds the block map for (B, N, mask) into `map` (device, `bytes` bytes, as
+ * returned by attn_blockmap_bytes) on `stream` (a hipStream_t; NULL = default
+ * stream).  Asynchronous; deterministic; the result is byte-identical for equal
+ * inputs.  A decreasing doc_id is recorded in the status section (see
+ * attn_blockmap_status) and makes attn_fwd write NaN to O and LSE of the batch row.
+ */
+attn_status attn_blockmap_build(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes,
+                                void* stream);
+
+/* Synchronises `stream`, then reads the map's status section: ATTN_OK or ATTN_ERR_BAD_DOC_ID. */
+attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream);
+
+/*
+ * Host-side validation of an attn_fwd call (no HIP call, usable without a GPU):
+ * the same arguments as attn_fwd minus the stream.
+ */
+attn_status attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int32_t B, int32_t H, int32_t N, int32_t d, float scale, int32_t dtype,
+                            const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                            const attn_fp8* fp8, float rescale_tau);
+
+/*
+ * Enqueues the forward pass on `stream` (a hipStream_t; NULL = default stream) and
+ * returns after the launch.
+ *   scale        : > 0 and finite (typically 1/sqrt(d)).
+ *   dtype        : ATTN_BF16 or ATTN_FP8_E4M3 (then `fp8` is required).
+ *   mask         : NULL for plain attention.
+ *   blockmap     : built by attn_blockmap_build for the same (B, N, mask); required
+ *                  iff the mask has CAUSAL, WINDOW or DOCUMENT; otherwise ignored.
+ *   rescale_tau  : online-softmax rescale threshold in log2 units, 0 <= tau <= 8:
+ *                  the running maximum used as the exponent offset is replaced only
+ *                  when a row's maximum exceeds it by more than tau.  The result
+ *                  does not depend on tau beyond rounding.
+ * Reads q, k, v (and the scales, doc ids, slopes, map); writes every element of
+ * o and lse.  Deterministic: equal inputs give bit-identical outputs.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                     int32_t H, int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
+                     const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8,
+                     float rescale_tau, void* stream);
+
+/* Static description of a status code. */
+const char* attn_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN119_H_ */

@@ -14,6 +14,9 @@ visibility predicate, evaluated for every (query, key) position:
   idx[b][qb][1][:] = PARTIAL kb in ascending order, then -1 padding
   row_lo[b][q], row_hi[b][q] = smallest and largest visible key of query q
       (0 and -1 for a row with no visible key)
+  qb_pairs[b][qb] = visible (q, k) pairs of the query rows of block qb
+  status[b][qb] = 1 if doc_id[b][q + 1] < doc_id[b][q] for some row q of block qb
+      (documents must be contiguous runs; only evaluated with the DOCUMENT flag)
 
 The visible-pair count is the number of (b, q, k) with visible(q, k); the
 metric's "unmasked FLOPs" are 4 * H * d times it.
@@ -25,7 +28,7 @@ from typing import Optional
 
 import numpy as np
 
-from .attention import visible
+from .attention import DOCUMENT, visible
 
 EMPTY, PARTIAL, FULL = 0, 1, 2
 BLOCK = 128
@@ -40,13 +43,19 @@ def blockmap_ref(B: int, N: int, flags: int, window: int = 0, doc_id: Optional[n
     row_lo = np.zeros((B, N), dtype=np.int32)
     row_hi = np.full((B, N), -1, dtype=np.int32)
     pairs = np.zeros(B, dtype=np.int64)
+    qb_pairs = np.zeros((B, nqb), dtype=np.int64)
+    status = np.zeros((B, nqb), dtype=np.int32)
     kpos = np.arange(N)
     for b in range(B):
         doc_row = None if doc_id is None else np.asarray(doc_id[b])
         for qb in range(nqb):
             q0, q1 = qb * block, min(N, (qb + 1) * block)
             vis = visible(np.arange(q0, q1), kpos, flags, window, doc_row)  # [rows][N]
-            pairs[b] += int(vis.sum())
+            qb_pairs[b, qb] = int(vis.sum())
+            pairs[b] += qb_pairs[b, qb]
+            if flags & DOCUMENT:
+                rows = np.arange(q0, min(q1, N - 1))
+                status[b, qb] = int(np.any(doc_row[rows + 1] < doc_row[rows]))
             anyv = vis.any(axis=1)
             r = np.nonzero(anyv)[0]
             row_lo[b, q0 + r] = vis[r].argmax(axis=1)
@@ -67,7 +76,7 @@ def blockmap_ref(B: int, N: int, flags: int, window: int = 0, doc_id: Optional[n
             idx[b, qb, 0, :len(full)] = full
             idx[b, qb, 1, :len(part)] = part
     return dict(cls=cls, counts=counts, idx=idx, row_lo=row_lo, row_hi=row_hi, pairs=pairs,
-                visible_pairs=int(pairs.sum()))
+                qb_pairs=qb_pairs, status=status, visible_pairs=int(pairs.sum()))
 
 
 def row_intervals_ref(N: int, flags: int, window: int = 0, doc_row=None):

@@ -1,0 +1,112 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and validates arguments before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn119.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from exact_attention_119_amd import lib
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.fail("libattn119.so is not built (python -m exact_attention_119_amd.build)")
+    lib.load()
+    return lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(L.EXPORTS)
+    cdll = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(cdll, n), n
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.status_str(s) and L.status_str(s) != "unknown status"
+    assert L.status_str(7) == "unknown status"
+
+
+def test_blockmap_layout(L):
+    lay = L.attn_blockmap_layout_of(2, 300)
+    nb = 3
+    assert lay["cls"] == 256
+    order = ["cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status", "total"]
+    for a, b in zip(order, order[1:]):
+        assert lay[a] < lay[b] and lay[b] % 256 == 0
+    assert lay["counts"] - lay["cls"] >= 2 * nb * nb
+    assert lay["row_hi"] - lay["row_lo"] >= 2 * 300 * 4
+    assert L.attn_blockmap_bytes(2, 300, L.make_mask(L.ATTN_CAUSAL)) == lay["total"]
+    with pytest.raises(L.AttnError):
+        L.attn_blockmap_bytes(0, 300)
+    with pytest.raises(L.AttnError):
+        L.attn_blockmap_bytes(1, 300, L.make_mask(L.ATTN_WINDOW, window=0))
+
+
+P = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced by validation
+
+
+def _args(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, N=300, d=128, scale=0.1, dtype=0, mask=None, blockmap=None,
+             blockmap_bytes=0, fp8=None, rescale_tau=8.0)
+    a.update(kw)
+    return a
+
+
+def test_check_args_ok_and_errors(L):
+    ck = lambda **kw: L.attn_check_args(**_args(**kw))
+    assert ck() == L.ATTN_OK
+    assert ck(d=64) == L.ATTN_OK
+    assert ck(q=None) == L.ATTN_ERR_INVALID_ARG
+    assert ck(lse=P + 4) == L.ATTN_ERR_INVALID_ARG
+    assert ck(d=96) == L.ATTN_ERR_UNSUPPORTED
+    assert ck(B=0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(H=0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(N=0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(scale=0.0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(scale=float("inf")) == L.ATTN_ERR_INVALID_ARG
+    assert ck(scale=float("nan")) == L.ATTN_ERR_INVALID_ARG
+    assert ck(rescale_tau=-1.0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(rescale_tau=9.0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(dtype=2) == L.ATTN_ERR_UNSUPPORTED
+    assert ck(mask=L.make_mask(64)) == L.ATTN_ERR_UNSUPPORTED
+    assert ck(mask=L.make_mask(L.ATTN_ALIBI | L.ATTN_SOFTCAP, softcap=30.0)) == L.ATTN_OK
+    assert ck(mask=L.make_mask(L.ATTN_SOFTCAP, softcap=0.0)) == L.ATTN_ERR_INVALID_ARG
+    assert ck(mask=L.make_mask(L.ATTN_SOFTCAP, softcap=float("inf"))) == L.ATTN_ERR_INVALID_ARG
+    # positional masks need a block map of exactly the right size
+    m = L.make_mask(L.ATTN_CAUSAL)
+    nbytes = L.attn_blockmap_bytes(2, 300, m)
+    assert ck(mask=m) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert ck(mask=m, blockmap=P, blockmap_bytes=nbytes - 1) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert ck(mask=m, blockmap=P, blockmap_bytes=nbytes) == L.ATTN_OK
+    assert ck(mask=L.make_mask(L.ATTN_WINDOW | L.ATTN_CAUSAL, window=0), blockmap=P,
+              blockmap_bytes=nbytes) == L.ATTN_ERR_INVALID_ARG
+    assert ck(mask=L.make_mask(L.ATTN_DOCUMENT), blockmap=P, blockmap_bytes=nbytes) == L.ATTN_ERR_INVALID_ARG
+    assert ck(mask=L.make_mask(L.ATTN_DOCUMENT, doc_id=P), blockmap=P, blockmap_bytes=nbytes) == L.ATTN_OK
+    # fp8 needs its scales; the e4m3 PV mode is not built
+    assert ck(dtype=1) == L.ATTN_ERR_INVALID_ARG
+    assert ck(dtype=1, fp8=L.make_fp8(P, P, None)) == L.ATTN_ERR_INVALID_ARG
+    assert ck(dtype=1, fp8=L.make_fp8(P, P, P)) == L.ATTN_OK
+    assert ck(dtype=1, fp8=L.make_fp8(P, P, P, pv_mode=5)) == L.ATTN_ERR_UNSUPPORTED
+
+
+def test_fwd_rejects_before_launch(L):
+    """attn_fwd with bad arguments returns the validation error without touching the GPU."""
+    lib = L.load()
+    st = lib.attn_fwd(P, P, P, P, P, 1, 1, 16, 80, 0.1, 0, None, None, 0, None, 8.0, None)
+    assert st == L.ATTN_ERR_UNSUPPORTED
+    st = lib.attn_fwd(None, P, P, P, P, 1, 1, 16, 64, 0.1, 0, None, None, 0, None, 8.0, None)
+    assert st == L.ATTN_ERR_INVALID_ARG

@@ -114,3 +114,13 @@ def test_row_intervals_closed_forms():
     # non-contiguous documents are not intervals
     _, _, contiguous = O.row_intervals_ref(6, DOCUMENT, 0, np.array([0, 1, 0, 1, 0, 1]))
     assert not contiguous
+
+
+def test_qb_pairs_and_doc_status():
+    doc = np.array([[0] * 100 + [1] * 200 + [2] * 20, [0] * 130 + [2] * 10 + [1] * 180]).astype(np.int32)
+    m = O.blockmap_ref(2, 320, CAUSAL | DOCUMENT, 0, doc)
+    assert m["qb_pairs"].sum() == m["visible_pairs"]
+    assert m["qb_pairs"][0].sum() == 100 * 101 // 2 + 200 * 201 // 2 + 20 * 21 // 2
+    assert m["status"][0].tolist() == [0, 0, 0]
+    assert m["status"][1].tolist() == [0, 1, 0]  # the decrease 2 -> 1 is at row 139
+    assert O.blockmap_ref(2, 320, CAUSAL, 0, doc)["status"].sum() == 0
