@@ -149,7 +149,7 @@ attn_status attn_check_args(const void* q, const void* k, const void* v, void* o
     return ATTN_ERR_INVALID_ARG;
   if (dtype == ATTN_FP8_E4M3) {
     if (!fp8 || !fp8->q_scale || !fp8->k_scale || !fp8->v_scale) return ATTN_ERR_INVALID_ARG;
-    if (fp8->pv_mode != ATTN_PV_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (fp8->pv_mode != ATTN_PV_F16) return ATTN_ERR_UNSUPPORTED;
     if (fp8->qk_mode != ATTN_QK_BF16 && fp8->qk_mode != ATTN_QK_E4M3) return ATTN_ERR_UNSUPPORTED;
   }
   if (positional(mask)) {

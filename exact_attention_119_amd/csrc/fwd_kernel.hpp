@@ -77,6 +77,16 @@ __device__ __forceinline__ bf16x2 cvt_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ uint32_t as_u32(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ f16x2 cvt_f16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even
+}
+
+__device__ __forceinline__ f32x16 mfma_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // Position of key kk (0..63 within a step) in the permuted order used for the
 // transposed V tile: within each 16-key group, bits [b3 b2 b1 b0] -> [b2 b3 b1 b0].
@@ -95,13 +105,24 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w) {
                as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
 }
 
+// e4m3 -> fp16 is exact as well (every e4m3 value, subnormals included, lies inside
+// fp16's normal range): v_cvt_scalef32_pk_f16_fp8, unit scale.
+__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(u32x2 w) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true))};
+}
+
 // Input modes of the kernel.
 //   kInBf16  : bf16 Q/K/V, bf16 MFMA for both products.
-//   kInFp8   : e4m3 Q/K/V with block scales; the codes are widened exactly to bf16 while
-//              they are staged (Q into VGPRs, K and V into LDS) and both products run on
-//              bf16 MFMA with fp32 accumulation.  This is the accurate fp8 mode: gfx950's
-//              fp8 MFMA sums its products with a precision of about 2^-13 of the largest
-//              one, which inputs with outlier channels turn into score errors of 1e-2.
+//   kInFp8   : e4m3 Q/K/V with block scales; the codes are widened exactly while they
+//              are staged (Q, K to bf16; V to fp16) and both products run on 16-bit MFMA
+//              with fp32 accumulation: Q.K^T on bf16, P.V on fp16, with P rounded to fp16
+//              (8x finer than bf16; P <= 2^tau stays far inside fp16's range).  This is
+//              the accurate fp8 mode: gfx950's fp8 MFMA sums its products with a
+//              precision of about 2^-13 of the largest one, which inputs with outlier
+//              channels turn into score errors of 1e-2.
 //   kInFp8Qk8: e4m3 inputs, Q.K^T on the e4m3 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4,
 //              twice the bf16 rate, the limited accumulation precision above), PV as kInFp8.
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
@@ -131,7 +152,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   constexpr int VCPR = D / 8;                  // 8-element d-chunks per V row
   constexpr int NDB = D / 32;                  // 32-wide d blocks of O^T
   constexpr int KT_BYTES = BN * KLB;           // one K tile
-  constexpr int VT_BYTES = D * BN * 2;         // one transposed bf16 V tile
+  constexpr int VT_BYTES = D * BN * 2;         // one transposed 16-bit V tile (fp16 for fp8)
   constexpr bool LINEAR = !ALIBI && !SOFTCAP;  // score = raw * c
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
@@ -227,7 +248,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   }
   const bool alibi_abs = !(a.mflags & kCausal);  // bidirectional masks: -slope*|q-k|
   float sq = 1.f;
-  if constexpr (FP8) sq = a.q_scale[(size_t)bh * nqb + qb];
+  // fp8: P is formed in units of vs/vs_max (the V block scale over the largest V block
+  // scale of this head), so that it stays <= 2^tau inside fp16's range whatever the
+  // scales are; O is multiplied back by vs_max in the epilogue.
+  float vs_max = 1.f;
+  if constexpr (FP8) {
+    sq = a.q_scale[(size_t)bh * nqb + qb];
+    const float* vsr = a.v_scale + (size_t)bh * nqb;
+    float mx = 0.f;
+    for (int i = lane; i < nqb; i += 64) mx = __builtin_fmaxf(mx, vsr[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+    vs_max = mx > 0.f ? mx : 1.f;
+  }
 
   // ---- step enumeration -----------------------------------------------------------
   auto step_kb = [&](int s, bool& partial) -> int {
@@ -293,7 +326,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < VKPT; ++r) {
       if constexpr (FP8) {
-        const u32x4 x = e4m3x8_to_bf16x8(vreg[r]);
+        const u32x4 x = e4m3x8_to_f16x8(vreg[r]);
         w[r][0] = x.x; w[r][1] = x.y; w[r][2] = x.z; w[r][3] = x.w;
       } else {
         w[r][0] = vreg[r].x; w[r][1] = vreg[r].y; w[r][2] = vreg[r].z; w[r][3] = vreg[r].w;
@@ -341,6 +374,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   __syncthreads();
 
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  const f16x2 ones_h = {(f16)1.0f, (f16)1.0f};
+  typedef typename std::conditional<FP8, f16x8, bf16x8>::type PVFrag;  // P and V^T fragments
 
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
@@ -381,7 +416,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
       const float sk = a.k_scale[(size_t)bh * nqb + kb];
       ct *= sq * sk;
       sc2t *= sq * sk;
-      vs = a.v_scale[(size_t)bh * nqb + kb];
+      vs = a.v_scale[(size_t)bh * nqb + kb] / vs_max;
       inv_vs = 1.f / vs;
       log2_vs = log2f(vs);
     }
@@ -439,8 +474,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
     // exponent offset; -inf only while every key seen so far is hidden (then p = 0)
     const float moff = (m_used == -__builtin_inff() ? 0.f : m_used) - log2_vs;
 
-    // ---- P = exp2(x - m), sums, bf16 packing ---------------------------------------
-    bf16x8 pf[4];
+    // ---- P = exp2(x - m), sums, 16-bit packing ---------------------------------------
+    PVFrag pf[4];
     float ls = 0.f, lqs = 0.f;
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
@@ -459,12 +494,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
             p1 = fast_exp2(sacc[bk][r + 1] - moff);
           }
           ls += p0 + p1;
-          const bf16x2 pb = cvt_bf16x2(p0, p1);
-          lqs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lqs, false);
-          pk[t] = as_u32(pb);
+          if constexpr (FP8) {
+            const f16x2 pb = cvt_f16x2(p0, p1);
+            lqs = __builtin_amdgcn_fdot2(pb, ones_h, lqs, false);
+            pk[t] = as_u32(pb);
+          } else {
+            const bf16x2 pb = cvt_bf16x2(p0, p1);
+            lqs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lqs, false);
+            pk[t] = as_u32(pb);
+          }
         }
         u32x4 v4 = {pk[0], pk[1], pk[2], pk[3]};
-        pf[bk * 2 + g] = __builtin_bit_cast(bf16x8, v4);
+        pf[bk * 2 + g] = __builtin_bit_cast(PVFrag, v4);
       }
     l_sum += ls * inv_vs;
     lq_sum += lqs * inv_vs;
@@ -477,8 +518,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
       for (int db = 0; db < NDB; ++db) {
         const int d = db * 32 + l32;
         const int phys = (ks * 2 + hh) ^ (((d >> 1) ^ (d >> 4)) & 7);
-        const bf16x8 vfr = *(const bf16x8*)(vbuf + d * 128 + phys * 16);
-        oacc[db] = mfma_bf16(vfr, pf[ks], oacc[db]);
+        const PVFrag vfr = *(const PVFrag*)(vbuf + d * 128 + phys * 16);
+        if constexpr (FP8)
+          oacc[db] = mfma_f16(vfr, pf[ks], oacc[db]);
+        else
+          oacc[db] = mfma_bf16(vfr, pf[ks], oacc[db]);
       }
 
     if (s + 1 < nsteps) store_step(buf ^ 1);
@@ -490,7 +534,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   lq_sum += __shfl_xor(lq_sum, 32);
   if (!qvalid) return;
   const float nanv = __builtin_nanf("");
-  const float inv = invalid ? nanv : (lq_sum > 0.f ? 1.f / lq_sum : 0.f);
+  const float inv = invalid ? nanv : (lq_sum > 0.f ? vs_max / lq_sum : 0.f);
   bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

@@ -33,7 +33,7 @@ ATTN_ALIBI = 8
 ATTN_SOFTCAP = 16
 POSITIONAL = ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT
 
-ATTN_PV_BF16 = 0
+ATTN_PV_F16 = 0
 ATTN_PV_E4M3 = 1
 
 ATTN_QK_BF16 = 0
@@ -126,7 +126,7 @@ def make_mask(flags: int = 0, window: int = 0, softcap: float = 0.0, doc_id=None
     return attn_mask(int(flags), int(window), float(softcap), _ptr(doc_id), _ptr(alibi_slopes))
 
 
-def make_fp8(q_scale, k_scale, v_scale, pv_mode: int = ATTN_PV_BF16, qk_mode: int = ATTN_QK_BF16):
+def make_fp8(q_scale, k_scale, v_scale, pv_mode: int = ATTN_PV_F16, qk_mode: int = ATTN_QK_BF16):
     return attn_fp8(_ptr(q_scale), _ptr(k_scale), _ptr(v_scale), int(pv_mode), int(qk_mode))
 
 

@@ -76,7 +76,9 @@ enum {
 
 /* attn_fp8.pv_mode */
 enum {
-  ATTN_PV_BF16 = 0, /* P rounded to bf16, V codes widened exactly to bf16, bf16 MFMA */
+  ATTN_PV_F16 = 0,  /* V codes widened exactly to fp16, P (in units of the V block scale over
+                       the head's largest V block scale, <= 2^tau) rounded to fp16, fp16 MFMA
+                       with fp32 accumulation */
   ATTN_PV_E4M3 = 1  /* P rounded to e4m3 (saturating), fp8 MFMA on the V codes (not built yet:
                        ATTN_ERR_UNSUPPORTED) */
 };

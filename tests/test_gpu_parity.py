@@ -35,7 +35,7 @@ def _announce(*a):
     print("CASE", *a, flush=True)
 
 
-def _run(p, tau=8.0, pv_mode=L.ATTN_PV_BF16, qk_mode=L.ATTN_QK_BF16):
+def _run(p, tau=8.0, pv_mode=L.ATTN_PV_F16, qk_mode=L.ATTN_QK_BF16):
     dp = WD.to_device(p, pv_mode=pv_mode, qk_mode=qk_mode)
     dp.o.fill_(float("nan"))
     dp.lse.fill_(float("nan"))

@@ -36,7 +36,7 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def to_device(p: Problem, device="cuda", pv_mode: int = L.ATTN_PV_BF16,
+def to_device(p: Problem, device="cuda", pv_mode: int = L.ATTN_PV_F16,
               qk_mode: int = L.ATTN_QK_BF16) -> DeviceProblem:
     if p.dtype == "bf16":
         q, k, v = (_dev(x.view(np.int16), device).view(torch.bfloat16) for x in (p.q, p.k, p.v))
