@@ -36,8 +36,13 @@ SOURCES = [
 
 # -packed-fp32-ops: hipcc must not emit v_pk_{add,mul,fma}_f32 (the host pass warns
 # that it does not know the feature; that warning is harmless).
+# -mno-amdgpu-ieee -fno-honor-nans: the kernels never produce or consume NaN on their
+# arithmetic path (masked scores are -inf, which these flags keep); without them
+# every fmaxf of an MFMA result is preceded by a quieting v_max_f32.  The one NaN the
+# kernels write (a poisoned batch row) is a stored bit pattern.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+          "-fno-honor-nans"]
 
 
 def hipcc() -> str:

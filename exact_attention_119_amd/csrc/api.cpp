@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 
 #include "../../include/attn119.h"
@@ -17,6 +18,11 @@ hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int
 template <int D, int IN>
 hipError_t launch_fwd_family(const FwdArgs& a, bool masked, bool alibi, bool softcap, hipStream_t st);
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
+namespace bf16path {
+constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
+template <int D>
+hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st);
+}  // namespace bf16path
 }  // namespace attn119
 
 using namespace attn119;
@@ -29,6 +35,52 @@ constexpr uint32_t kAllFlags = ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT | ATTN_
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool positional(const attn_mask* m) { return m && (m->flags & (ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT)); }
+
+// The compiled kernel variant a call selects (host logic only, testable on a CPU).
+struct FwdVariant {
+  int d;
+  int input;     // kInBf16, kInFp8, kInFp8Qk8
+  bool masked;   // positional mask through the block map
+  int mode;      // bf16 kernel: score-modifier mode
+  bool alibi, softcap;
+};
+
+FwdVariant select_variant(int32_t d, int32_t dtype, const attn_mask* mask, const attn_fp8* fp8) {
+  FwdVariant v;
+  const uint32_t flags = mask ? mask->flags : 0u;
+  v.d = d;
+  v.input = dtype == ATTN_BF16 ? kInBf16 : (fp8 && fp8->qk_mode == ATTN_QK_E4M3 ? kInFp8Qk8 : kInFp8);
+  v.masked = positional(mask);
+  v.alibi = flags & ATTN_ALIBI;
+  v.softcap = flags & ATTN_SOFTCAP;
+  if (!v.alibi) v.mode = v.softcap ? bf16path::kSoftcap : bf16path::kLinear;
+  else if (!v.softcap && (flags & ATTN_CAUSAL)) v.mode = bf16path::kAlibiCausal;
+  else v.mode = bf16path::kGeneric;
+  return v;
+}
+
+const char* variant_name(const FwdVariant& v) {
+  static const char* const kIn[] = {"bf16", "fp8", "fp8-qk8"};
+  static const char* const kMode[] = {"linear", "softcap", "alibi-causal", "generic-alibi", "generic-alibi-softcap"};
+  static const char* const kMods[] = {"none", "softcap", "alibi", "alibi+softcap"};
+  static char names[2][3][2][5][64];
+  static bool init = false;
+  if (!init) {  // (filled once; every entry is a pure function of its indices)
+    for (int di = 0; di < 2; ++di)
+      for (int in = 0; in < 3; ++in)
+        for (int m = 0; m < 2; ++m)
+          for (int k = 0; k < 5; ++k) {
+            const char* tail = in == 0 ? kMode[k] : kMods[k < 4 ? k : 3];
+            std::snprintf(names[di][in][m][k], 64, "%s d%d %s %s", kIn[in], di ? 128 : 64,
+                          m ? "masked" : "unmasked", tail);
+          }
+    init = true;
+  }
+  int k;
+  if (v.input == kInBf16) k = v.mode == bf16path::kGeneric ? (v.softcap ? 4 : 3) : v.mode;
+  else k = (v.alibi ? 2 : 0) + (v.softcap ? 1 : 0);
+  return names[v.d == 128][v.input][v.masked][k];
+}
 
 attn_status check_mask(const attn_mask* m) {
   if (!m) return ATTN_OK;
@@ -159,6 +211,14 @@ attn_status attn_check_args(const void* q, const void* k, const void* v, void* o
   return ATTN_OK;
 }
 
+const char* attn_fwd_kernel_name(int32_t d, int32_t dtype, const attn_mask* mask, const attn_fp8* fp8) {
+  if (d != 64 && d != 128) return nullptr;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return nullptr;
+  if (check_mask(mask) != ATTN_OK) return nullptr;
+  if (dtype == ATTN_FP8_E4M3 && !fp8) return nullptr;
+  return variant_name(select_variant(d, dtype, mask, fp8));
+}
+
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
                      int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
                      const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
@@ -203,9 +263,10 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   }
   hipError_t e;
   const hipStream_t s = (hipStream_t)stream;
+  const FwdVariant var = select_variant(d, dtype, mask, fp8);
   if (dtype == ATTN_BF16)
-    e = d == 128 ? launch_fwd_family<128, kInBf16>(a, masked, alibi, softcap, s)
-                 : launch_fwd_family<64, kInBf16>(a, masked, alibi, softcap, s);
+    e = d == 128 ? bf16path::launch<128>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else if (fp8->qk_mode == ATTN_QK_BF16)
     e = d == 128 ? launch_fwd_family<128, kInFp8>(a, masked, alibi, softcap, s)
                  : launch_fwd_family<64, kInFp8>(a, masked, alibi, softcap, s);

@@ -1,0 +1,531 @@
+// Fused exact-attention forward pass for bf16 inputs on gfx950 (MI355X): the
+// software-pipelined kernel.
+//
+// What is computed (pages, by title and section):
+//  * "FlashAttention 4: Γρηγορότερη και Αποδοτική σε Μνήμη Προσοχή για LLMs"
+//    (el.linux-konsole.com), "Εισαγωγή" and "Γιατί οι πυρήνες προσοχής ...":
+//    scores Q.K^T, softmax, times V, taken tile by tile on chip, keeping only the
+//    running maximum and sum of every query row.  "Τι νέο υπάρχει στο FlashAttention
+//    4": each workgroup owns an output tile and streams K/V tiles through on-chip
+//    memory; the asynchronous pipeline keeps the matrix units busy while the
+//    softmax of the previous tile runs.  "Έξυπνος επανακανονισμός Softmax ...": the
+//    accumulator is rescaled only when a row's maximum grows past the one in use by
+//    a significant margin (tau, in log2 units).
+//  * "PyTorchs FlexAttention mit FlashAttention-4 ist ein Game-Changer" (liora.io),
+//    opening section: ALiBi, sliding window, document masking, soft-capping;
+//    "Aktuelle Einschränkungen": fully masked blocks are skipped (block sparsity).
+//
+// gfx950 mapping:
+//  * a workgroup of 4 waves owns 128 query rows of one (b, h), a wave 32 rows; the
+//    non-empty 128-key blocks of the row block are walked in 64-key steps, FULL
+//    blocks first (no mask code at all), then PARTIAL ones.
+//  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as A, the wave's Q tile
+//    resident in VGPRs as B): each lane holds one query row and 16 keys per 32-key
+//    block, so row maxima and sums are in-lane plus one v_permlane32_swap.
+//  * O^T += V^T . P^T on the same MFMA, with the S accumulators (converted to bf16)
+//    as the B operand.  V stays row-major in LDS; the V^T A operand is gathered
+//    with two ds_read_b64_tr_b16 per MFMA (a 16-lane transposing read), in the key
+//    order the S accumulator layout dictates.
+//  * K and V tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//    staging).  The buffer range check returns zeros past the head's last row.
+//  * software pipeline, one barrier per step: at step s the workgroup has K(s+1) and
+//    V(s) in LDS; it issues the loads of K(s+2) and V(s+1), then the MFMAs of
+//    S(s+1) = K(s+1) Q^T interleaved with the exponentials of step s, then
+//    O += V(s) P(s) followed by the mask, score modifiers and maximum of S(s+1).
+//  * LDS layouts are XOR-swizzled in 16-byte chunks so that both the K reads
+//    (ds_read_b128) and the V transposing reads are free of bank conflicts.
+//  * score modifiers are arranged to cost little per element:
+//      LINEAR   x = s*c                       max on raw s, p = exp2(s*c - m)
+//      SOFTCAP  x = cap*tanh(s*scale/cap)     monotone in s: max on raw s; in the
+//               (log2 units)                  P.V phase r = 1/(exp2(2 s c/cap)+1),
+//                                             then p = exp2(cap' - m - 2 cap' r)
+//      ALIBI_C  x = s*c + slope*(k - q)       causal masks: y = s*c + slope*(k - k0
+//                                             - 4hh) per element; the per-row part
+//                                             slope*(k0 + 4hh - q) moves into m
+//      GENERIC  anything else (ALiBi with softcap or a bidirectional mask)
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "fwd_args.hpp"
+
+namespace attn119 {
+namespace bf16path {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// score-modifier modes
+constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ bf16x2 to_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+}
+
+// v_permlane32_swap(a, b) exchanges the upper 32 lanes of a with the lower 32 lanes
+// of b.  With a = b = x, lane l < 32 ends with (x[l], x[l+32]) and lane l >= 32 with
+// (x[l-32], x[l]): both halves see the pair.  (The two results are copied out as
+// integers before the bit casts: a bit cast applied to an element of the returned
+// vector reads element 0 in this compiler.)
+__device__ __forceinline__ void pair_of(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                  false, false);
+  const int r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+// max / sum of x over lanes l and l^32 (the two halves holding one query row)
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_of(x, a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_of(x, a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One 16-byte chunk per lane from a buffer into LDS at lds_base + 16*lane.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* lds_base, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voffset, 0, 0, 0);
+}
+
+// key offset (within a 64-key step, minus 4*hh) of accumulator register r of block bk
+__host__ __device__ constexpr int key_off(int bk, int r) { return 32 * bk + 8 * (r >> 2) + (r & 3); }
+
+//   D       head dim (64 or 128)
+//   MASKED  positional mask through the block map (else: all keys visible)
+//   MODE    score-modifier mode (kLinear, kSoftcap, kAlibiCausal, kGeneric)
+//   GALIBI, GSOFTCAP  modifiers of the generic mode
+template <int D, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
+__global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) {
+  constexpr int BN = 64;                 // keys per step
+  constexpr int ROWB = D * 2;            // bytes per row of Q/K/V
+  constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  constexpr int RP256 = 256 / ROWB;      // rows per 256-byte LDS line
+  constexpr int TILE = BN * ROWB;        // bytes of one K or V tile
+  constexpr int LOADS = TILE / 1024;     // 1 KiB direct loads per tile
+  constexpr int LPW = LOADS / 4;         // ... per wave
+  constexpr int RPL = 1024 / ROWB;       // rows per direct load
+  constexpr int NQC = D / 16;            // 16-wide d chunks of Q (MFMA k steps)
+  constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
+
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int N = a.N;
+  const int nqb = a.nqb;
+
+  // ---- XCD-aware work mapping: consecutive workgroups of one XCD take consecutive
+  //      row blocks of one (b, h); row blocks of a head run last-first --------------
+  const int T = a.B * a.H * nqb;
+  const int L = blockIdx.x;
+  const int xcd = L & 7, jx = L >> 3;
+  const int wid = xcd * (T >> 3) + min(xcd, T & 7) + jx;
+  const int bh = wid / nqb;
+  const int qb = nqb - 1 - (wid - bh * nqb);
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+
+  const int q0 = qb * 128;
+  const int qrow = q0 + wave * 32 + l32;
+  const bool qvalid = qrow < N;
+  const size_t head_row0 = (size_t)bh * N;
+
+  // ---- block-map lookups (scalar loads through the constant address space: the map
+  //      is read-only here and every index is uniform over the workgroup) -------------
+  typedef const __attribute__((address_space(4))) int cint;
+  int nfull, npart;
+  cint* flist = nullptr;
+  cint* plist = nullptr;
+  int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
+  bool invalid = false;
+  if constexpr (MASKED) {
+    const __attribute__((address_space(4))) MapHeader* hd =
+        (const __attribute__((address_space(4))) MapHeader*)a.map;
+    invalid = hd->magic != kMapMagic || hd->B != a.B || hd->N != N || hd->flags != a.mflags ||
+              hd->window != a.window;
+    cint* cnt = (cint*)(a.map + a.lay.counts) + ((size_t)b * nqb + qb) * 2;
+    nfull = min(max(cnt[0], 0), nqb);
+    npart = min(max(cnt[1], 0), nqb - nfull);
+    flist = (cint*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
+    plist = flist + nqb;
+    if (qvalid) {
+      lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
+      hi_q = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
+    }
+    if (a.mflags & kDocument) {
+      const int* st = (const int*)(a.map + a.lay.status) + (size_t)b * nqb;
+      int bad = 0;
+      for (int i = tid; i < nqb; i += 256) bad |= st[i];
+      invalid |= __syncthreads_or(bad) != 0;
+    }
+    if (invalid) { nfull = 0; npart = 0; }
+  } else {
+    const bool tail = (N & 127) != 0;
+    nfull = tail ? nqb - 1 : nqb;
+    npart = tail ? 1 : 0;
+  }
+  const int nblk = nfull + npart;
+  const int nsteps = 2 * nblk;
+
+  // first key of step s (blocks: FULL list, then PARTIAL list)
+  auto step_k0 = [&](int s) -> int {
+    const int blk = s >> 1;
+    int kb = blk;
+    if constexpr (MASKED) {
+      kb = blk < nfull ? flist[blk] : plist[blk - nfull];
+      kb = min(max(kb, 0), nqb - 1);  // a corrupted map never addresses outside the head
+    }
+    return kb * 128 + (s & 1) * BN;
+  };
+
+  // ---- Q tile -> VGPRs (B operand of S^T = K Q^T) ----------------------------------------
+  bf16x8 qf[NQC];
+  {
+    const bf16* qp = (const bf16*)a.q + (head_row0 + (qvalid ? qrow : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      const bf16x8 v = *(const bf16x8*)(qp + c * 16 + hh * 8);
+      qf[c] = qvalid ? v : bf16x8{};
+    }
+  }
+
+  // ---- direct HBM -> LDS loads ---------------------------------------------------------
+  // K rows: 16-byte chunk ch of row r sits at chunk position ch ^ kswz(r).
+  // V rows: chunk ch of row r sits at ch ^ vswz(r).
+  auto kswz = [](int r) { return (r / RP256) % CPR; };
+  auto vswz = [](int r) { return 4 * ((r / RP256) % (CPR / 4)); };
+  // The buffer descriptor of a step starts at its first key row and covers the rows
+  // left in the head, so every row past N reads as zero (range-checked on the lane
+  // offset; no address ever leaves the head).
+  const unsigned char* const kbase = (const unsigned char*)a.k + head_row0 * ROWB;
+  const unsigned char* const vbase = (const unsigned char*)a.v + head_row0 * ROWB;
+  auto rsrc = [&](const unsigned char* base, int k0) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), (short)0,
+                                             max(N - k0, 0) * ROWB, 0x00020000);
+  };
+  int koff[LPW], voff[LPW];  // byte offsets within a tile, per direct load of this wave
+#pragma unroll
+  for (int r = 0; r < LPW; ++r) {
+    const int ld = wave * LPW + r;
+    const int row = ld * RPL + lane / CPR;
+    const int pos = lane % CPR;
+    koff[r] = row * ROWB + (pos ^ kswz(row)) * 16;
+    voff[r] = row * ROWB + (pos ^ vswz(row)) * 16;
+  }
+  auto issue_k = [&](int s, lds_u8* dst) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, step_k0(s));
+#pragma unroll
+    for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, koff[r]);
+  };
+  auto issue_v = [&](int s, lds_u8* dst) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, step_k0(s));
+#pragma unroll
+    for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, voff[r]);
+  };
+
+  // ---- LDS read addressing -------------------------------------------------------------
+  // K (A operand of S^T): lane reads row 32*bk + l32, chunk 2c + hh.
+  int kread[NQC];
+  {
+    const int sw = kswz(l32);  // the same for rows l32 and 32 + l32
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) kread[c] = l32 * ROWB + ((2 * c + hh) ^ sw) * 16;
+  }
+  // V^T (A operand of O^T): two 16-lane transposing reads per MFMA.  Within a 16-lane
+  // group, source lane 4e + a addresses key row key_e and the 4 d values
+  // 32 db + 16 dh + 4a .. +3; the read hands lane 4a + b the value of d = ... + 4a + b
+  // for the 4 keys key_0..key_3.  key_e = 16 ks + 8 t + 4 hh + e.
+  int vread[NDB];
+  {
+    const int e = (lane & 15) >> 2, aa = lane & 3, dh = (lane >> 4) & 1;
+    const int row = 4 * hh + e;  // + 16 ks + 8 t (multiples of 8 keep vswz unchanged)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int chunk = 4 * db + 2 * dh + (aa >> 1);
+      vread[db] = row * ROWB + (chunk ^ vswz(row)) * 16 + (aa & 1) * 8;
+    }
+  }
+  auto kfrag = [&](const lds_u8* kt, int bk, int c) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(kt + bk * 32 * ROWB + kread[c]);
+  };
+  auto vfrag = [&](const lds_u8* vt, int ks, int db) {
+    const lds_u8* base = vt + ks * 16 * ROWB + vread[db];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * ROWB));
+    const short __attribute__((ext_vector_type(8))) w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+  };
+
+  // ---- per-row constants ------------------------------------------------------------------
+  float slope2 = 0.f;  // ALiBi slope in log2 units
+  if constexpr (MODE == kAlibiCausal || GALIBI) {
+    const float sl = a.alibi_slopes ? a.alibi_slopes[h] : exp2_(a.alibi_exp * (float)(h + 1));
+    slope2 = sl * 1.4426950408889634f;
+  }
+  const bool alibi_abs = !(a.mflags & kCausal);  // bidirectional masks: -slope*|q-k|
+  const float ct = a.c, sc2 = a.sc2, cap2 = a.cap2, tau = a.tau;
+  const float ninf = -__builtin_inff();
+
+  // ---- state ----------------------------------------------------------------------------
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  float m_used = ninf;
+  float l_sum = 0.f;   // sum of p (unrounded), for LSE
+  float lq_sum = 0.f;  // sum of p as rounded to bf16, the normaliser of O
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+  // Mask, score modifiers and row maximum of the raw S^T accumulators of a step whose
+  // first key is k0.  Leaves in sacc what the exponential phase consumes (raw s,
+  // softcap r, ALiBi y or the full score x) and returns the row maximum of the
+  // scores in log2 units (both lane halves), -inf for a row with no visible key.
+  // Hidden keys (PARTIAL blocks only: a uniform branch) become -inf (softcap: r=+inf).
+  auto prepare = [&](f32x16 (&sacc)[2], int k0, bool partial) -> float {
+    float mx;
+    if constexpr (MODE == kAlibiCausal) {
+      // y = s*c + slope*key_off; the row part slope*(k0 + 4hh - q) is added to the max
+      // here and subtracted from the exponent offset in the exponential phase
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[bk][r] = __builtin_fmaf(sacc[bk][r], ct, slope2 * (float)key_off(bk, r));
+    } else if constexpr (MODE == kGeneric) {
+      const int kq = k0 + 4 * hh - qrow;
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sraw = sacc[bk][r];
+          float x;
+          if constexpr (GSOFTCAP) x = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(sraw * sc2) + 1.f), cap2);
+          else x = sraw * ct;
+          if constexpr (GALIBI) {
+            const float dist = (float)(kq + key_off(bk, r));
+            x = __builtin_fmaf(slope2, alibi_abs ? -__builtin_fabsf(dist) : dist, x);
+          }
+          sacc[bk][r] = x;
+        }
+    }
+    if (partial) {
+      const int rlo = lo_q - (k0 + 4 * hh), rhi = hi_q - (k0 + 4 * hh);
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = key_off(bk, r);
+          sacc[bk][r] = (off < rlo || off > rhi) ? ninf : sacc[bk][r];
+        }
+    }
+    mx = __builtin_fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+    for (int i = 2; i < 32; i += 2)
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[i >> 4][i & 15], sacc[i >> 4][(i & 15) + 1]));
+    if constexpr (MODE == kAlibiCausal) mx = __builtin_fmaf(slope2, (float)(k0 + 4 * hh - qrow), mx);
+    mx = pair_max(mx);
+    if constexpr (MODE == kLinear) {
+      mx *= ct;  // ct > 0 keeps the order; -inf stays -inf
+    } else if constexpr (MODE == kSoftcap) {
+      // r = 1 / (exp2(2 s c / cap) + 1); a hidden key (s = -inf) gets r = +inf, p = 0
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sv = sacc[bk][r];
+          const float rr = rcp_(exp2_(sv * sc2) + 1.f);
+          sacc[bk][r] = sv == ninf ? __builtin_inff() : rr;
+        }
+      const float xm = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(mx * sc2) + 1.f), cap2);
+      mx = mx == ninf ? ninf : xm;
+    }
+    return mx;
+  };
+
+  // P of one 16-key slice (registers 8g..8g+7 of block bk) packed as the bf16 B
+  // operand; adds the unrounded and the rounded sums.  moff: exponent offset.
+  auto pslice = [&](const f32x16& sacc, int g, float moff, float& ls, float& lqs) -> bf16x8 {
+    uint32_t pk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = g * 8 + 2 * t;
+      float p0, p1;
+      if constexpr (MODE == kLinear) {
+        p0 = exp2_(__builtin_fmaf(sacc[r], ct, -moff));
+        p1 = exp2_(__builtin_fmaf(sacc[r + 1], ct, -moff));
+      } else if constexpr (MODE == kSoftcap) {
+        p0 = exp2_(__builtin_fmaf(-2.f * cap2, sacc[r], cap2 - moff));
+        p1 = exp2_(__builtin_fmaf(-2.f * cap2, sacc[r + 1], cap2 - moff));
+      } else {
+        p0 = exp2_(sacc[r] - moff);
+        p1 = exp2_(sacc[r + 1] - moff);
+      }
+      ls += p0 + p1;
+      const bf16x2 pb = to_bf16x2(p0, p1);
+      lqs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lqs, false);
+      pk[t] = __builtin_bit_cast(uint32_t, pb);
+    }
+    const u32x4 v4 = {pk[0], pk[1], pk[2], pk[3]};
+    return __builtin_bit_cast(bf16x8, v4);
+  };
+
+  lds_u8* const kl0 = (lds_u8*)k_lds0;
+  lds_u8* const kl1 = (lds_u8*)k_lds1;
+  lds_u8* const vl0 = (lds_u8*)v_lds0;
+  lds_u8* const vl1 = (lds_u8*)v_lds1;
+
+  // One pipelined step s.  On entry: S(s) in scur, already prepared, with its row
+  // maximum mcur; K(s+1) and V(s) requested into knext and vcur.
+  //   1. wait for this wave's loads, barrier (all loads in; all reads of step s-1 done)
+  //   2. request K(s+2) into kcur and V(s+1) into vnext
+  //   3. threshold rescale for step s
+  //   4. S(s+1) = K(s+1) Q^T interleaved with P(s)
+  //   5. O += V(s) P(s), then prepare S(s+1)
+  auto step = [&](int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur, lds_u8* vnext, f32x16 (&scur)[2],
+                  f32x16 (&snext)[2], float& mcur) {
+    wait_vmem();
+    __syncthreads();
+    const bool has_next = s + 1 < nsteps;
+    if (s + 2 < nsteps) issue_k(s + 2, kcur);
+    if (has_next) issue_v(s + 1, vnext);
+    const int k0 = step_k0(s);
+
+    const float m_new = __builtin_fmaxf(m_used, mcur);
+    const bool need = m_new > m_used + tau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? exp2_(m_used - m_new) : 1.f;
+      m_used = need ? m_new : m_used;
+      l_sum *= alpha;
+      lq_sum *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+    }
+    // exponent offset; m_used is -inf only while every key seen so far is hidden
+    // (then p = 0 whatever the offset)
+    float moff = m_used == ninf ? 0.f : m_used;
+    if constexpr (MODE == kAlibiCausal) moff = __builtin_fmaf(-slope2, (float)(k0 + 4 * hh - qrow), moff);
+
+    bf16x8 pf[4];
+    float ls = 0.f, lqs = 0.f;
+    if (has_next) {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        snext[bk] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NQC; ++c) {
+          snext[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(knext, bk, c), qf[c], snext[bk], 0, 0, 0);
+          if (c % (NQC / 2) == NQC / 2 - 1) {  // two P slices per 32-key block of S(s+1)
+            const int sl = bk * 2 + c / (NQC / 2);
+            pf[sl] = pslice(scur[sl >> 1], sl & 1, moff, ls, lqs);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(scur[sl >> 1], sl & 1, moff, ls, lqs);
+    }
+    l_sum += ls;
+    lq_sum += lqs;
+
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vcur, ks, db), pf[ks], oacc[db], 0, 0, 0);
+    if (has_next) {
+      const int k1 = step_k0(s + 1);
+      mcur = prepare(snext, k1, (s + 1) >> 1 >= nfull);
+    }
+  };
+
+  f32x16 sa[2], sb[2];
+  float mcand = ninf;  // row maximum of the step about to be exponentiated
+  if (nsteps > 0) {
+    issue_k(0, kl0);
+    issue_v(0, vl0);
+    if (nsteps > 1) issue_k(1, kl1);
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      sa[bk] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NQC; ++c)
+        sa[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kl0, bk, c), qf[c], sa[bk], 0, 0, 0);
+    }
+    mcand = prepare(sa, step_k0(0), nfull == 0);
+  }
+  // nsteps is even: step 2j uses buffers 0 -> 1 and S in sa -> sb, step 2j+1 the reverse
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, kl0, kl1, vl0, vl1, sa, sb, mcand);
+    step(s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
+  }
+
+  // ---- epilogue -------------------------------------------------------------------------
+  l_sum = pair_sum(l_sum);
+  lq_sum = pair_sum(lq_sum);
+  if (!qvalid) return;
+  const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
+  const float inv = invalid ? nanv : (lq_sum > 0.f ? 1.f / lq_sum : 0.f);
+  bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 v01 = to_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
+      const bf16x2 v23 = to_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+      const u32x2 st = {__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
+      *(u32x2*)(op + db * 32 + 8 * i + 4 * hh) = st;
+    }
+  if (hh == 0) {
+    float lse;
+    if (invalid) lse = nanv;
+    else if (l_sum > 0.f) lse = (m_used + __builtin_amdgcn_logf(l_sum)) * 0.6931471805599453f;
+    else lse = ninf;
+    a.lse[head_row0 + qrow] = lse;
+  }
+}
+
+// Launches the variant (masked, mode, generic modifiers) chosen on the host; a
+// masked variant is never launched without a block map.
+template <int D>
+hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st) {
+  const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
+  if (masked && a.map == nullptr) return hipErrorInvalidValue;
+  if (masked) {
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kLinear, false, false>), grid, block, 0, st, a);
+    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kSoftcap, false, false>), grid, block, 0, st, a);
+    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kGeneric, true, true>), grid, block, 0, st, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kLinear, false, false>), grid, block, 0, st, a);
+    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kSoftcap, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kGeneric, true, true>), grid, block, 0, st, a);
+    else return hipErrorInvalidValue;  // (ALiBi on a causal mask always has a block map)
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bf16path
+}  // namespace attn119

@@ -1,6 +1,8 @@
-// Forward-pass kernels: bf16 inputs, head dim 128.
-#include "fwd_kernel.hpp"
+// Forward-pass kernels: bf16 inputs, head dim 128 (the software-pipelined kernel).
+#include "fwd_bf16.hpp"
 
 namespace attn119 {
-template hipError_t launch_fwd_family<128, kInBf16>(const FwdArgs&, bool, bool, bool, hipStream_t);
+namespace bf16path {
+template hipError_t launch<128>(const FwdArgs&, bool, int, bool, bool, hipStream_t);
+}  // namespace bf16path
 }  // namespace attn119

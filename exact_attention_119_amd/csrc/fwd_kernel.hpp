@@ -533,7 +533,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   l_sum += __shfl_xor(l_sum, 32);
   lq_sum += __shfl_xor(lq_sum, 32);
   if (!qvalid) return;
-  const float nanv = __builtin_nanf("");
+  const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
   const float inv = invalid ? nanv : (lq_sum > 0.f ? vs_max / lq_sum : 0.f);
   bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
 #pragma unroll

@@ -40,7 +40,7 @@ ATTN_QK_BF16 = 0
 ATTN_QK_E4M3 = 1
 
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
-           "attn_blockmap_status", "attn_check_args", "attn_fwd", "attn_status_str")
+           "attn_blockmap_status", "attn_check_args", "attn_fwd", "attn_fwd_kernel_name", "attn_status_str")
 
 
 class AttnError(RuntimeError):
@@ -92,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask), vp, sz,
                              ctypes.POINTER(attn_fp8), f32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_kernel_name.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(attn_fp8)]
+    lib.attn_fwd_kernel_name.restype = ctypes.c_char_p
     _LIB = lib
     return lib
 
@@ -161,6 +163,14 @@ def attn_check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, mask=None, blockm
     return load().attn_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                                   int(dtype), ctypes.byref(mask) if mask else None, _ptr(blockmap),
                                   int(blockmap_bytes), ctypes.byref(fp8) if fp8 else None, float(rescale_tau))
+
+
+def attn_fwd_kernel_name(d: int, dtype: int = ATTN_BF16, mask: Optional[attn_mask] = None,
+                         fp8: Optional[attn_fp8] = None) -> Optional[str]:
+    """The compiled kernel variant attn_fwd selects (host logic only), or None."""
+    r = load().attn_fwd_kernel_name(int(d), int(dtype), ctypes.byref(mask) if mask else None,
+                                    ctypes.byref(fp8) if fp8 else None)
+    return r.decode() if r is not None else None
 
 
 def attn_fwd(q, k, v, o, lse, *, scale: float, dtype: int = ATTN_BF16, mask: Optional[attn_mask] = None,

@@ -196,6 +196,15 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8,
                      float rescale_tau, void* stream);
 
+/*
+ * Name of the compiled kernel variant attn_fwd selects for these arguments, e.g.
+ * "bf16 d128 masked softcap" (host logic only, no HIP call, usable without a GPU);
+ * NULL when the combination is unsupported.  The string is static.  A "masked"
+ * variant reads the block map; it is chosen exactly when the mask has CAUSAL,
+ * WINDOW or DOCUMENT.
+ */
+const char* attn_fwd_kernel_name(int32_t d, int32_t dtype, const attn_mask* mask, const attn_fp8* fp8);
+
 /* Static description of a status code. */
 const char* attn_status_str(int32_t status);
 

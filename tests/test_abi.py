@@ -110,3 +110,30 @@ def test_fwd_rejects_before_launch(L):
     assert st == L.ATTN_ERR_UNSUPPORTED
     st = lib.attn_fwd(None, P, P, P, P, 1, 1, 16, 64, 0.1, 0, None, None, 0, None, 8.0, None)
     assert st == L.ATTN_ERR_INVALID_ARG
+
+
+def test_kernel_variant_selection(L):
+    """A masked kernel variant (the one that reads the block map) is selected exactly
+    when the mask has a positional flag; the score-modifier mode follows the flags."""
+    C, WI, DOC, AL, SC = L.ATTN_CAUSAL, L.ATTN_WINDOW, L.ATTN_DOCUMENT, L.ATTN_ALIBI, L.ATTN_SOFTCAP
+    name = lambda d, flags, **kw: L.attn_fwd_kernel_name(d, 0, L.make_mask(flags, **kw) if flags else None)
+    for d in (64, 128):
+        assert name(d, 0) == f"bf16 d{d} unmasked linear"
+        assert name(d, SC, softcap=5.0) == f"bf16 d{d} unmasked softcap"
+        assert name(d, AL) == f"bf16 d{d} unmasked generic-alibi"
+        assert name(d, AL | SC, softcap=5.0) == f"bf16 d{d} unmasked generic-alibi-softcap"
+        assert name(d, C) == f"bf16 d{d} masked linear"
+        assert name(d, C | WI | SC, window=9, softcap=50.0) == f"bf16 d{d} masked softcap"
+        assert name(d, C | DOC | AL, doc_id=P) == f"bf16 d{d} masked alibi-causal"
+        assert name(d, WI | AL, window=9) == f"bf16 d{d} masked generic-alibi"
+        assert name(d, DOC | AL | SC, doc_id=P, softcap=1.0) == f"bf16 d{d} masked generic-alibi-softcap"
+    for flags in range(32):
+        kw = dict(window=3 if flags & WI else 0, softcap=2.0 if flags & SC else 0.0,
+                  doc_id=P if flags & DOC else None)
+        n = name(128, flags, **kw)
+        assert n is not None and ("unmasked" not in n) == bool(flags & (C | WI | DOC)), (flags, n)
+    fp8 = L.make_fp8(P, P, P)
+    assert L.attn_fwd_kernel_name(128, 1, None, fp8) == "fp8 d128 unmasked none"
+    assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8) == "fp8 d64 masked alibi"
+    assert L.attn_fwd_kernel_name(96, 0, None, None) is None
+    assert L.attn_fwd_kernel_name(128, 1, None, None) is None
