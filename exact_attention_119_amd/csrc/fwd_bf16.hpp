@@ -186,13 +186,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   const int nblk = nfull + npart;
   const int nsteps = 2 * nblk;
 
-  // first key of step s (blocks: FULL list, then PARTIAL list)
+  // Steps walk the PARTIAL blocks first (masked, one step at a time), then the FULL
+  // blocks (software-pipelined, no mask code).  First key of step s:
   auto step_k0 = [&](int s) -> int {
     const int blk = s >> 1;
-    int kb = blk;
+    int kb;
     if constexpr (MASKED) {
-      kb = blk < nfull ? flist[blk] : plist[blk - nfull];
+      kb = blk < npart ? plist[blk] : flist[blk - npart];
       kb = min(max(kb, 0), nqb - 1);  // a corrupted map never addresses outside the head
+    } else {
+      kb = blk < npart ? nqb - 1 : blk - npart;  // the ragged tail block is the PARTIAL one
     }
     return kb * 128 + (s & 1) * BN;
   };
@@ -294,12 +297,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   float lq_sum = 0.f;  // sum of p as rounded to bf16, the normaliser of O
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  // Mask, score modifiers and row maximum of the raw S^T accumulators of a step whose
-  // first key is k0.  Leaves in sacc what the exponential phase consumes (raw s,
-  // softcap r, ALiBi y or the full score x) and returns the row maximum of the
-  // scores in log2 units (both lane halves), -inf for a row with no visible key.
-  // Hidden keys (PARTIAL blocks only: a uniform branch) become -inf (softcap: r=+inf).
-  auto prepare = [&](f32x16 (&sacc)[2], int k0, bool partial) -> float {
+  // Mask (PARTIAL steps only), score modifiers and row maximum of the raw S^T
+  // accumulators of a step whose first key is k0.  Leaves in sacc what the
+  // exponential phase consumes (raw s, softcap r, ALiBi y or the full score x) and
+  // returns the row maximum of the scores in log2 units (both lane halves), -inf for
+  // a row with no visible key.  Hidden keys become -inf (softcap: r = +inf).
+  auto prepare = [&](auto mask_tag, f32x16 (&sacc)[2], int k0) -> float {
+    constexpr bool MASK = decltype(mask_tag)::value;
     float mx;
     if constexpr (MODE == kAlibiCausal) {
       // y = s*c + slope*key_off; the row part slope*(k0 + 4hh - q) is added to the max
@@ -326,7 +330,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
           sacc[bk][r] = x;
         }
     }
-    if (partial) {
+    if constexpr (MASK) {
       const int rlo = lo_q - (k0 + 4 * hh), rhi = hi_q - (k0 + 4 * hh);
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
@@ -352,7 +356,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
         for (int r = 0; r < 16; ++r) {
           const float sv = sacc[bk][r];
           const float rr = rcp_(exp2_(sv * sc2) + 1.f);
-          sacc[bk][r] = sv == ninf ? __builtin_inff() : rr;
+          if constexpr (MASK) sacc[bk][r] = sv == ninf ? __builtin_inff() : rr;
+          else sacc[bk][r] = rr;
         }
       const float xm = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(mx * sc2) + 1.f), cap2);
       mx = mx == ninf ? ninf : xm;
@@ -392,22 +397,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   lds_u8* const vl0 = (lds_u8*)v_lds0;
   lds_u8* const vl1 = (lds_u8*)v_lds1;
 
-  // One pipelined step s.  On entry: S(s) in scur, already prepared, with its row
-  // maximum mcur; K(s+1) and V(s) requested into knext and vcur.
-  //   1. wait for this wave's loads, barrier (all loads in; all reads of step s-1 done)
-  //   2. request K(s+2) into kcur and V(s+1) into vnext
-  //   3. threshold rescale for step s
-  //   4. S(s+1) = K(s+1) Q^T interleaved with P(s)
-  //   5. O += V(s) P(s), then prepare S(s+1)
-  auto step = [&](int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur, lds_u8* vnext, f32x16 (&scur)[2],
-                  f32x16 (&snext)[2], float& mcur) {
-    wait_vmem();
-    __syncthreads();
-    const bool has_next = s + 1 < nsteps;
-    if (s + 2 < nsteps) issue_k(s + 2, kcur);
-    if (has_next) issue_v(s + 1, vnext);
-    const int k0 = step_k0(s);
-
+  // threshold rescale of the running state for a step whose row maximum is mcur;
+  // returns the exponent offset of the step's exponentials
+  auto rescale = [&](float mcur, int k0) -> float {
     const float m_new = __builtin_fmaxf(m_used, mcur);
     const bool need = m_new > m_used + tau;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -418,14 +410,77 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     }
-    // exponent offset; m_used is -inf only while every key seen so far is hidden
-    // (then p = 0 whatever the offset)
+    // m_used is -inf only while every key seen so far is hidden (then p = 0 whatever
+    // the offset)
     float moff = m_used == ninf ? 0.f : m_used;
     if constexpr (MODE == kAlibiCausal) moff = __builtin_fmaf(-slope2, (float)(k0 + 4 * hh - qrow), moff);
+    return moff;
+  };
+  auto qk_full = [&](const lds_u8* kt, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      sacc[bk] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NQC; ++c)
+        sacc[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kt, bk, c), qf[c], sacc[bk], 0, 0, 0);
+    }
+  };
+  auto pv_full = [&](const lds_u8* vt, const bf16x8 (&pf)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vt, ks, db), pf[ks], oacc[db], 0, 0, 0);
+  };
 
-    bf16x8 pf[4];
+  f32x16 sa[2], sb[2];
+  bf16x8 pf[4];
+
+  // ---- phase 1: PARTIAL blocks, one step at a time (K(s), V(s) in buffers s % 2) ----------
+  const int np_steps = 2 * npart;
+  if (nsteps > 0) {
+    issue_k(0, kl0);
+    issue_v(0, vl0);
+  }
+  for (int s = 0; s < np_steps; ++s) {
+    lds_u8* const kc = (s & 1) ? kl1 : kl0;
+    lds_u8* const vc = (s & 1) ? vl1 : vl0;
+    wait_vmem();
+    __syncthreads();  // K(s), V(s) in; every read of step s-1 done
+    if (s + 1 < nsteps) {
+      issue_k(s + 1, (s & 1) ? kl0 : kl1);
+      issue_v(s + 1, (s & 1) ? vl0 : vl1);
+    }
+    const int k0 = step_k0(s);
+    qk_full(kc, sa);
+    const float moff = rescale(prepare(std::true_type{}, sa, k0), k0);
     float ls = 0.f, lqs = 0.f;
-    if (has_next) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(sa[sl >> 1], sl & 1, moff, ls, lqs);
+    l_sum += ls;
+    lq_sum += lqs;
+    pv_full(vc, pf);
+  }
+
+  // ---- phase 2: FULL blocks, software-pipelined ---------------------------------------------
+  // Step s (even steps: buffers 0 -> 1 and S in sa -> sb; odd steps the reverse).  On
+  // entry: S(s) in scur, prepared, with its row maximum mcur; K(s+1) and V(s)
+  // requested.
+  //   wait for this wave's loads, barrier (all loads in; all reads of step s-1 done);
+  //   request K(s+2) into kcur and V(s+1) into vnext; threshold rescale for step s;
+  //   S(s+1) = K(s+1) Q^T interleaved with P(s); O += V(s) P(s); prepare S(s+1).
+  auto step = [&](auto next_tag, auto issue_k_tag, int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur,
+                  lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr bool ISSUE_K = decltype(issue_k_tag)::value;
+    wait_vmem();
+    __syncthreads();
+    if constexpr (ISSUE_K) issue_k(s + 2, kcur);
+    if constexpr (NEXT) issue_v(s + 1, vnext);
+    const float moff = rescale(mcur, step_k0(s));
+
+    float ls = 0.f, lqs = 0.f;
+    if constexpr (NEXT) {
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk) {
         snext[bk] = f32x16{};
@@ -444,39 +499,26 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     }
     l_sum += ls;
     lq_sum += lqs;
-
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vcur, ks, db), pf[ks], oacc[db], 0, 0, 0);
-    if (has_next) {
-      const int k1 = step_k0(s + 1);
-      mcur = prepare(snext, k1, (s + 1) >> 1 >= nfull);
-    }
+    pv_full(vcur, pf);
+    if constexpr (NEXT) mcur = prepare(std::false_type{}, snext, step_k0(s + 1));
   };
+  constexpr std::true_type YES{};
+  constexpr std::false_type NO{};
 
-  f32x16 sa[2], sb[2];
-  float mcand = ninf;  // row maximum of the step about to be exponentiated
-  if (nsteps > 0) {
-    issue_k(0, kl0);
-    issue_v(0, vl0);
-    if (nsteps > 1) issue_k(1, kl1);
+  if (np_steps < nsteps) {
+    const int t = np_steps;  // first FULL step (even); K(t), V(t) requested
     wait_vmem();
-    __syncthreads();
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      sa[bk] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NQC; ++c)
-        sa[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kl0, bk, c), qf[c], sa[bk], 0, 0, 0);
+    __syncthreads();  // K(t) in; every read of step t-1 done
+    if (t + 1 < nsteps) issue_k(t + 1, kl1);
+    qk_full(kl0, sa);
+    float mcand = prepare(std::false_type{}, sa, step_k0(t));
+    int s = t;
+    for (; s + 2 < nsteps; s += 2) {
+      step(YES, YES, s, kl0, kl1, vl0, vl1, sa, sb, mcand);
+      step(YES, YES, s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
     }
-    mcand = prepare(sa, step_k0(0), nfull == 0);
-  }
-  // nsteps is even: step 2j uses buffers 0 -> 1 and S in sa -> sb, step 2j+1 the reverse
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, kl0, kl1, vl0, vl1, sa, sb, mcand);
-    step(s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
+    step(YES, NO, s, kl0, kl1, vl0, vl1, sa, sb, mcand);
+    step(NO, NO, s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
   }
 
   // ---- epilogue -------------------------------------------------------------------------
