@@ -30,8 +30,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["exact_attention_119_amd/csrc/fwd_kernel.hpp", "exact_attention_119_amd/csrc/fwd_args.hpp",
-                  "exact_attention_119_amd/csrc/common.hpp"]
+KERNEL_SOURCES = ["exact_attention_119_amd/csrc/fwd_bf16.hpp", "exact_attention_119_amd/csrc/fwd_kernel.hpp",
+                  "exact_attention_119_amd/csrc/fwd_args.hpp", "exact_attention_119_amd/csrc/common.hpp",
+                  "exact_attention_119_amd/build.py"]
+METRIC = "attention fwd TFLOP/s (unmasked FLOPs) and % of MI355X bf16/fp8 MFMA peak"
 
 
 def log(*a):
@@ -196,12 +198,14 @@ def main(argv=None):
     achieved = flop_per_step / (fwd_avg * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
     traffic = traffic_record(name)
+    from exact_attention_119_amd import lib as L
+    kernel_name = L.attn_fwd_kernel_name(p.d, dp.dtype, dp.mask, dp.fp8)
     alg_bytes = p.B * p.H * (p.N * p.d * (3 * (1 if dtype == "fp8" else 2) + 2) + 4 * p.N)
     log(f"bench: algorithmic HBM bytes per launch {alg_bytes}; at the forward kernel's time that is "
         f"{alg_bytes / (fwd_avg * 1e-3) / 1e9:.1f} GB/s of {HBM_PEAK_GBS:.0f}")
 
     out = {
-        "metric": "attention fwd TFLOP/s (unmasked FLOPs)",
+        "metric": METRIC,
         "value": round(flop_per_step / (step_ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -218,7 +222,8 @@ def main(argv=None):
                    "step": "block-map build + forward pass", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "kernel_avg_ms": round(fwd_avg, 5)},
+                     "kernel": kernel_name, "kernel_avg_ms": round(fwd_avg, 5),
+                     "kernel_median_ms": round(fwd_ms[len(fwd_ms) // 2], 5)},
     }
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a bounded sample ...")

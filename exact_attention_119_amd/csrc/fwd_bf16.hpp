@@ -481,26 +481,49 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
     float ls = 0.f, lqs = 0.f;
     if constexpr (NEXT) {
+      // S(s+1) = K(s+1) Q^T, the two 32-key blocks interleaved, with P slices 0 and 1
+      // of step s computed under these MFMAs ...
+      snext[0] = f32x16{};
+      snext[1] = f32x16{};
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        snext[bk] = f32x16{};
+      for (int c = 0; c < NQC; ++c) {
+        snext[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(knext, 0, c), qf[c], snext[0], 0, 0, 0);
+        snext[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(knext, 1, c), qf[c], snext[1], 0, 0, 0);
+        if (c == NQC / 2 - 1) pf[0] = pslice(scur[0], 0, moff, ls, lqs);
+        if (c == NQC - 1) pf[1] = pslice(scur[0], 1, moff, ls, lqs);
+      }
+      // ... O += V(s) P(s) with slices 2 and 3 under the first half of its MFMAs and
+      // the maximum of S(s+1) under the second half
 #pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-          snext[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(knext, bk, c), qf[c], snext[bk], 0, 0, 0);
-          if (c % (NQC / 2) == NQC / 2 - 1) {  // two P slices per 32-key block of S(s+1)
-            const int sl = bk * 2 + c / (NQC / 2);
-            pf[sl] = pslice(scur[sl >> 1], sl & 1, moff, ls, lqs);
-          }
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vcur, ks, db), pf[ks], oacc[db], 0, 0, 0);
+        if (ks < 2) pf[ks + 2] = pslice(scur[1], ks, moff, ls, lqs);
+      }
+      mcur = prepare(std::false_type{}, snext, step_k0(s + 1));
+      // issue order (MFMA 32 cycles each): phase A 2*NQC MFMAs, one K read and four
+      // VALU ops after each; phase B 4*NDB MFMAs, two V reads and three VALU ops after each
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NQC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
     } else {
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(scur[sl >> 1], sl & 1, moff, ls, lqs);
+      pv_full(vcur, pf);
     }
     l_sum += ls;
     lq_sum += lqs;
-    pv_full(vcur, pf);
-    if constexpr (NEXT) mcur = prepare(std::false_type{}, snext, step_k0(s + 1));
   };
   constexpr std::true_type YES{};
   constexpr std::false_type NO{};
