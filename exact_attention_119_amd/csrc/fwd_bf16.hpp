@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
   const int hh = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
@@ -188,12 +188,35 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   // Steps walk the PARTIAL blocks first (masked, one step at a time), then the FULL
   // blocks (software-pipelined, no mask code).  First key of step s:
+  // (masked: the block order sits in VGPR lanes -- lane i of kbv[r] holds block
+  // 64r + i -- so a lookup is one v_readlane with no memory latency; orders longer
+  // than 128 blocks read the rest from the map)
+  constexpr int NKV = 2;
+  int kbv[NKV];
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int r = 0; r < NKV; ++r) {
+      const int j = 64 * r + lane;
+      int kb = 0;
+      if (j < nblk) kb = j < npart ? plist[j] : flist[j - npart];
+      kbv[r] = min(max(kb, 0), nqb - 1);  // a corrupted map never addresses outside the head
+    }
+  }
   auto step_k0 = [&](int s) -> int {
     const int blk = s >> 1;
     int kb;
     if constexpr (MASKED) {
-      kb = blk < npart ? plist[blk] : flist[blk - npart];
-      kb = min(max(kb, 0), nqb - 1);  // a corrupted map never addresses outside the head
+      if (blk < 64) {
+        kb = __builtin_amdgcn_readlane(kbv[0], blk);
+      } else if (blk < 64 * NKV) {
+        kb = __builtin_amdgcn_readlane(kbv[1], blk - 64);
+      } else {
+        // (the empty asm keeps the compiler from hoisting this rare scalar load, and its
+        // wait, above the branch into every step)
+        asm volatile("" ::: "memory");
+        kb = blk < npart ? plist[blk] : flist[blk - npart];
+        kb = min(max(kb, 0), nqb - 1);
+      }
     } else {
       kb = blk < npart ? nqb - 1 : blk - npart;  // the ragged tail block is the PARTIAL one
     }
