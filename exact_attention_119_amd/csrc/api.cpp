@@ -261,6 +261,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     a.mflags = flags & (ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT);
     a.window = (flags & ATTN_WINDOW) ? mask->window : 0;
   }
+  // Causal masks give the last row blocks of a head the most key blocks.  When the grid
+  // is only a few workgroups per slot (2 per CU on 256 CUs), take them heaviest-first.
+  constexpr long kSlots = 2 * 256;
+  const long items = (long)B * H * a.nqb;
+  a.order = ((flags & ATTN_CAUSAL) && items < 4 * kSlots) ? kOrderHeavyFirst : kOrderHeadMajor;
   hipError_t e;
   const hipStream_t s = (hipStream_t)stream;
   const FwdVariant var = select_variant(d, dtype, mask, fp8);

@@ -26,6 +26,35 @@ struct FwdArgs {
   MapLayout lay;
   uint32_t mflags;            // positional mask flags the map was built for
   int window;
+  int order;                  // work order: kOrderHeadMajor or kOrderHeavyFirst
 };
+
+// Order in which workgroups take (b*H + h, row block) work items.  Workgroup L runs on
+// XCD L % 8 (the dispatcher deals workgroups round-robin over the 8 XCDs).
+//  kOrderHeadMajor : each XCD takes a contiguous range of items, head by head, a head's
+//                    row blocks last-first -- the row blocks sharing a head's K/V run
+//                    on one XCD at the same time (L2 reuse).
+//  kOrderHeavyFirst: items in row-block-major order, last row block first: under a
+//                    causal mask the last row blocks carry the most key blocks, so this
+//                    is longest-first list scheduling, which evens out the finish times
+//                    when there are only a few workgroups per slot.  With B*H a multiple
+//                    of 8 a head still stays on one XCD (h = L mod B*H).
+constexpr int kOrderHeadMajor = 0, kOrderHeavyFirst = 1;
+
+__device__ __forceinline__ void work_item(const FwdArgs& a, int L, int& bh, int& qb) {
+  const int nqb = a.nqb;
+  if (a.order == kOrderHeavyFirst) {
+    const int BH = a.B * a.H;
+    const int r = L / BH;
+    bh = L - r * BH;
+    qb = nqb - 1 - r;
+  } else {
+    const int T = a.B * a.H * nqb;
+    const int xcd = L & 7, jx = L >> 3;
+    const int wid = xcd * (T >> 3) + min(xcd, T & 7) + jx;
+    bh = wid / nqb;
+    qb = nqb - 1 - (wid - bh * nqb);
+  }
+}
 
 }  // namespace attn119

@@ -92,6 +92,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return a + b;
 }
 
+// Pins v to this point of the program (an empty volatile asm that reads and rewrites
+// it in a VGPR): whatever computes v stays before it, whatever uses the new v stays
+// after it, so neither can drift across the scheduling fences around it.
+template <typename T>
+__device__ __forceinline__ void pin(T& v) {
+  static_assert(sizeof(T) == 4, "one VGPR");
+  asm volatile("" : "+v"(v));
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One 16-byte chunk per lane from a buffer into LDS at lds_base + 16*lane.
@@ -133,14 +142,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   const int N = a.N;
   const int nqb = a.nqb;
 
-  // ---- XCD-aware work mapping: consecutive workgroups of one XCD take consecutive
-  //      row blocks of one (b, h); row blocks of a head run last-first --------------
-  const int T = a.B * a.H * nqb;
-  const int L = blockIdx.x;
-  const int xcd = L & 7, jx = L >> 3;
-  const int wid = xcd * (T >> 3) + min(xcd, T & 7) + jx;
-  const int bh = wid / nqb;
-  const int qb = nqb - 1 - (wid - bh * nqb);
+  // ---- XCD-aware work mapping (head-major or heaviest-first, chosen on the host) -----
+  int bh, qb;
+  work_item(a, blockIdx.x, bh, qb);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
 
@@ -320,97 +324,106 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   float lq_sum = 0.f;  // sum of p as rounded to bf16, the normaliser of O
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  // Mask (PARTIAL steps only), score modifiers and row maximum of the raw S^T
-  // accumulators of a step whose first key is k0.  Leaves in sacc what the
-  // exponential phase consumes (raw s, softcap r, ALiBi y or the full score x) and
-  // returns the row maximum of the scores in log2 units (both lane halves), -inf for
-  // a row with no visible key.  Hidden keys become -inf (softcap: r = +inf).
-  auto prepare = [&](auto mask_tag, f32x16 (&sacc)[2], int k0) -> float {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    float mx;
+  // ---- score modifiers, mask and row maximum ---------------------------------------------
+  // Score of one accumulator element before the maximum is taken (kq = k0 + 4hh - q):
+  // ALiBi-causal and generic modes transform it here; linear and softcap keep raw s
+  // (both are monotone in s, so the maximum is taken on s and converted afterwards).
+  auto xform = [&](float sraw, int bk, int r, int kq) -> float {
     if constexpr (MODE == kAlibiCausal) {
       // y = s*c + slope*key_off; the row part slope*(k0 + 4hh - q) is added to the max
-      // here and subtracted from the exponent offset in the exponential phase
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sacc[bk][r] = __builtin_fmaf(sacc[bk][r], ct, slope2 * (float)key_off(bk, r));
+      // and subtracted from the exponent offset instead
+      return __builtin_fmaf(sraw, ct, slope2 * (float)key_off(bk, r));
     } else if constexpr (MODE == kGeneric) {
-      const int kq = k0 + 4 * hh - qrow;
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sraw = sacc[bk][r];
-          float x;
-          if constexpr (GSOFTCAP) x = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(sraw * sc2) + 1.f), cap2);
-          else x = sraw * ct;
-          if constexpr (GALIBI) {
-            const float dist = (float)(kq + key_off(bk, r));
-            x = __builtin_fmaf(slope2, alibi_abs ? -__builtin_fabsf(dist) : dist, x);
-          }
-          sacc[bk][r] = x;
-        }
+      float x;
+      if constexpr (GSOFTCAP) x = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(sraw * sc2) + 1.f), cap2);
+      else x = sraw * ct;
+      if constexpr (GALIBI) {
+        const float dist = (float)(kq + key_off(bk, r));
+        x = __builtin_fmaf(slope2, alibi_abs ? -__builtin_fabsf(dist) : dist, x);
+      }
+      return x;
+    } else {
+      return sraw;
     }
-    if constexpr (MASK) {
-      const int rlo = lo_q - (k0 + 4 * hh), rhi = hi_q - (k0 + 4 * hh);
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = key_off(bk, r);
-          sacc[bk][r] = (off < rlo || off > rhi) ? ninf : sacc[bk][r];
-        }
-    }
-    mx = __builtin_fmaxf(sacc[0][0], sacc[0][1]);
-#pragma unroll
-    for (int i = 2; i < 32; i += 2)
-      mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[i >> 4][i & 15], sacc[i >> 4][(i & 15) + 1]));
+  };
+  // Row maximum in log2 units (both lane halves) from the in-lane maximum mx of the
+  // transformed scores of a step whose first key is k0; -inf for a row with no visible key.
+  auto finalize = [&](float mx, int k0) -> float {
     if constexpr (MODE == kAlibiCausal) mx = __builtin_fmaf(slope2, (float)(k0 + 4 * hh - qrow), mx);
     mx = pair_max(mx);
     if constexpr (MODE == kLinear) {
       mx *= ct;  // ct > 0 keeps the order; -inf stays -inf
     } else if constexpr (MODE == kSoftcap) {
-      // r = 1 / (exp2(2 s c / cap) + 1); a hidden key (s = -inf) gets r = +inf, p = 0
+      const float xm = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(mx * sc2) + 1.f), cap2);
+      mx = mx == ninf ? ninf : xm;
+    }
+    return mx;
+  };
+  // Transform, mask (MASK: PARTIAL steps) and row maximum of the S^T accumulators of a
+  // step whose first key is k0.  Hidden keys become -inf.  With RAW false a softcap step
+  // also leaves r = 1 / (exp2(2 s c / cap) + 1) in sacc (r = +inf for a hidden key, so
+  // that p = 0); with RAW true softcap scores stay raw and the exponential phase forms r.
+  auto prepare = [&](auto mask_tag, auto raw_tag, f32x16 (&sacc)[2], int k0) -> float {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool RAW = decltype(raw_tag)::value;
+    const int kq = k0 + 4 * hh - qrow;
+    const int rlo = lo_q - (k0 + 4 * hh), rhi = hi_q - (k0 + 4 * hh);
+    float mx = ninf;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = xform(sacc[bk][r], bk, r, kq);
+        if constexpr (MASK) {
+          const int off = key_off(bk, r);
+          x = (off < rlo || off > rhi) ? ninf : x;
+        }
+        sacc[bk][r] = x;
+        mx = __builtin_fmaxf(mx, x);
+      }
+    if constexpr (MODE == kSoftcap && !RAW) {
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float sv = sacc[bk][r];
           const float rr = rcp_(exp2_(sv * sc2) + 1.f);
-          if constexpr (MASK) sacc[bk][r] = sv == ninf ? __builtin_inff() : rr;
-          else sacc[bk][r] = rr;
+          sacc[bk][r] = sv == ninf ? __builtin_inff() : rr;
         }
-      const float xm = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(mx * sc2) + 1.f), cap2);
-      mx = mx == ninf ? ninf : xm;
     }
-    return mx;
+    return finalize(mx, k0);
   };
 
-  // P of one 16-key slice (registers 8g..8g+7 of block bk) packed as the bf16 B
-  // operand; adds the unrounded and the rounded sums.  moff: exponent offset.
-  auto pslice = [&](const f32x16& sacc, int g, float moff, float& ls, float& lqs) -> bf16x8 {
+  // Exponentials of two scores (as prepare left them; RAW: softcap scores untransformed)
+  // packed as a bf16 pair of the B operand; adds the unrounded and the rounded sums.
+  // moff: exponent offset.
+  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls, float& lqs) -> uint32_t {
+    constexpr bool RAW = decltype(raw_tag)::value;
+    float p0, p1;
+    if constexpr (MODE == kLinear) {
+      p0 = exp2_(__builtin_fmaf(s0, ct, -moff));
+      p1 = exp2_(__builtin_fmaf(s1, ct, -moff));
+    } else if constexpr (MODE == kSoftcap) {
+      if constexpr (RAW) {
+        s0 = rcp_(exp2_(s0 * sc2) + 1.f);
+        s1 = rcp_(exp2_(s1 * sc2) + 1.f);
+      }
+      p0 = exp2_(__builtin_fmaf(-2.f * cap2, s0, cap2 - moff));
+      p1 = exp2_(__builtin_fmaf(-2.f * cap2, s1, cap2 - moff));
+    } else {
+      p0 = exp2_(s0 - moff);
+      p1 = exp2_(s1 - moff);
+    }
+    ls += p0 + p1;
+    const bf16x2 pb = to_bf16x2(p0, p1);
+    lqs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lqs, false);
+    return __builtin_bit_cast(uint32_t, pb);
+  };
+  // P of one 16-key slice (registers 8g..8g+7 of block bk) as the bf16 B operand
+  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls, float& lqs) -> bf16x8 {
     uint32_t pk[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = g * 8 + 2 * t;
-      float p0, p1;
-      if constexpr (MODE == kLinear) {
-        p0 = exp2_(__builtin_fmaf(sacc[r], ct, -moff));
-        p1 = exp2_(__builtin_fmaf(sacc[r + 1], ct, -moff));
-      } else if constexpr (MODE == kSoftcap) {
-        p0 = exp2_(__builtin_fmaf(-2.f * cap2, sacc[r], cap2 - moff));
-        p1 = exp2_(__builtin_fmaf(-2.f * cap2, sacc[r + 1], cap2 - moff));
-      } else {
-        p0 = exp2_(sacc[r] - moff);
-        p1 = exp2_(sacc[r + 1] - moff);
-      }
-      ls += p0 + p1;
-      const bf16x2 pb = to_bf16x2(p0, p1);
-      lqs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lqs, false);
-      pk[t] = __builtin_bit_cast(uint32_t, pb);
-    }
+    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls, lqs);
     const u32x4 v4 = {pk[0], pk[1], pk[2], pk[3]};
     return __builtin_bit_cast(bf16x8, v4);
   };
@@ -458,6 +471,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   f32x16 sa[2], sb[2];
   bf16x8 pf[4];
+  constexpr std::true_type YES{};
+  constexpr std::false_type NO{};
 
   // ---- phase 1: PARTIAL blocks, one step at a time (K(s), V(s) in buffers s % 2) ----------
   const int np_steps = 2 * npart;
@@ -476,10 +491,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     }
     const int k0 = step_k0(s);
     qk_full(kc, sa);
-    const float moff = rescale(prepare(std::true_type{}, sa, k0), k0);
+    const float moff = rescale(prepare(YES, NO, sa, k0), k0);
     float ls = 0.f, lqs = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(sa[sl >> 1], sl & 1, moff, ls, lqs);
+    for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(NO, sa[sl >> 1], sl & 1, moff, ls, lqs);
     l_sum += ls;
     lq_sum += lqs;
     pv_full(vc, pf);
@@ -487,11 +502,25 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   // ---- phase 2: FULL blocks, software-pipelined ---------------------------------------------
   // Step s (even steps: buffers 0 -> 1 and S in sa -> sb; odd steps the reverse).  On
-  // entry: S(s) in scur, prepared, with its row maximum mcur; K(s+1) and V(s)
-  // requested.
+  // entry: S(s) in scur, prepared (softcap scores raw), with its row maximum mcur; K(s+1)
+  // and V(s) requested.
   //   wait for this wave's loads, barrier (all loads in; all reads of step s-1 done);
   //   request K(s+2) into kcur and V(s+1) into vnext; threshold rescale for step s;
-  //   S(s+1) = K(s+1) Q^T interleaved with P(s); O += V(s) P(s); prepare S(s+1).
+  //   then NS issue slots, one MFMA each: slots [0, NQ) S(s+1) = K(s+1) Q^T, slots
+  //   [NQ, NS) O += V(s) P(s).  Every LDS fragment is read PD slots before its MFMA.
+  //   The 16 exponential pairs of P(s) take slots [0, WP), pair k in slot k*WP/16, each
+  //   finished before the P.V MFMA that consumes it; the transform and maximum of
+  //   S(s+1) take slots [WP, NS), after its MFMAs have completed.  Scheduling fences
+  //   between the slots keep this interleaving, so the VALU work of a slot runs under
+  //   that slot's MFMA.
+  constexpr int NQ = 2 * NQC, NP = 4 * NDB, NS = NQ + NP;
+  constexpr int PD = 3;
+  constexpr int WP = NQ + NP / 2;
+  constexpr int EPS = 32 / (NS - WP);  // S(s+1) elements per maximum slot
+  static_assert(EPS * (NS - WP) == 32, "maximum slots");
+  static_assert(((4 * 0 + 3) * WP) / 16 < NQ + NDB * 0 && ((4 * 1 + 3) * WP) / 16 < NQ + NDB * 1 &&
+                    ((4 * 2 + 3) * WP) / 16 < NQ + NDB * 2 && ((4 * 3 + 3) * WP) / 16 < NQ + NDB * 3,
+                "every P slice is complete before its first P.V MFMA");
   auto step = [&](auto next_tag, auto issue_k_tag, int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur,
                   lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
     constexpr bool NEXT = decltype(next_tag)::value;
@@ -504,52 +533,67 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
     float ls = 0.f, lqs = 0.f;
     if constexpr (NEXT) {
-      // S(s+1) = K(s+1) Q^T, the two 32-key blocks interleaved, with P slices 0 and 1
-      // of step s computed under these MFMAs ...
+      const int k1 = step_k0(s + 1);
+      const int kq1 = k1 + 4 * hh - qrow;
+      auto frag = [&](int i) -> bf16x8 {
+        if (i < NQ) return kfrag(knext, i & 1, i >> 1);
+        const int j = i - NQ;
+        return vfrag(vcur, j / NDB, j % NDB);
+      };
+      bf16x8 fr[PD + 1];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) fr[i] = frag(i);
       snext[0] = f32x16{};
       snext[1] = f32x16{};
+      uint32_t pk[16];
+      float mx = ninf;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < NQC; ++c) {
-        snext[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(knext, 0, c), qf[c], snext[0], 0, 0, 0);
-        snext[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(knext, 1, c), qf[c], snext[1], 0, 0, 0);
-        if (c == NQC / 2 - 1) pf[0] = pslice(scur[0], 0, moff, ls, lqs);
-        if (c == NQC - 1) pf[1] = pslice(scur[0], 1, moff, ls, lqs);
+      for (int i = 0; i < NS; ++i) {
+        if (i + PD < NS) fr[(i + PD) % (PD + 1)] = frag(i + PD);
+        if (i < NQ) {
+          snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], snext[i & 1], 0, 0, 0);
+        } else {
+          const int j = i - NQ, ks = j / NDB, db = j % NDB;
+          const u32x4 v4 = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4),
+                                                             oacc[db], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if ((k * WP) / 16 == i) {
+            const int sl = k >> 2, r = (sl & 1) * 8 + 2 * (k & 3);
+            float s0 = scur[sl >> 1][r], s1 = scur[sl >> 1][r + 1];
+            pin(s0);
+            pin(s1);
+            pk[k] = ppair(YES, s0, s1, moff, ls, lqs);
+            pin(pk[k]);
+            pin(ls);
+            pin(lqs);
+          }
+        if (i >= WP) {
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int idx = (i - WP) * EPS + e, bk = idx >> 4, r = idx & 15;
+            float sv = snext[bk][r];
+            pin(sv);
+            const float x = xform(sv, bk, r, kq1);
+            snext[bk][r] = x;
+            mx = __builtin_fmaxf(mx, x);
+          }
+          pin(mx);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // ... O += V(s) P(s) with slices 2 and 3 under the first half of its MFMAs and
-      // the maximum of S(s+1) under the second half
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vcur, ks, db), pf[ks], oacc[db], 0, 0, 0);
-        if (ks < 2) pf[ks + 2] = pslice(scur[1], ks, moff, ls, lqs);
-      }
-      mcur = prepare(std::false_type{}, snext, step_k0(s + 1));
-      // issue order (MFMA 32 cycles each): phase A 2*NQC MFMAs, one K read and four
-      // VALU ops after each; phase B 4*NDB MFMAs, two V reads and three VALU ops after each
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * NQC; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4 * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
+      mcur = finalize(mx, k1);
     } else {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(scur[sl >> 1], sl & 1, moff, ls, lqs);
+      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls, lqs);
       pv_full(vcur, pf);
     }
     l_sum += ls;
     lq_sum += lqs;
   };
-  constexpr std::true_type YES{};
-  constexpr std::false_type NO{};
 
   if (np_steps < nsteps) {
     const int t = np_steps;  // first FULL step (even); K(t), V(t) requested
@@ -557,7 +601,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     __syncthreads();  // K(t) in; every read of step t-1 done
     if (t + 1 < nsteps) issue_k(t + 1, kl1);
     qk_full(kl0, sa);
-    float mcand = prepare(std::false_type{}, sa, step_k0(t));
+    float mcand = prepare(NO, YES, sa, step_k0(t));
     int s = t;
     for (; s + 2 < nsteps; s += 2) {
       step(YES, YES, s, kl0, kl1, vl0, vl1, sa, sb, mcand);

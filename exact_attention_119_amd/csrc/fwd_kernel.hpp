@@ -167,13 +167,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   const int N = a.N;
   const int nqb = a.nqb;
 
-  // ---- XCD-aware work mapping ------------------------------------------------
-  const int T = a.B * a.H * nqb;
-  const int L = blockIdx.x;
-  const int xcd = L & 7, jx = L >> 3;
-  const int wid = xcd * (T >> 3) + min(xcd, T & 7) + jx;
-  const int bh = wid / nqb;
-  const int qb = nqb - 1 - (wid - bh * nqb);
+  // ---- XCD-aware work mapping (head-major or heaviest-first, chosen on the host) ---
+  int bh, qb;
+  work_item(a, blockIdx.x, bh, qb);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
 
