@@ -46,6 +46,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "fwd_args.hpp"
@@ -59,6 +60,16 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // score-modifier modes
 constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -320,9 +331,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_used = ninf;
-  float l_sum = 0.f;   // sum of p (unrounded), for LSE
-  float lq_sum = 0.f;  // sum of p as rounded to bf16, the normaliser of O
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  float l_sum = 0.f;  // row sum of p (fp32, before rounding to bf16): LSE and the normaliser of O
 
   // ---- score modifiers, mask and row maximum ---------------------------------------------
   // Score of one accumulator element before the maximum is taken (kq = k0 + 4hh - q):
@@ -394,36 +403,35 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     return finalize(mx, k0);
   };
 
-  // Exponentials of two scores (as prepare left them; RAW: softcap scores untransformed)
-  // packed as a bf16 pair of the B operand; adds the unrounded and the rounded sums.
-  // moff: exponent offset.
-  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls, float& lqs) -> uint32_t {
-    constexpr bool RAW = decltype(raw_tag)::value;
-    float p0, p1;
-    if constexpr (MODE == kLinear) {
-      p0 = exp2_(__builtin_fmaf(s0, ct, -moff));
-      p1 = exp2_(__builtin_fmaf(s1, ct, -moff));
-    } else if constexpr (MODE == kSoftcap) {
-      if constexpr (RAW) {
-        s0 = rcp_(exp2_(s0 * sc2) + 1.f);
-        s1 = rcp_(exp2_(s1 * sc2) + 1.f);
-      }
-      p0 = exp2_(__builtin_fmaf(-2.f * cap2, s0, cap2 - moff));
-      p1 = exp2_(__builtin_fmaf(-2.f * cap2, s1, cap2 - moff));
-    } else {
-      p0 = exp2_(s0 - moff);
-      p1 = exp2_(s1 - moff);
-    }
+  // Exponentials of two scores, in three stages that the pipelined loop issues in
+  // different slots (the non-pipelined paths run them back to back):
+  //   pre  (softcap scores still raw only): r = 1 / (exp2(2 s c / cap) + 1)
+  //   expo p = 2^(score - moff) for the mode's score form
+  //   pack the bf16 pair of the B operand; adds both values to the row sum
+  auto p_pre = [&](float sv) -> float { return rcp_(exp2_(sv * sc2) + 1.f); };
+  auto p_exp = [&](float sv, float moff) -> float {
+    if constexpr (MODE == kLinear) return exp2_(__builtin_fmaf(sv, ct, -moff));
+    else if constexpr (MODE == kSoftcap) return exp2_(__builtin_fmaf(-2.f * cap2, sv, cap2 - moff));
+    else return exp2_(sv - moff);
+  };
+  auto p_pack = [&](float p0, float p1, float& ls) -> uint32_t {
     ls += p0 + p1;
-    const bf16x2 pb = to_bf16x2(p0, p1);
-    lqs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lqs, false);
-    return __builtin_bit_cast(uint32_t, pb);
+    return __builtin_bit_cast(uint32_t, to_bf16x2(p0, p1));
+  };
+  // all three stages of one pair (RAW: softcap scores untransformed)
+  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls) -> uint32_t {
+    constexpr bool RAW = decltype(raw_tag)::value;
+    if constexpr (MODE == kSoftcap && RAW) {
+      s0 = p_pre(s0);
+      s1 = p_pre(s1);
+    }
+    return p_pack(p_exp(s0, moff), p_exp(s1, moff), ls);
   };
   // P of one 16-key slice (registers 8g..8g+7 of block bk) as the bf16 B operand
-  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls, float& lqs) -> bf16x8 {
+  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls) -> bf16x8 {
     uint32_t pk[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls, lqs);
+    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls);
     const u32x4 v4 = {pk[0], pk[1], pk[2], pk[3]};
     return __builtin_bit_cast(bf16x8, v4);
   };
@@ -442,7 +450,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       const float alpha = need ? exp2_(m_used - m_new) : 1.f;
       m_used = need ? m_new : m_used;
       l_sum *= alpha;
-      lq_sum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     }
@@ -492,11 +499,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     const int k0 = step_k0(s);
     qk_full(kc, sa);
     const float moff = rescale(prepare(YES, NO, sa, k0), k0);
-    float ls = 0.f, lqs = 0.f;
+    float ls = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(NO, sa[sl >> 1], sl & 1, moff, ls, lqs);
+    for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(NO, sa[sl >> 1], sl & 1, moff, ls);
     l_sum += ls;
-    lq_sum += lqs;
     pv_full(vc, pf);
   }
 
@@ -508,8 +514,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   //   request K(s+2) into kcur and V(s+1) into vnext; threshold rescale for step s;
   //   then NS issue slots, one MFMA each: slots [0, NQ) S(s+1) = K(s+1) Q^T, slots
   //   [NQ, NS) O += V(s) P(s).  Every LDS fragment is read PD slots before its MFMA.
-  //   The 16 exponential pairs of P(s) take slots [0, WP), pair k in slot k*WP/16, each
-  //   finished before the P.V MFMA that consumes it; the transform and maximum of
+  //   The 16 exponential pairs of P(s) start in slots [0, WP), pair k in slot k*WP/16,
+  //   its later stages one and two slots on, each packed before the P.V MFMA that
+  //   consumes it; the transform and maximum of
   //   S(s+1) take slots [WP, NS), after its MFMAs have completed.  Scheduling fences
   //   between the slots keep this interleaving, so the VALU work of a slot runs under
   //   that slot's MFMA.
@@ -517,10 +524,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   constexpr int PD = 3;
   constexpr int WP = NQ + NP / 2;
   constexpr int EPS = 32 / (NS - WP);  // S(s+1) elements per maximum slot
+  constexpr bool PRE = MODE == kSoftcap;  // softcap scores reach the loop raw
+  constexpr int NSTG = PRE ? 3 : 2;       // slots a pair's stages span
   static_assert(EPS * (NS - WP) == 32, "maximum slots");
-  static_assert(((4 * 0 + 3) * WP) / 16 < NQ + NDB * 0 && ((4 * 1 + 3) * WP) / 16 < NQ + NDB * 1 &&
-                    ((4 * 2 + 3) * WP) / 16 < NQ + NDB * 2 && ((4 * 3 + 3) * WP) / 16 < NQ + NDB * 3,
-                "every P slice is complete before its first P.V MFMA");
+  static_assert(((4 * 0 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 0 &&
+                    ((4 * 1 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 1 &&
+                    ((4 * 2 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 2 &&
+                    ((4 * 3 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 3,
+                "every P slice is packed before its first P.V MFMA");
   auto step = [&](auto next_tag, auto issue_k_tag, int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur,
                   lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
     constexpr bool NEXT = decltype(next_tag)::value;
@@ -531,7 +542,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     if constexpr (NEXT) issue_v(s + 1, vnext);
     const float moff = rescale(mcur, step_k0(s));
 
-    float ls = 0.f, lqs = 0.f;
+    float ls = 0.f;
     if constexpr (NEXT) {
       const int k1 = step_k0(s + 1);
       const int kq1 = k1 + 4 * hh - qrow;
@@ -541,58 +552,78 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
         return vfrag(vcur, j / NDB, j % NDB);
       };
       bf16x8 fr[PD + 1];
-#pragma unroll
-      for (int i = 0; i < PD; ++i) fr[i] = frag(i);
+      static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic.value); });
       snext[0] = f32x16{};
       snext[1] = f32x16{};
       uint32_t pk[16];
+      float pv0[16], pv1[16];  // pair values between stages
       float mx = ninf;
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        if (i + PD < NS) fr[(i + PD) % (PD + 1)] = frag(i + PD);
-        if (i < NQ) {
+      static_for<NS>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PD < NS) fr[(i + PD) % (PD + 1)] = frag(i + PD);
+        if constexpr (i < NQ) {
           snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], snext[i & 1], 0, 0, 0);
         } else {
-          const int j = i - NQ, ks = j / NDB, db = j % NDB;
+          constexpr int j = i - NQ, ks = j / NDB, db = j % NDB;
           const u32x4 v4 = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4),
                                                              oacc[db], 0, 0, 0);
         }
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if ((k * WP) / 16 == i) {
-            const int sl = k >> 2, r = (sl & 1) * 8 + 2 * (k & 3);
+        // pair k: stages in slots a(k) (+1, +2), a(k) = k*WP/16; the instructions of
+        // one slot come from different pairs and do not wait on each other
+        static_for<16>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          constexpr int a = (k * WP) / 16;
+          constexpr int sl = k >> 2, r = (sl & 1) * 8 + 2 * (k & 3);
+          if constexpr (a == i) {
             float s0 = scur[sl >> 1][r], s1 = scur[sl >> 1][r + 1];
             pin(s0);
             pin(s1);
-            pk[k] = ppair(YES, s0, s1, moff, ls, lqs);
+            if constexpr (PRE) {
+              s0 = p_pre(s0);
+              s1 = p_pre(s1);
+            } else {
+              s0 = p_exp(s0, moff);
+              s1 = p_exp(s1, moff);
+            }
+            pin(s0);
+            pin(s1);
+            pv0[k] = s0;
+            pv1[k] = s1;
+          }
+          if constexpr (PRE && a + 1 == i) {
+            pv0[k] = p_exp(pv0[k], moff);
+            pv1[k] = p_exp(pv1[k], moff);
+            pin(pv0[k]);
+            pin(pv1[k]);
+          }
+          if constexpr (a + NSTG - 1 == i) {
+            pk[k] = p_pack(pv0[k], pv1[k], ls);
             pin(pk[k]);
             pin(ls);
-            pin(lqs);
           }
-        if (i >= WP) {
-#pragma unroll
-          for (int e = 0; e < EPS; ++e) {
-            const int idx = (i - WP) * EPS + e, bk = idx >> 4, r = idx & 15;
+        });
+        if constexpr (i >= WP) {
+          static_for<EPS>([&](auto ec) {
+            constexpr int idx = (i - WP) * EPS + decltype(ec)::value, bk = idx >> 4, r = idx & 15;
             float sv = snext[bk][r];
             pin(sv);
             const float x = xform(sv, bk, r, kq1);
             snext[bk][r] = x;
             mx = __builtin_fmaxf(mx, x);
-          }
+          });
           pin(mx);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
       mcur = finalize(mx, k1);
     } else {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls, lqs);
+      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls);
       pv_full(vcur, pf);
     }
     l_sum += ls;
-    lq_sum += lqs;
   };
 
   if (np_steps < nsteps) {
@@ -613,10 +644,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   // ---- epilogue -------------------------------------------------------------------------
   l_sum = pair_sum(l_sum);
-  lq_sum = pair_sum(lq_sum);
   if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
-  const float inv = invalid ? nanv : (lq_sum > 0.f ? 1.f / lq_sum : 0.f);
+  const float inv = invalid ? nanv : (l_sum > 0.f ? 1.f / l_sum : 0.f);
   bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
