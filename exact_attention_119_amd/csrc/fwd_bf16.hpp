@@ -377,19 +377,43 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     constexpr bool RAW = decltype(raw_tag)::value;
     const int kq = k0 + 4 * hh - qrow;
     const int rlo = lo_q - (k0 + 4 * hh), rhi = hi_q - (k0 + 4 * hh);
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[bk][r] = xform(sacc[bk][r], bk, r, kq);
+    if constexpr (MASK) {
+      // Only the bounds that hide a key of this step in some lane of the wave are
+      // applied (wave-uniform branches): a causal diagonal step needs the upper bound
+      // alone, a window's far edge the lower alone, and a wave whose 32 x 64 tile is
+      // all visible none.  Key offsets run from 0 to key_off(1, 15).
+      constexpr int kOffMax = key_off(1, 15);
+      const bool need_lo = __builtin_amdgcn_ballot_w64(rlo > 0) != 0;
+      const bool need_hi = __builtin_amdgcn_ballot_w64(rhi < kOffMax) != 0;
+      if (need_lo && need_hi) {
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = key_off(bk, r);
+            sacc[bk][r] = (off < rlo || off > rhi) ? ninf : sacc[bk][r];
+          }
+      } else if (need_hi) {
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[bk][r] = key_off(bk, r) > rhi ? ninf : sacc[bk][r];
+      } else if (need_lo) {
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[bk][r] = key_off(bk, r) < rlo ? ninf : sacc[bk][r];
+      }
+    }
     float mx = ninf;
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = xform(sacc[bk][r], bk, r, kq);
-        if constexpr (MASK) {
-          const int off = key_off(bk, r);
-          x = (off < rlo || off > rhi) ? ninf : x;
-        }
-        sacc[bk][r] = x;
-        mx = __builtin_fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sacc[bk][r]);
     if constexpr (MODE == kSoftcap && !RAW) {
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
@@ -459,6 +483,38 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     if constexpr (MODE == kAlibiCausal) moff = __builtin_fmaf(-slope2, (float)(k0 + 4 * hh - qrow), moff);
     return moff;
   };
+  constexpr int NQ = 2 * NQC, NP = 4 * NDB, NS = NQ + NP;  // MFMAs of S = K Q^T, of O += V P, of a step
+  constexpr int PD = 3;                                     // LDS fragments are read PD MFMAs ahead
+
+  // Non-pipelined step halves (PARTIAL steps): S = K Q^T, and O += V P with the P
+  // slices formed under the MFMAs of the slice before; both read their LDS fragments
+  // PD MFMAs ahead, with scheduling fences between the MFMAs.
+  auto qk_sched = [&](const lds_u8* kt, f32x16 (&sacc)[2]) {
+    bf16x8 fr[PD + 1];
+    static_for<PD>([&](auto ic) { fr[ic.value] = kfrag(kt, ic.value & 1, ic.value >> 1); });
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NQ>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + PD < NQ) fr[(i + PD) % (PD + 1)] = kfrag(kt, (i + PD) & 1, (i + PD) >> 1);
+      sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], sacc[i & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto pv_sched = [&](auto raw_tag, const lds_u8* vt, const f32x16 (&sacc)[2], float moff, float& ls) {
+    bf16x8 fr[PD + 1], pf[4];
+    static_for<PD>([&](auto ic) { fr[ic.value] = vfrag(vt, ic.value / NDB, ic.value % NDB); });
+    pf[0] = pslice(raw_tag, sacc[0], 0, moff, ls);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NP>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, ks = j / NDB, db = j % NDB;
+      if constexpr (j + PD < NP) fr[(j + PD) % (PD + 1)] = vfrag(vt, (j + PD) / NDB, (j + PD) % NDB);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % (PD + 1)], pf[ks], oacc[db], 0, 0, 0);
+      if constexpr (db == 0 && ks + 1 < 4) pf[ks + 1] = pslice(raw_tag, sacc[(ks + 1) >> 1], (ks + 1) & 1, moff, ls);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
   auto qk_full = [&](const lds_u8* kt, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk) {
@@ -497,13 +553,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       issue_v(s + 1, (s & 1) ? vl0 : vl1);
     }
     const int k0 = step_k0(s);
-    qk_full(kc, sa);
+    qk_sched(kc, sa);
     const float moff = rescale(prepare(YES, NO, sa, k0), k0);
     float ls = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(NO, sa[sl >> 1], sl & 1, moff, ls);
+    pv_sched(NO, vc, sa, moff, ls);
     l_sum += ls;
-    pv_full(vc, pf);
   }
 
   // ---- phase 2: FULL blocks, software-pipelined ---------------------------------------------
@@ -520,8 +574,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   //   S(s+1) take slots [WP, NS), after its MFMAs have completed.  Scheduling fences
   //   between the slots keep this interleaving, so the VALU work of a slot runs under
   //   that slot's MFMA.
-  constexpr int NQ = 2 * NQC, NP = 4 * NDB, NS = NQ + NP;
-  constexpr int PD = 3;
   constexpr int WP = NQ + NP / 2;
   constexpr int EPS = 32 / (NS - WP);  // S(s+1) elements per maximum slot
   constexpr bool PRE = MODE == kSoftcap;  // softcap scores reach the loop raw
