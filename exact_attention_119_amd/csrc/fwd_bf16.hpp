@@ -565,24 +565,26 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // entry: S(s) in scur, prepared (softcap scores raw), with its row maximum mcur; K(s+1)
   // and V(s) requested.
   //   wait for this wave's loads, barrier (all loads in; all reads of step s-1 done);
-  //   request K(s+2) into kcur and V(s+1) into vnext; threshold rescale for step s;
-  //   then NS issue slots, one MFMA each: slots [0, NQ) S(s+1) = K(s+1) Q^T, slots
+  //   NS issue slots, one MFMA each: slots [0, NQ) S(s+1) = K(s+1) Q^T, slots
   //   [NQ, NS) O += V(s) P(s).  Every LDS fragment is read PD slots before its MFMA.
-  //   The 16 exponential pairs of P(s) start in slots [0, WP), pair k in slot k*WP/16,
+  //   The loads of the step and its rescale follow the first E slots.  The 16
+  //   exponential pairs of P(s) start in slots [E, WP), pair k in slot E + k(WP-E)/16,
   //   its later stages one and two slots on, each packed before the P.V MFMA that
   //   consumes it; the transform and maximum of
   //   S(s+1) take slots [WP, NS), after its MFMAs have completed.  Scheduling fences
   //   between the slots keep this interleaving, so the VALU work of a slot runs under
   //   that slot's MFMA.
+  constexpr int E = 2;                 // slots issued before the loads and the rescale
   constexpr int WP = NQ + NP / 2;
   constexpr int EPS = 32 / (NS - WP);  // S(s+1) elements per maximum slot
   constexpr bool PRE = MODE == kSoftcap;  // softcap scores reach the loop raw
   constexpr int NSTG = PRE ? 3 : 2;       // slots a pair's stages span
   static_assert(EPS * (NS - WP) == 32, "maximum slots");
-  static_assert(((4 * 0 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 0 &&
-                    ((4 * 1 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 1 &&
-                    ((4 * 2 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 2 &&
-                    ((4 * 3 + 3) * WP) / 16 + NSTG - 1 < NQ + NDB * 3,
+  // pair k starts in slot E + k(WP - E)/16
+  static_assert(E + ((4 * 0 + 3) * (WP - E)) / 16 + NSTG - 1 < NQ + NDB * 0 &&
+                    E + ((4 * 1 + 3) * (WP - E)) / 16 + NSTG - 1 < NQ + NDB * 1 &&
+                    E + ((4 * 2 + 3) * (WP - E)) / 16 + NSTG - 1 < NQ + NDB * 2 &&
+                    E + ((4 * 3 + 3) * (WP - E)) / 16 + NSTG - 1 < NQ + NDB * 3,
                 "every P slice is packed before its first P.V MFMA");
   auto step = [&](auto next_tag, auto issue_k_tag, int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur,
                   lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
@@ -590,9 +592,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     constexpr bool ISSUE_K = decltype(issue_k_tag)::value;
     wait_vmem();
     __syncthreads();
-    if constexpr (ISSUE_K) issue_k(s + 2, kcur);
-    if constexpr (NEXT) issue_v(s + 1, vnext);
-    const float moff = rescale(mcur, step_k0(s));
+    // the loads of this step and the rescale go after the first E slots, so that the
+    // matrix cores have work right after the barrier
+    float moff = 0.f;
+    auto loads_and_rescale = [&]() {
+      if constexpr (ISSUE_K) issue_k(s + 2, kcur);
+      if constexpr (NEXT) issue_v(s + 1, vnext);
+      moff = rescale(mcur, step_k0(s));
+    };
 
     float ls = 0.f;
     if constexpr (NEXT) {
@@ -613,6 +620,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       __builtin_amdgcn_sched_barrier(0);
       static_for<NS>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        if constexpr (i == E) {
+          loads_and_rescale();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (i + PD < NS) fr[(i + PD) % (PD + 1)] = frag(i + PD);
         if constexpr (i < NQ) {
           snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], snext[i & 1], 0, 0, 0);
@@ -622,11 +633,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4),
                                                              oacc[db], 0, 0, 0);
         }
-        // pair k: stages in slots a(k) (+1, +2), a(k) = k*WP/16; the instructions of
-        // one slot come from different pairs and do not wait on each other
+        // pair k: stages in slots a(k) (+1, +2), a(k) = E + k(WP - E)/16; the
+        // instructions of one slot come from different pairs and do not wait on each other
         static_for<16>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
-          constexpr int a = (k * WP) / 16;
+          constexpr int a = E + (k * (WP - E)) / 16;
           constexpr int sl = k >> 2, r = (sl & 1) * 8 + 2 * (k & 3);
           if constexpr (a == i) {
             float s0 = scur[sl >> 1][r], s1 = scur[sl >> 1][r + 1];
@@ -671,6 +682,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       });
       mcur = finalize(mx, k1);
     } else {
+      loads_and_rescale();
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls);
       pv_full(vcur, pf);
