@@ -28,8 +28,8 @@ SOURCES = [
     "blockmap.hip",
     "fwd_bf16_d128.hip",
     "fwd_bf16_d64.hip",
-    "fwd_fp8_d128.hip",
-    "fwd_fp8_d64.hip",
+    "fwd_fp8p_d128.hip",
+    "fwd_fp8p_d64.hip",
     "fwd_fp8qk8_d128.hip",
     "fwd_fp8qk8_d64.hip",
 ]

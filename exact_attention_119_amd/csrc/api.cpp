@@ -20,7 +20,7 @@ hipError_t launch_fwd_family(const FwdArgs& a, bool masked, bool alibi, bool sof
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
 namespace bf16path {
 constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
-template <int D>
+template <int D, bool FP8>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st);
 }  // namespace bf16path
 }  // namespace attn119
@@ -70,14 +70,14 @@ const char* variant_name(const FwdVariant& v) {
       for (int in = 0; in < 3; ++in)
         for (int m = 0; m < 2; ++m)
           for (int k = 0; k < 5; ++k) {
-            const char* tail = in == 0 ? kMode[k] : kMods[k < 4 ? k : 3];
+            const char* tail = in != 2 ? kMode[k] : kMods[k < 4 ? k : 3];
             std::snprintf(names[di][in][m][k], 64, "%s d%d %s %s", kIn[in], di ? 128 : 64,
                           m ? "masked" : "unmasked", tail);
           }
     init = true;
   }
   int k;
-  if (v.input == kInBf16) k = v.mode == bf16path::kGeneric ? (v.softcap ? 4 : 3) : v.mode;
+  if (v.input != kInFp8Qk8) k = v.mode == bf16path::kGeneric ? (v.softcap ? 4 : 3) : v.mode;
   else k = (v.alibi ? 2 : 0) + (v.softcap ? 1 : 0);
   return names[v.d == 128][v.input][v.masked][k];
 }
@@ -270,11 +270,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   const hipStream_t s = (hipStream_t)stream;
   const FwdVariant var = select_variant(d, dtype, mask, fp8);
   if (dtype == ATTN_BF16)
-    e = d == 128 ? bf16path::launch<128>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else if (fp8->qk_mode == ATTN_QK_BF16)
-    e = d == 128 ? launch_fwd_family<128, kInFp8>(a, masked, alibi, softcap, s)
-                 : launch_fwd_family<64, kInFp8>(a, masked, alibi, softcap, s);
+    e = d == 128 ? bf16path::launch<128, true>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else
     e = d == 128 ? launch_fwd_family<128, kInFp8Qk8>(a, masked, alibi, softcap, s)
                  : launch_fwd_family<64, kInFp8Qk8>(a, masked, alibi, softcap, s);

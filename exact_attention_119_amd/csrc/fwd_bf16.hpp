@@ -120,17 +120,40 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* 
                                            voffset, 0, 0, 0);
 }
 
+// e4m3 (OCP) codes widen exactly to bf16 and to fp16 (3 mantissa bits; every e4m3
+// exponent, subnormals included, lies inside both formats' normal range): one
+// v_cvt_scalef32_pk_*_fp8 with unit scale per two codes.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
+}
+
 // key offset (within a 64-key step, minus 4*hh) of accumulator register r of block bk
 __host__ __device__ constexpr int key_off(int bk, int r) { return 32 * bk + 8 * (r >> 2) + (r & 3); }
 
 //   D       head dim (64 or 128)
+//   FP8     e4m3 Q/K/V codes with per-(b, h, 128-row block) fp32 scales: the codes are
+//           widened exactly as they are staged (Q, K to bf16, V to fp16); Q.K^T runs on
+//           the bf16 MFMA, P.V on the fp16 MFMA with P rounded to fp16, in units of
+//           vs_kb / vs_max (the key block's V scale over the head's largest), so that
+//           P <= 2^tau stays inside fp16 whatever the scales; O is multiplied back by
+//           vs_max and normalised by the sum of P as rounded.
 //   MASKED  positional mask through the block map (else: all keys visible)
 //   MODE    score-modifier mode (kLinear, kSoftcap, kAlibiCausal, kGeneric)
 //   GALIBI, GSOFTCAP  modifiers of the generic mode
-template <int D, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
+template <int D, bool FP8, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
 __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) {
   constexpr int BN = 64;                 // keys per step
-  constexpr int ROWB = D * 2;            // bytes per row of Q/K/V
+  constexpr int ROWB = D * 2;            // bytes per 16-bit row of Q/K/V (LDS; HBM for bf16)
+  constexpr int HROWB = FP8 ? D : D * 2;  // bytes per row in HBM
   constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   constexpr int RP256 = 256 / ROWB;      // rows per 256-byte LDS line
   constexpr int TILE = BN * ROWB;        // bytes of one K or V tile
@@ -240,7 +263,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   // ---- Q tile -> VGPRs (B operand of S^T = K Q^T) ----------------------------------------
   bf16x8 qf[NQC];
-  {
+  if constexpr (FP8) {
+    const unsigned char* qp = (const unsigned char*)a.q + (head_row0 + (qvalid ? qrow : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      const u32x2 w = *(const u32x2*)(qp + c * 16 + hh * 8);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(w.x, w.y));
+      qf[c] = qvalid ? v : bf16x8{};
+    }
+  } else {
     const bf16* qp = (const bf16*)a.q + (head_row0 + (qvalid ? qrow : 0)) * D;
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
@@ -257,11 +288,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // The buffer descriptor of a step starts at its first key row and covers the rows
   // left in the head, so every row past N reads as zero (range-checked on the lane
   // offset; no address ever leaves the head).
-  const unsigned char* const kbase = (const unsigned char*)a.k + head_row0 * ROWB;
-  const unsigned char* const vbase = (const unsigned char*)a.v + head_row0 * ROWB;
+  const unsigned char* const kbase = (const unsigned char*)a.k + head_row0 * HROWB;
+  const unsigned char* const vbase = (const unsigned char*)a.v + head_row0 * HROWB;
   auto rsrc = [&](const unsigned char* base, int k0) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), (short)0,
-                                             max(N - k0, 0) * ROWB, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * HROWB), (short)0,
+                                             max(N - k0, 0) * HROWB, 0x00020000);
   };
   int koff[LPW], voff[LPW];  // byte offsets within a tile, per direct load of this wave
 #pragma unroll
@@ -281,6 +312,64 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, step_k0(s));
 #pragma unroll
     for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, voff[r]);
+  };
+
+  // ---- fp8: staging through VGPRs ------------------------------------------------------
+  // Thread t stages row t/4 of a 64-row tile, codes (t%4)*CPT .. +CPT: stage_* loads the
+  // codes of a step into registers (range-checked: rows past N read as zero codes), and
+  // commit_*_chunk widens 8 of them (one 16-byte chunk of the 16-bit row) and writes the
+  // chunk to the tile in the same swizzled layouts as above.  A tile is staged one step
+  // before it is committed, so the load latency is spent under a whole step.
+  constexpr int CPT = D / 4;       // codes per thread per tile
+  constexpr int SLD = CPT / 16;    // 16-byte loads per thread per tile
+  constexpr int SCH = CPT / 8;     // 16-byte 16-bit chunks per thread per tile
+  u32x4 kst[FP8 ? SLD : 1], vst[FP8 ? SLD : 1];
+  const int srow = tid >> 2;
+  auto stage_k = [&](int s) {
+    if constexpr (FP8) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, step_k0(s));
+#pragma unroll
+      for (int j = 0; j < SLD; ++j)
+        kst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, srow * D + (tid & 3) * CPT + 16 * j, 0, 0));
+    }
+  };
+  auto stage_v = [&](int s) {
+    if constexpr (FP8) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, step_k0(s));
+#pragma unroll
+      for (int j = 0; j < SLD; ++j)
+        vst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, srow * D + (tid & 3) * CPT + 16 * j, 0, 0));
+    }
+  };
+  auto commit_k_chunk = [&](lds_u8* dst, int j) {
+    if constexpr (FP8) {
+      const u32x4& w = kst[j >> 1];
+      const u32x4 v = (j & 1) ? e4m3x8_to_bf16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.x, w.y);
+      const int ch = (tid & 3) * SCH + j;
+      *(__attribute__((address_space(3))) u32x4*)(dst + srow * ROWB + (ch ^ kswz(srow)) * 16) = v;
+    }
+  };
+  auto commit_v_chunk = [&](lds_u8* dst, int j) {
+    if constexpr (FP8) {
+      const u32x4& w = vst[j >> 1];
+      const u32x4 v = (j & 1) ? e4m3x8_to_f16x8(w.z, w.w) : e4m3x8_to_f16x8(w.x, w.y);
+      const int ch = (tid & 3) * SCH + j;
+      *(__attribute__((address_space(3))) u32x4*)(dst + srow * ROWB + (ch ^ vswz(srow)) * 16) = v;
+    }
+  };
+  auto commit_k = [&](lds_u8* dst) {
+#pragma unroll
+    for (int j = 0; j < SCH; ++j) commit_k_chunk(dst, j);
+  };
+  auto commit_v = [&](lds_u8* dst) {
+#pragma unroll
+    for (int j = 0; j < SCH; ++j) commit_v_chunk(dst, j);
+  };
+  // the tiles of step s (bf16: requested straight into LDS; fp8: committed from the
+  // staging registers, then the tiles of the step after are staged)
+  auto wait_tiles = [&]() {
+    if constexpr (FP8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's chunk writes
+    else wait_vmem();                                                        // this wave's direct loads
   };
 
   // ---- LDS read addressing -------------------------------------------------------------
@@ -323,7 +412,43 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     slope2 = sl * 1.4426950408889634f;
   }
   const bool alibi_abs = !(a.mflags & kCausal);  // bidirectional masks: -slope*|q-k|
-  const float ct = a.c, sc2 = a.sc2, cap2 = a.cap2, tau = a.tau;
+  const float cap2 = a.cap2, tau = a.tau;
+  // Score multipliers: c = scale*log2e and sc2 = 2c/cap for the exponentials of the
+  // current step (ct, sc2) and for the maximum of the step being prepared (ctp, sc2p);
+  // for fp8 both carry the Q and K block scales sq*sk, which change with the key block.
+  float ct = a.c, sc2 = a.sc2, ctp = a.c, sc2p = a.sc2;
+  // fp8: V block scale of the current step over the head's largest (log2 and inverse)
+  float lvs = 0.f, ivs = 1.f;
+  float sq = 1.f, vs_max = 1.f;
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* const ksc = FP8 ? (cfloat*)a.k_scale + (size_t)bh * nqb : nullptr;
+  cfloat* const vsc = FP8 ? (cfloat*)a.v_scale + (size_t)bh * nqb : nullptr;
+  if constexpr (FP8) {
+    sq = ((cfloat*)a.q_scale)[(size_t)bh * nqb + qb];
+    float mx = 0.f;
+    for (int i = lane; i < nqb; i += 64) mx = __builtin_fmaxf(mx, a.v_scale[(size_t)bh * nqb + i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+    vs_max = mx > 0.f ? mx : 1.f;
+  }
+  // the multipliers of the step whose first key is k0 (for the maximum / the exponentials)
+  auto scales_p = [&](int k0) {
+    if constexpr (FP8) {
+      const float f = sq * ksc[k0 >> 7];
+      ctp = a.c * f;
+      sc2p = a.sc2 * f;
+    }
+  };
+  auto scales_e = [&](int k0) {
+    if constexpr (FP8) {
+      const float f = sq * ksc[k0 >> 7];
+      ct = a.c * f;
+      sc2 = a.sc2 * f;
+      const float vr = vsc[k0 >> 7] / vs_max;
+      lvs = __builtin_amdgcn_logf(vr);  // log2
+      ivs = 1.f / vr;
+    }
+  };
   const float ninf = -__builtin_inff();
 
   // ---- state ----------------------------------------------------------------------------
@@ -331,7 +456,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_used = ninf;
-  float l_sum = 0.f;  // row sum of p (fp32, before rounding to bf16): LSE and the normaliser of O
+  float l_sum = 0.f;   // row sum of p (fp32, before rounding): LSE; for bf16 also the normaliser of O
+  float lq_sum = 0.f;  // fp8: row sum of p as rounded to fp16, the normaliser of O
+  const f16x2 ones_h = {(f16)1.0f, (f16)1.0f};
 
   // ---- score modifiers, mask and row maximum ---------------------------------------------
   // Score of one accumulator element before the maximum is taken (kq = k0 + 4hh - q):
@@ -341,11 +468,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     if constexpr (MODE == kAlibiCausal) {
       // y = s*c + slope*key_off; the row part slope*(k0 + 4hh - q) is added to the max
       // and subtracted from the exponent offset instead
-      return __builtin_fmaf(sraw, ct, slope2 * (float)key_off(bk, r));
+      return __builtin_fmaf(sraw, ctp, slope2 * (float)key_off(bk, r));
     } else if constexpr (MODE == kGeneric) {
       float x;
-      if constexpr (GSOFTCAP) x = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(sraw * sc2) + 1.f), cap2);
-      else x = sraw * ct;
+      if constexpr (GSOFTCAP) x = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(sraw * sc2p) + 1.f), cap2);
+      else x = sraw * ctp;
       if constexpr (GALIBI) {
         const float dist = (float)(kq + key_off(bk, r));
         x = __builtin_fmaf(slope2, alibi_abs ? -__builtin_fabsf(dist) : dist, x);
@@ -361,9 +488,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     if constexpr (MODE == kAlibiCausal) mx = __builtin_fmaf(slope2, (float)(k0 + 4 * hh - qrow), mx);
     mx = pair_max(mx);
     if constexpr (MODE == kLinear) {
-      mx *= ct;  // ct > 0 keeps the order; -inf stays -inf
+      mx *= ctp;  // ctp > 0 keeps the order; -inf stays -inf
     } else if constexpr (MODE == kSoftcap) {
-      const float xm = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(mx * sc2) + 1.f), cap2);
+      const float xm = __builtin_fmaf(-2.f * cap2, rcp_(exp2_(mx * sc2p) + 1.f), cap2);
       mx = mx == ninf ? ninf : xm;
     }
     return mx;
@@ -420,7 +547,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float sv = sacc[bk][r];
-          const float rr = rcp_(exp2_(sv * sc2) + 1.f);
+          const float rr = rcp_(exp2_(sv * sc2p) + 1.f);
           sacc[bk][r] = sv == ninf ? __builtin_inff() : rr;
         }
     }
@@ -438,24 +565,31 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     else if constexpr (MODE == kSoftcap) return exp2_(__builtin_fmaf(-2.f * cap2, sv, cap2 - moff));
     else return exp2_(sv - moff);
   };
-  auto p_pack = [&](float p0, float p1, float& ls) -> uint32_t {
+  auto p_pack = [&](float p0, float p1, float& ls, float& lqs) -> uint32_t {
     ls += p0 + p1;
-    return __builtin_bit_cast(uint32_t, to_bf16x2(p0, p1));
+    if constexpr (FP8) {
+      const f32x2 v = {p0, p1};
+      const f16x2 pb = __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even
+      lqs = __builtin_amdgcn_fdot2(pb, ones_h, lqs, false);
+      return __builtin_bit_cast(uint32_t, pb);
+    } else {
+      return __builtin_bit_cast(uint32_t, to_bf16x2(p0, p1));
+    }
   };
   // all three stages of one pair (RAW: softcap scores untransformed)
-  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls) -> uint32_t {
+  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls, float& lqs) -> uint32_t {
     constexpr bool RAW = decltype(raw_tag)::value;
     if constexpr (MODE == kSoftcap && RAW) {
       s0 = p_pre(s0);
       s1 = p_pre(s1);
     }
-    return p_pack(p_exp(s0, moff), p_exp(s1, moff), ls);
+    return p_pack(p_exp(s0, moff), p_exp(s1, moff), ls, lqs);
   };
   // P of one 16-key slice (registers 8g..8g+7 of block bk) as the bf16 B operand
-  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls) -> bf16x8 {
+  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls, float& lqs) -> bf16x8 {
     uint32_t pk[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls);
+    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls, lqs);
     const u32x4 v4 = {pk[0], pk[1], pk[2], pk[3]};
     return __builtin_bit_cast(bf16x8, v4);
   };
@@ -474,6 +608,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       const float alpha = need ? exp2_(m_used - m_new) : 1.f;
       m_used = need ? m_new : m_used;
       l_sum *= alpha;
+      lq_sum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     }
@@ -481,7 +616,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     // the offset)
     float moff = m_used == ninf ? 0.f : m_used;
     if constexpr (MODE == kAlibiCausal) moff = __builtin_fmaf(-slope2, (float)(k0 + 4 * hh - qrow), moff);
+    if constexpr (FP8) moff -= lvs;  // P in units of vs_kb / vs_max
     return moff;
+  };
+  // O^T += V^T P^T: bf16 operands, or fp16 ones for fp8 inputs (the fragments carry the
+  // 16-bit patterns either way)
+  auto pv_mma = [&](bf16x8 va, bf16x8 pb, const f32x16& acc) -> f32x16 {
+    if constexpr (FP8)
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, pb), acc,
+                                                    0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc, 0, 0, 0);
   };
   constexpr int NQ = 2 * NQC, NP = 4 * NDB, NS = NQ + NP;  // MFMAs of S = K Q^T, of O += V P, of a step
   constexpr int PD = 3;                                     // LDS fragments are read PD MFMAs ahead
@@ -502,16 +647,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto pv_sched = [&](auto raw_tag, const lds_u8* vt, const f32x16 (&sacc)[2], float moff, float& ls) {
+  auto pv_sched = [&](auto raw_tag, const lds_u8* vt, const f32x16 (&sacc)[2], float moff, float& ls, float& lqs) {
     bf16x8 fr[PD + 1], pf[4];
     static_for<PD>([&](auto ic) { fr[ic.value] = vfrag(vt, ic.value / NDB, ic.value % NDB); });
-    pf[0] = pslice(raw_tag, sacc[0], 0, moff, ls);
+    pf[0] = pslice(raw_tag, sacc[0], 0, moff, ls, lqs);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NP>([&](auto jc) {
       constexpr int j = decltype(jc)::value, ks = j / NDB, db = j % NDB;
       if constexpr (j + PD < NP) fr[(j + PD) % (PD + 1)] = vfrag(vt, (j + PD) / NDB, (j + PD) % NDB);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % (PD + 1)], pf[ks], oacc[db], 0, 0, 0);
-      if constexpr (db == 0 && ks + 1 < 4) pf[ks + 1] = pslice(raw_tag, sacc[(ks + 1) >> 1], (ks + 1) & 1, moff, ls);
+      oacc[db] = pv_mma(fr[j % (PD + 1)], pf[ks], oacc[db]);
+      if constexpr (db == 0 && ks + 1 < 4) pf[ks + 1] = pslice(raw_tag, sacc[(ks + 1) >> 1], (ks + 1) & 1, moff, ls, lqs);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -529,7 +674,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(vt, ks, db), pf[ks], oacc[db], 0, 0, 0);
+        oacc[db] = pv_mma(vfrag(vt, ks, db), pf[ks], oacc[db]);
   };
 
   f32x16 sa[2], sb[2];
@@ -538,26 +683,51 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   constexpr std::false_type NO{};
 
   // ---- phase 1: PARTIAL blocks, one step at a time (K(s), V(s) in buffers s % 2) ----------
+  // (fp8: on entry to step s the tiles of step s are committed and those of step s+1
+  // staged)
   const int np_steps = 2 * npart;
   if (nsteps > 0) {
-    issue_k(0, kl0);
-    issue_v(0, vl0);
+    if constexpr (FP8) {
+      stage_k(0);
+      stage_v(0);
+      commit_k(kl0);
+      commit_v(vl0);
+      if (1 < nsteps) {
+        stage_k(1);
+        stage_v(1);
+      }
+    } else {
+      issue_k(0, kl0);
+      issue_v(0, vl0);
+    }
   }
   for (int s = 0; s < np_steps; ++s) {
     lds_u8* const kc = (s & 1) ? kl1 : kl0;
     lds_u8* const vc = (s & 1) ? vl1 : vl0;
-    wait_vmem();
+    wait_tiles();
     __syncthreads();  // K(s), V(s) in; every read of step s-1 done
     if (s + 1 < nsteps) {
-      issue_k(s + 1, (s & 1) ? kl0 : kl1);
-      issue_v(s + 1, (s & 1) ? vl0 : vl1);
+      if constexpr (FP8) {
+        commit_k((s & 1) ? kl0 : kl1);
+        commit_v((s & 1) ? vl0 : vl1);
+        if (s + 2 < nsteps) {
+          stage_k(s + 2);
+          stage_v(s + 2);
+        }
+      } else {
+        issue_k(s + 1, (s & 1) ? kl0 : kl1);
+        issue_v(s + 1, (s & 1) ? vl0 : vl1);
+      }
     }
     const int k0 = step_k0(s);
+    scales_p(k0);
+    scales_e(k0);
     qk_sched(kc, sa);
     const float moff = rescale(prepare(YES, NO, sa, k0), k0);
-    float ls = 0.f;
-    pv_sched(NO, vc, sa, moff, ls);
-    l_sum += ls;
+    float ls = 0.f, lqs = 0.f;
+    pv_sched(NO, vc, sa, moff, ls, lqs);
+    l_sum += FP8 ? ls * ivs : ls;
+    lq_sum += lqs * ivs;
   }
 
   // ---- phase 2: FULL blocks, software-pipelined ---------------------------------------------
@@ -590,21 +760,35 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
                   lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr bool ISSUE_K = decltype(issue_k_tag)::value;
-    wait_vmem();
+    wait_tiles();
     __syncthreads();
     // the loads of this step and the rescale go after the first E slots, so that the
-    // matrix cores have work right after the barrier
+    // matrix cores have work right after the barrier (fp8: commit K(s+2), V(s+1) from the
+    // staging registers, then stage K(s+3), V(s+2))
     float moff = 0.f;
     auto loads_and_rescale = [&]() {
-      if constexpr (ISSUE_K) issue_k(s + 2, kcur);
-      if constexpr (NEXT) issue_v(s + 1, vnext);
+      if constexpr (FP8) {
+        if constexpr (ISSUE_K) {
+          commit_k(kcur);
+          if (s + 3 < nsteps) stage_k(s + 3);
+        }
+        if constexpr (NEXT) {
+          commit_v(vnext);
+          if (s + 2 < nsteps) stage_v(s + 2);
+        }
+      } else {
+        if constexpr (ISSUE_K) issue_k(s + 2, kcur);
+        if constexpr (NEXT) issue_v(s + 1, vnext);
+      }
+      scales_e(step_k0(s));
       moff = rescale(mcur, step_k0(s));
     };
 
-    float ls = 0.f;
+    float ls = 0.f, lqs = 0.f;
     if constexpr (NEXT) {
       const int k1 = step_k0(s + 1);
       const int kq1 = k1 + 4 * hh - qrow;
+      scales_p(k1);
       auto frag = [&](int i) -> bf16x8 {
         if (i < NQ) return kfrag(knext, i & 1, i >> 1);
         const int j = i - NQ;
@@ -630,8 +814,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
         } else {
           constexpr int j = i - NQ, ks = j / NDB, db = j % NDB;
           const u32x4 v4 = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4),
-                                                             oacc[db], 0, 0, 0);
+          oacc[db] = pv_mma(fr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4), oacc[db]);
         }
         // pair k: stages in slots a(k) (+1, +2), a(k) = E + k(WP - E)/16; the
         // instructions of one slot come from different pairs and do not wait on each other
@@ -662,7 +845,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
             pin(pv1[k]);
           }
           if constexpr (a + NSTG - 1 == i) {
-            pk[k] = p_pack(pv0[k], pv1[k], ls);
+            pk[k] = p_pack(pv0[k], pv1[k], ls, lqs);
             pin(pk[k]);
             pin(ls);
           }
@@ -684,18 +867,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     } else {
       loads_and_rescale();
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls);
+      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls, lqs);
       pv_full(vcur, pf);
     }
-    l_sum += ls;
+    l_sum += FP8 ? ls * ivs : ls;
+    lq_sum += lqs * ivs;
   };
 
   if (np_steps < nsteps) {
     const int t = np_steps;  // first FULL step (even); K(t), V(t) requested
-    wait_vmem();
+    wait_tiles();
     __syncthreads();  // K(t) in; every read of step t-1 done
-    if (t + 1 < nsteps) issue_k(t + 1, kl1);
+    if (t + 1 < nsteps) {
+      if constexpr (FP8) {
+        commit_k(kl1);
+        if (t + 2 < nsteps) stage_k(t + 2);
+      } else {
+        issue_k(t + 1, kl1);
+      }
+    }
     qk_full(kl0, sa);
+    scales_p(step_k0(t));
     float mcand = prepare(NO, YES, sa, step_k0(t));
     int s = t;
     for (; s + 2 < nsteps; s += 2) {
@@ -708,9 +900,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   // ---- epilogue -------------------------------------------------------------------------
   l_sum = pair_sum(l_sum);
+  if constexpr (FP8) lq_sum = pair_sum(lq_sum);
   if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
-  const float inv = invalid ? nanv : (l_sum > 0.f ? 1.f / l_sum : 0.f);
+  const float onorm = FP8 ? lq_sum : l_sum;
+  const float inv = invalid ? nanv : (onorm > 0.f ? (FP8 ? vs_max : 1.f) / onorm : 0.f);
   bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -732,22 +926,23 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
 // Launches the variant (masked, mode, generic modifiers) chosen on the host; a
 // masked variant is never launched without a block map.
-template <int D>
+template <int D, bool FP8>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st) {
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
   if (masked && a.map == nullptr) return hipErrorInvalidValue;
+  if (FP8 && (!a.q_scale || !a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
   if (masked) {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kLinear, false, false>), grid, block, 0, st, a);
-    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kSoftcap, false, false>), grid, block, 0, st, a);
-    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kLinear, false, false>), grid, block, 0, st, a);
+    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kSoftcap, false, false>), grid, block, 0, st, a);
+    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;
   } else {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kLinear, false, false>), grid, block, 0, st, a);
-    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kSoftcap, false, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kLinear, false, false>), grid, block, 0, st, a);
+    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kSoftcap, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;  // (ALiBi on a causal mask always has a block map)
   }
   return hipGetLastError();

@@ -133,7 +133,12 @@ def test_kernel_variant_selection(L):
         n = name(128, flags, **kw)
         assert n is not None and ("unmasked" not in n) == bool(flags & (C | WI | DOC)), (flags, n)
     fp8 = L.make_fp8(P, P, P)
-    assert L.attn_fwd_kernel_name(128, 1, None, fp8) == "fp8 d128 unmasked none"
-    assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8) == "fp8 d64 masked alibi"
+    assert L.attn_fwd_kernel_name(128, 1, None, fp8) == "fp8 d128 unmasked linear"
+    assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8) == "fp8 d64 masked alibi-causal"
+    assert L.attn_fwd_kernel_name(128, 1, L.make_mask(C | WI | SC, window=9, softcap=50.0), fp8) == \
+        "fp8 d128 masked softcap"
+    fp8q = L.make_fp8(P, P, P, qk_mode=L.ATTN_QK_E4M3)
+    assert L.attn_fwd_kernel_name(128, 1, None, fp8q) == "fp8-qk8 d128 unmasked none"
+    assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8q) == "fp8-qk8 d64 masked alibi"
     assert L.attn_fwd_kernel_name(96, 0, None, None) is None
     assert L.attn_fwd_kernel_name(128, 1, None, None) is None
