@@ -763,19 +763,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     wait_tiles();
     __syncthreads();
     // the loads of this step and the rescale go after the first E slots, so that the
-    // matrix cores have work right after the barrier (fp8: commit K(s+2), V(s+1) from the
-    // staging registers, then stage K(s+3), V(s+2))
+    // matrix cores have work right after the barrier (fp8: K(s+2) and V(s+1) are committed
+    // from the staging registers one 16-byte chunk per slot from slot E on, each tile
+    // restaged -- K(s+3), V(s+2) -- after its last chunk; the last step commits nothing)
     float moff = 0.f;
-    auto loads_and_rescale = [&]() {
-      if constexpr (FP8) {
-        if constexpr (ISSUE_K) {
-          commit_k(kcur);
+    auto fp8_tiles = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (FP8 && ISSUE_K && i >= E && i < E + SCH) {
+        commit_k_chunk(kcur, i - E);
+        if constexpr (i == E + SCH - 1) {
           if (s + 3 < nsteps) stage_k(s + 3);
         }
-        if constexpr (NEXT) {
-          commit_v(vnext);
+      }
+      if constexpr (FP8 && NEXT && i >= E + SCH && i < E + 2 * SCH) {
+        commit_v_chunk(vnext, i - E - SCH);
+        if constexpr (i == E + 2 * SCH - 1) {
           if (s + 2 < nsteps) stage_v(s + 2);
         }
+      }
+    };
+    auto loads_and_rescale = [&]() {
+      if constexpr (FP8) {
       } else {
         if constexpr (ISSUE_K) issue_k(s + 2, kcur);
         if constexpr (NEXT) issue_v(s + 1, vnext);
@@ -808,6 +816,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
           loads_and_rescale();
           __builtin_amdgcn_sched_barrier(0);
         }
+        fp8_tiles(ic);
         if constexpr (i + PD < NS) fr[(i + PD) % (PD + 1)] = frag(i + PD);
         if constexpr (i < NQ) {
           snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], snext[i & 1], 0, 0, 0);
