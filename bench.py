@@ -10,8 +10,9 @@ unmasked FLOPs, 4*d*H*(visible (q, k) pairs) per step, divided by the step time.
 Default workload: B=4 H=16 N=2048 d=128, causal, bf16 (configuration 2).  Other
 --config values are the other synthetic workloads (1: B1 H2 N256 d64 plain;
 3: B2 H32 N8192 d128 causal+window 1024+softcap 50; 4: B1 H16 N16384 d128
-document-causal+ALiBi; 5: B1 H16 N16384 d128 fp8 plain) and --plain-causal the
-configuration-3 shape with a plain causal mask.
+document-causal+ALiBi; 5: B1 H16 N16384 d128 fp8 plain), --plain-causal the
+configuration-3 shape with a plain causal mask, and --shape B,H,N,d [--mask causal] any
+other bf16 shape.
 
 Printed on stdout: ONE JSON line.  Extra diagnostics go to stderr.
 """
@@ -129,6 +130,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--plain-causal", action="store_true", help="configuration-3 shape, plain causal mask")
+    ap.add_argument("--shape", type=str, default=None,
+                    help="supplementary bf16 workload B,H,N,d (with --mask), instead of a configuration")
+    ap.add_argument("--mask", choices=["none", "causal"], default="none", help="mask of a --shape workload")
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
@@ -159,7 +163,10 @@ def main(argv=None):
     import workload as W
     from workload import device as WD
 
-    if args.plain_causal:
+    if args.shape:
+        B, H, N, d = (int(x) for x in args.shape.split(","))
+        p = W.make_problem(B, H, N, d, flags=W.ATTN_CAUSAL if args.mask == "causal" else 0, seed=4)
+    elif args.plain_causal:
         p = W.make_problem(2, 32, 8192, 128, flags=W.ATTN_CAUSAL, seed=3)
     else:
         p = W.config_problem(args.config)
