@@ -189,3 +189,22 @@ def test_cfg5_qk_on_fp8_mfma_error_is_bounded_by_its_accumulation():
     print(f"cfg5 qk8: max|dO|={e_o:.3e} beyond-half-ulp={e_ob:.3e} max|dLSE|={e_l:.3e} "
           f"max|LSE|={np.abs(lse_ref).max():.1f}", flush=True)
     assert e_l <= 2.0 ** -11 * np.abs(lse_ref).max()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("variant", ["plain", "causal", "cfg3like", "cfg4like"])
+def test_fp8_block_scales_spread(d, variant):
+    """K and V block scales spread over 2^-3 .. 2^3 between 128-row blocks (the codes are
+    kept; the oracle dequantises with the new scales): every key block's K scale must reach
+    its own scores and its V scale its own P units, with and without threshold rescaling."""
+    kw = VARIANTS[variant]
+    p = W.make_problem(1, 2, 1000, d, dtype="fp8", seed=(d, 11, sorted(VARIANTS).index(variant)),
+                       doc_len_range=(100, 400), **kw)
+    rng = np.random.default_rng([119, 11, d, sorted(VARIANTS).index(variant)])
+    p.k_scale = (p.k_scale * 2.0 ** rng.integers(-3, 4, p.k_scale.shape)).astype(np.float32)
+    p.v_scale = (p.v_scale * 2.0 ** rng.integers(-3, 4, p.v_scale.shape)).astype(np.float32)
+    o_ref, lse_ref = oracle.attention_problem(p)
+    for tau in (8.0, 0.0):
+        _announce("fp8 spread scales", variant, d, tau)
+        _, o, lse = _run(p, tau=tau)
+        assert_close(p, o, lse, o_ref, lse_ref, f"fp8 spread scales {variant} d={d} tau={tau}")
