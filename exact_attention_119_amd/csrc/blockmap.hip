@@ -5,14 +5,14 @@
 // section "Aktuelle Einschränkungen".  Every mask this library supports (causal,
 // sliding window, document with contiguous documents, and their conjunctions)
 // leaves each query row a single interval of visible keys [row_lo, row_hi], so
-// the map is built from those intervals:
-//   pass 1 (one thread per query row): the interval, and a flag for any place
-//          where doc_id decreases (documents must be contiguous runs);
-//          and per query block a status word: 1 if doc_id decreases at one of
-//          its rows (a batch row with any such word is invalid);
-//   pass 2 (one workgroup per 128-query block): the class of every 128x128
-//          block, the ascending lists of FULL and PARTIAL key blocks and the
-//          visible-pair count of the query block.
+// the map is built from those intervals, in one launch with one workgroup per
+// 128-row query block:
+//   its rows (one thread each): the interval, and a flag for any place where doc_id
+//          decreases (documents must be contiguous runs), giving the block's status
+//          word: 1 if doc_id decreases at one of its rows (a batch row with any such
+//          word is invalid);
+//   its row of blocks: the class of every 128x128 block, the ascending lists of FULL
+//          and PARTIAL key blocks and the visible-pair count of the query block.
 // No atomics, no memset: every byte of every section is written, so the result is
 // byte-identical for equal inputs and the calls are safe to capture in a graph.
 #include "common.hpp"
@@ -38,63 +38,51 @@ __device__ inline int lower_bound_i32(const int32_t* row, int N, int v) {
   return lo;
 }
 
-__global__ void __launch_bounds__(256) blockmap_rows_kernel(MapArgs a) {
-  const int b = blockIdx.y;
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  const int N = a.N;
-  int32_t* row_lo = (int32_t*)(a.map + a.lay.row_lo) + (size_t)b * N;
-  int32_t* row_hi = (int32_t*)(a.map + a.lay.row_hi) + (size_t)b * N;
-  int bad = 0;
-  if (q < N) {
-    int lo = 0, hi = N - 1;
-    if (a.flags & kCausal) hi = q;
-    if (a.flags & kWindow) {
-      lo = max(lo, q - (a.window - 1));
-      if (!(a.flags & kCausal)) hi = min(hi, q + (a.window - 1));
-    }
-    if (a.flags & kDocument) {
-      const int32_t* drow = a.doc_id + (size_t)b * N;
-      const int dq = drow[q];
-      if (q + 1 < N && drow[q + 1] < dq) bad = 1;
-      const int first = lower_bound_i32(drow, N, dq);
-      const int last = (dq == INT32_MAX) ? N - 1 : lower_bound_i32(drow, N, dq + 1) - 1;
-      lo = max(lo, first);
-      hi = min(hi, last);
-    }
-    if (hi < lo) { lo = 0; hi = -1; }
-    row_lo[q] = lo;
-    row_hi[q] = hi;
-  }
-  // Status word of each of the (up to) two query blocks this workgroup covers:
-  // 1 if doc_id decreases between one of its rows and the next row.
-  const int bad0 = __syncthreads_or(bad && threadIdx.x < kBlock);
-  const int bad1 = __syncthreads_or(bad && threadIdx.x >= kBlock);
-  if (threadIdx.x == 0) {
-    int32_t* st = (int32_t*)(a.map + a.lay.status) + (size_t)b * a.nb;
-    const int qb = 2 * blockIdx.x;
-    st[qb] = bad0 ? 1 : 0;
-    if (qb + 1 < a.nb) st[qb + 1] = bad1 ? 1 : 0;
-  }
-}
-
-// One workgroup (256 threads, 4 waves) per (query block, batch row).
-__global__ void __launch_bounds__(256) blockmap_blocks_kernel(MapArgs a) {
+// One workgroup (256 threads, 4 waves) per (query block, batch row): the intervals and
+// the status word of its 128 rows, then the classes and lists of its row of blocks.
+__global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   const int qb = blockIdx.x, b = blockIdx.y;
   const int N = a.N, nb = a.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* row_lo = (const int32_t*)(a.map + a.lay.row_lo) + (size_t)b * N;
-  const int32_t* row_hi = (const int32_t*)(a.map + a.lay.row_hi) + (size_t)b * N;
   const int q0 = qb * kBlock, q1 = min(N, q0 + kBlock);
   const int nrows = q1 - q0;
 
   __shared__ int s_lo[kBlock], s_hi[kBlock];
   __shared__ int s_wave_full[4], s_wave_part[4];
   __shared__ long long s_pairs[4];
+
+  // ---- row intervals (threads 0..127, one query row each) and the status word ----------
+  int bad = 0;
   if (tid < kBlock) {
-    s_lo[tid] = tid < nrows ? row_lo[q0 + tid] : 0;
-    s_hi[tid] = tid < nrows ? row_hi[q0 + tid] : -1;
+    int lo = 0, hi = -1;
+    if (tid < nrows) {
+      const int q = q0 + tid;
+      lo = 0;
+      hi = N - 1;
+      if (a.flags & kCausal) hi = q;
+      if (a.flags & kWindow) {
+        lo = max(lo, q - (a.window - 1));
+        if (!(a.flags & kCausal)) hi = min(hi, q + (a.window - 1));
+      }
+      if (a.flags & kDocument) {
+        const int32_t* drow = a.doc_id + (size_t)b * N;
+        const int dq = drow[q];
+        if (q + 1 < N && drow[q + 1] < dq) bad = 1;
+        const int first = lower_bound_i32(drow, N, dq);
+        const int last = (dq == INT32_MAX) ? N - 1 : lower_bound_i32(drow, N, dq + 1) - 1;
+        lo = max(lo, first);
+        hi = min(hi, last);
+      }
+      if (hi < lo) { lo = 0; hi = -1; }
+      ((int32_t*)(a.map + a.lay.row_lo))[(size_t)b * N + q] = lo;
+      ((int32_t*)(a.map + a.lay.row_hi))[(size_t)b * N + q] = hi;
+    }
+    s_lo[tid] = lo;
+    s_hi[tid] = hi;
   }
-  __syncthreads();
+  // status: 1 if doc_id decreases between one of this block's rows and the next row
+  const int bad_any = __syncthreads_or(bad);  // (also orders the interval writes above)
+  if (tid == 0) ((int32_t*)(a.map + a.lay.status))[(size_t)b * nb + qb] = bad_any ? 1 : 0;
 
   // visible pairs of this query block
   long long my_pairs = 0;
@@ -172,8 +160,7 @@ hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int
   a.nb = (N + kBlock - 1) / kBlock;
   a.flags = flags & kPositional;
   a.window = window;
-  hipLaunchKernelGGL(blockmap_rows_kernel, dim3((N + 255) / 256, B), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(blockmap_blocks_kernel, dim3(a.nb, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(blockmap_kernel, dim3(a.nb, B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
