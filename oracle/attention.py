@@ -19,10 +19,14 @@ Game-Changer", liora.io):
             & [doc[q] == doc[k]    if DOCUMENT]
   m = max_k s,  l = sum_k exp(s - m),  LSE = m + ln l,  O = sum_k exp(s - m) V[k] / l
   a row with no visible key: O = 0, LSE = -inf.
+  grouped-query attention (GQA; MQA with one key/value head): K and V carry H_kv
+  heads, H_kv dividing H, and query head h reads key/value head h // (H / H_kv)
+  (same page, section "Συμβατότητα και τρέχουσα κατάσταση": several query heads
+  share one key/value projection).
 
 Readings where the pages are silent: scale first, then softcap, then ALiBi,
 then the mask; default ALiBi slopes 2^(-8(h+1)/H) for heads h = 0..H-1;
-natural-log LSE.
+natural-log LSE; under GQA consecutive query heads share a key/value head.
 """
 
 from __future__ import annotations
@@ -94,10 +98,15 @@ def attention_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, *, scale: float, 
                   heads: Optional[Sequence[tuple]] = None, chunk: int = 1024):
     """O [B][H][R][d] and LSE [B][H][R] (float64) for query rows `rows` (default: all).
 
-    Q, K, V: float64 [B][H][N][d].  `heads`, if given, restricts the work to a
-    list of (b, h) pairs; the other outputs are left as NaN.
+    Q: float64 [B][H][N][d]; K, V: float64 [B][H_kv][N][d] with H_kv dividing H
+    (H_kv = H: one key/value head per query head).  `heads`, if given, restricts the
+    work to a list of (b, h) pairs; the other outputs are left as NaN.
     """
     B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    if H_kv < 1 or H % H_kv or V.shape[1] != H_kv:
+        raise ValueError(f"{H} query heads cannot share {H_kv} key/value heads")
+    group = H // H_kv
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.shape[0]
     slopes = default_alibi_slopes(H) if alibi_slopes is None else np.asarray(alibi_slopes, np.float64)
@@ -108,9 +117,9 @@ def attention_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, *, scale: float, 
         doc_row = None if doc_id is None else doc_id[b]
         for c0 in range(0, R, chunk):
             rr = rows[c0:c0 + chunk]
-            s = scores_ref(Q[b, h], K[b, h], rr, scale=scale, flags=flags, window=window,
+            s = scores_ref(Q[b, h], K[b, h // group], rr, scale=scale, flags=flags, window=window,
                            softcap=softcap, doc_row=doc_row, slope=float(slopes[h]))
-            O[b, h, c0:c0 + chunk], L[b, h, c0:c0 + chunk] = _softmax_rows(s, V[b, h])
+            O[b, h, c0:c0 + chunk], L[b, h, c0:c0 + chunk] = _softmax_rows(s, V[b, h // group])
     return O, L
 
 

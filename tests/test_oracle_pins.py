@@ -54,13 +54,14 @@ def _visible_keys(q, N, flags, W, doc_row):
 
 def _brute(Q, K, V, scale, flags, W, cap, doc, slopes):
     B, H, N, d = Q.shape
+    g = H // K.shape[1]  # query heads per key/value head
     Ob = np.zeros((B, H, N, V.shape[3]))
     Lb = np.zeros((B, H, N))
     for b, h, q in itertools.product(range(B), range(H), range(N)):
         keys = _visible_keys(q, N, flags, W, None if doc is None else doc[b])
         sc = []
         for k in keys:
-            s = math.fsum(float(Q[b, h, q, i]) * float(K[b, h, k, i]) for i in range(d)) * scale
+            s = math.fsum(float(Q[b, h, q, i]) * float(K[b, h // g, k, i]) for i in range(d)) * scale
             if flags & SOFTCAP:
                 s = cap * math.tanh(s / cap)
             if flags & ALIBI:
@@ -74,7 +75,7 @@ def _brute(Q, K, V, scale, flags, W, cap, doc, slopes):
         l = math.fsum(w)
         Lb[b, h, q] = m + math.log(l)
         for j in range(V.shape[3]):
-            Ob[b, h, q, j] = math.fsum(wi * float(V[b, h, k, j]) for wi, k in zip(w, keys)) / l
+            Ob[b, h, q, j] = math.fsum(wi * float(V[b, h // g, k, j]) for wi, k in zip(w, keys)) / l
     return Ob, Lb
 
 
@@ -108,6 +109,40 @@ def test_oracle_matches_brute_force_all_flag_combinations(N, d):
             ob, lb = _brute(Q, K, V, float(np.float32(0.7)), flags, W, float(np.float32(cap)), doc, slopes)
             np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12, err_msg=f"flags={flags}")
             np.testing.assert_allclose(l, lb, rtol=1e-12, atol=1e-12, err_msg=f"flags={flags}")
+
+
+@pytest.mark.parametrize("H_kv", [1, 2])
+def test_oracle_matches_brute_force_grouped_heads(H_kv):
+    """GQA (H_kv = 2) and MQA (H_kv = 1) with four query heads: query head h reads
+    key/value head h // (4 / H_kv), for a spread of flag combinations."""
+    rng = np.random.default_rng(70 + H_kv)
+    B, H, N, d = 1, 4, 9, 4
+    Q = rng.standard_normal((B, H, N, d)) * 1.5
+    K = rng.standard_normal((B, H_kv, N, d)) * 1.5
+    V = rng.standard_normal((B, H_kv, N, d))
+    doc = _doc_rows(B, N, rng)
+    slopes = [0.5, 0.25, 0.125, 0.0625]
+    for flags in (0, CAUSAL, CAUSAL | WINDOW | SOFTCAP, DOCUMENT | ALIBI, CAUSAL | DOCUMENT | ALIBI | SOFTCAP):
+        o, l = O.attention_ref(Q, K, V, scale=0.7, flags=flags, window=3, softcap=2.5, doc_id=doc,
+                               alibi_slopes=slopes)
+        ob, lb = _brute(Q, K, V, float(np.float32(0.7)), flags, 3, float(np.float32(2.5)), doc, slopes)
+        np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12, err_msg=f"flags={flags}")
+        np.testing.assert_allclose(l, lb, rtol=1e-12, atol=1e-12, err_msg=f"flags={flags}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_vs_torch_sdpa_grouped_heads(causal):
+    """torch's scaled_dot_product_attention with enable_gqa (float64, CPU)."""
+    rng = np.random.default_rng(77)
+    Q = rng.standard_normal((2, 6, 90, 16))
+    K = rng.standard_normal((2, 2, 90, 16))
+    V = rng.standard_normal((2, 2, 90, 16))
+    o, l = O.attention_ref(Q, K, V, scale=0.25, flags=CAUSAL if causal else 0)
+    q, k, v = (torch.from_numpy(x) for x in (Q, K, V))
+    ot = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=0.25, enable_gqa=True)
+    np.testing.assert_allclose(o, ot.numpy(), rtol=1e-11, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.attention_ref(Q, K[:, :1].repeat(4, axis=1), V[:, :1].repeat(4, axis=1), scale=0.25)
 
 
 def test_empty_row_convention():

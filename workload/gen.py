@@ -51,8 +51,9 @@ CONFIGS = {
 class Problem:
     """One attention-forward problem instance, in storage formats.
 
-    q, k, v: uint16 bf16 bit patterns, or uint8 E4M3FN codes, shape [B][H][N][d].
-    q_scale/k_scale/v_scale: float32 [B][H][ceil(N/128)] for fp8, else None.
+    q: uint16 bf16 bit patterns, or uint8 E4M3FN codes, shape [B][H][N][d]; k, v the
+    same with H_kv heads ([B][H_kv][N][d]; H_kv = H unless set, H_kv divides H).
+    q_scale: float32 [B][H][ceil(N/128)], k_scale/v_scale [B][H_kv][...] for fp8, else None.
     doc_id: int32 [B][N] (non-decreasing per batch row) when the DOCUMENT flag is set.
     alibi_slopes: float32 [H] or None (None = the default geometric slopes).
     """
@@ -77,6 +78,12 @@ class Problem:
     doc_lengths: Optional[List[List[int]]] = None
     outlier_channels: Optional[np.ndarray] = None
     alibi_slopes: Optional[np.ndarray] = None
+    H_kv: Optional[int] = None
+
+    @property
+    def Hkv(self) -> int:
+        """Key/value heads (grouped-query attention when below H)."""
+        return self.H if self.H_kv is None else self.H_kv
 
     def digests(self) -> dict:
         """sha256 of every generated buffer (hex)."""
@@ -187,16 +194,18 @@ def _f32(x: float) -> float:
 
 
 def _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale, doc_lengths, n_outliers,
-           outlier_gain, alibi_slopes=None) -> Problem:
+           outlier_gain, alibi_slopes=None, H_kv=None) -> Problem:
     doc_id = None
     if doc_lengths is not None:
         doc_id = np.stack([doc_ids_from_lengths(doc_lengths[b]) for b in range(B)]).astype(np.int32)
     outl = None
     if n_outliers:
         outl = np.sort(rng.choice(d, n_outliers, replace=False)).astype(np.int64)
-    shape = (B, H, N, d)
+    Hkv = H if H_kv is None else H_kv
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{H} query heads cannot share {Hkv} key/value heads")
     xs = []
-    for _ in range(3):
+    for shape in ((B, H, N, d), (B, Hkv, N, d), (B, Hkv, N, d)):
         x = rng.standard_normal(shape, dtype=np.float32)
         if outl is not None:
             x[..., outl] *= np.float32(outlier_gain)
@@ -204,7 +213,7 @@ def _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale, doc_leng
     kw = dict(name=name, B=B, H=H, N=N, d=d, dtype=dtype, flags=flags, window=window,
               softcap=_f32(softcap), scale=_f32(scale), doc_id=doc_id, outlier_channels=outl,
               doc_lengths=None if doc_lengths is None else [list(map(int, l)) for l in doc_lengths],
-              alibi_slopes=alibi_slopes)
+              alibi_slopes=alibi_slopes, H_kv=H_kv)
     if dtype == "bf16":
         return Problem(q=bf16_bits_from_f32(xs[0]), k=bf16_bits_from_f32(xs[1]),
                        v=bf16_bits_from_f32(xs[2]), **kw)
@@ -239,8 +248,10 @@ def make_problem(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", flags: 
                  window: int = 0, softcap: float = 0.0, scale: Optional[float] = None,
                  seed: Union[int, Tuple[int, ...]] = 0,
                  doc_len_range: Optional[Tuple[int, int]] = None, n_outliers: int = 0,
-                 outlier_gain: float = 20.0, alibi_slopes: Optional[np.ndarray] = None) -> Problem:
-    """An ad-hoc problem of any shape, drawn with ``default_rng([119, 1000, *seed])``."""
+                 outlier_gain: float = 20.0, alibi_slopes: Optional[np.ndarray] = None,
+                 H_kv: Optional[int] = None) -> Problem:
+    """An ad-hoc problem of any shape, drawn with ``default_rng([119, 1000, *seed])``;
+    H_kv key/value heads shared by groups of H / H_kv query heads (default H_kv = H)."""
     seed_t = (seed,) if isinstance(seed, int) else tuple(seed)
     rng = np.random.default_rng([119, 1000, *seed_t])
     if scale is None:
@@ -251,5 +262,6 @@ def make_problem(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", flags: 
         doc_lengths = [draw_doc_lengths(rng, N, lo, hi) for _ in range(B)]
     if alibi_slopes is not None:
         alibi_slopes = np.asarray(alibi_slopes, dtype=np.float32)
-    return _build(f"B{B}H{H}N{N}d{d}", rng, B, H, N, d, dtype, flags, window, softcap, scale,
-                  doc_lengths, n_outliers, outlier_gain, alibi_slopes)
+    name = f"B{B}H{H}N{N}d{d}" + ("" if H_kv is None else f"Hkv{H_kv}")
+    return _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale,
+                  doc_lengths, n_outliers, outlier_gain, alibi_slopes, H_kv)
