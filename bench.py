@@ -12,7 +12,7 @@ Default workload: B=4 H=16 N=2048 d=128, causal, bf16 (configuration 2).  Other
 3: B2 H32 N8192 d128 causal+window 1024+softcap 50; 4: B1 H16 N16384 d128
 document-causal+ALiBi; 5: B1 H16 N16384 d128 fp8 plain), --plain-causal the
 configuration-3 shape with a plain causal mask, and --shape B,H,N,d [--mask causal] any
-other bf16 shape.
+other bf16 shape (--kv-heads H_kv for grouped-query attention).
 
 Printed on stdout: ONE JSON line.  Extra diagnostics go to stderr.
 """
@@ -61,7 +61,8 @@ def workload_name(p) -> str:
         mods.append(f"softcap{p.softcap:g}")
     if p.flags & 8:
         mods.append("alibi")
-    return f"B{p.B} H{p.H} N{p.N} d{p.d} {'+'.join(mods) or 'no-mask'} {p.dtype}"
+    kv = "" if p.Hkv == p.H else f" Hkv{p.Hkv}"
+    return f"B{p.B} H{p.H}{kv} N{p.N} d{p.d} {'+'.join(mods) or 'no-mask'} {p.dtype}"
 
 
 def visible_pairs(p) -> int:
@@ -131,8 +132,11 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--plain-causal", action="store_true", help="configuration-3 shape, plain causal mask")
     ap.add_argument("--shape", type=str, default=None,
-                    help="supplementary bf16 workload B,H,N,d (with --mask), instead of a configuration")
+                    help="supplementary bf16 workload B,H,N,d (with --mask, --kv-heads), instead of a "
+                         "configuration")
     ap.add_argument("--mask", choices=["none", "causal"], default="none", help="mask of a --shape workload")
+    ap.add_argument("--kv-heads", type=int, default=None,
+                    help="key/value heads of a --shape workload (grouped-query attention)")
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
@@ -165,7 +169,8 @@ def main(argv=None):
 
     if args.shape:
         B, H, N, d = (int(x) for x in args.shape.split(","))
-        p = W.make_problem(B, H, N, d, flags=W.ATTN_CAUSAL if args.mask == "causal" else 0, seed=4)
+        p = W.make_problem(B, H, N, d, flags=W.ATTN_CAUSAL if args.mask == "causal" else 0, seed=4,
+                           H_kv=args.kv_heads)
     elif args.plain_causal:
         p = W.make_problem(2, 32, 8192, 128, flags=W.ATTN_CAUSAL, seed=3)
     else:
@@ -207,7 +212,8 @@ def main(argv=None):
     traffic = traffic_record(name)
     from exact_attention_119_amd import lib as L
     kernel_name = L.attn_fwd_kernel_name(p.d, dp.dtype, dp.mask, dp.fp8)
-    alg_bytes = p.B * p.H * (p.N * p.d * (3 * (1 if dtype == "fp8" else 2) + 2) + 4 * p.N)
+    eb = 1 if dtype == "fp8" else 2
+    alg_bytes = p.B * p.N * (p.H * (p.d * (eb + 2) + 4) + p.Hkv * 2 * p.d * eb)
     log(f"bench: algorithmic HBM bytes per launch {alg_bytes}; at the forward kernel's time that is "
         f"{alg_bytes / (fwd_avg * 1e-3) / 1e9:.1f} GB/s of {HBM_PEAK_GBS:.0f}")
 

@@ -178,15 +178,15 @@ attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
   return bad ? ATTN_ERR_BAD_DOC_ID : ATTN_OK;
 }
 
-attn_status attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                            int32_t H, int32_t N, int32_t d, float scale, int32_t dtype,
-                            const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
-                            const attn_fp8* fp8, float rescale_tau) {
+attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                                int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
+                                const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                                const attn_fp8* fp8, float rescale_tau) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (H < 1) return ATTN_ERR_INVALID_ARG;
+  if (H < 1 || H_kv < 1 || H % H_kv != 0) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_shape(B, N);
   if (st != ATTN_OK) return st;
   if ((int64_t)B * H > (int64_t)INT32_MAX / ((N + 127) / 128) ||
@@ -211,6 +211,14 @@ attn_status attn_check_args(const void* q, const void* k, const void* v, void* o
   return ATTN_OK;
 }
 
+attn_status attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                            int32_t H, int32_t N, int32_t d, float scale, int32_t dtype,
+                            const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                            const attn_fp8* fp8, float rescale_tau) {
+  return attn_check_args_gqa(q, k, v, o, lse, B, H, H, N, d, scale, dtype, mask, blockmap, blockmap_bytes,
+                             fp8, rescale_tau);
+}
+
 const char* attn_fwd_kernel_name(int32_t d, int32_t dtype, const attn_mask* mask, const attn_fp8* fp8) {
   if (d != 64 && d != 128) return nullptr;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return nullptr;
@@ -219,12 +227,12 @@ const char* attn_fwd_kernel_name(int32_t d, int32_t dtype, const attn_mask* mask
   return variant_name(select_variant(d, dtype, mask, fp8));
 }
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
-                     int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
-                     const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
-                     void* stream) {
-  const attn_status st = attn_check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, mask, blockmap,
-                                         blockmap_bytes, fp8, rescale_tau);
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                         int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
+                         const attn_mask* mask, const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8,
+                         float rescale_tau, void* stream) {
+  const attn_status st = attn_check_args_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap,
+                                             blockmap_bytes, fp8, rescale_tau);
   if (st != ATTN_OK) return st;
   const uint32_t flags = mask ? mask->flags : 0u;
   const bool masked = positional(mask);
@@ -240,6 +248,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   a.lse = lse;
   a.B = B;
   a.H = H;
+  a.Hkv = H_kv;
   a.N = N;
   a.nqb = (N + 127) / 128;
   a.c = (float)((double)scale * kLog2e);
@@ -279,6 +288,14 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     e = d == 128 ? launch_fwd_family<128, kInFp8Qk8>(a, masked, alibi, softcap, s)
                  : launch_fwd_family<64, kInFp8Qk8>(a, masked, alibi, softcap, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
+                     int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
+                     const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
+                     void* stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, dtype, mask, blockmap, blockmap_bytes, fp8,
+                      rescale_tau, stream);
 }
 
 }  // extern "C"

@@ -12,6 +12,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, N;
+  int Hkv;            // key/value heads (H_kv divides H; query head h reads h / (H / Hkv))
   int nqb;            // ceil(N / 128) query blocks = key blocks
   float c;            // scale * log2(e)
   float sc2;          // softcap: 2 * scale * log2(e) / cap
@@ -38,15 +39,25 @@ struct FwdArgs {
 //                    causal mask the last row blocks carry the most key blocks, so this
 //                    is longest-first list scheduling, which evens out the finish times
 //                    when there are only a few workgroups per slot.  With B*H a multiple
-//                    of 8 a head still stays on one XCD (h = L mod B*H).
+//                    of 8 a head still stays on one XCD, and so does a run of
+//                    consecutive heads.
 constexpr int kOrderHeadMajor = 0, kOrderHeavyFirst = 1;
+
+// Flat key/value head index (b * Hkv + key/value head) of flat query head bh = b * H + h.
+__device__ __forceinline__ int kv_head(const FwdArgs& a, int bh) {
+  const int b = bh / a.H, h = bh - b * a.H;
+  return b * a.Hkv + h / (a.H / a.Hkv);
+}
 
 __device__ __forceinline__ void work_item(const FwdArgs& a, int L, int& bh, int& qb) {
   const int nqb = a.nqb;
   if (a.order == kOrderHeavyFirst) {
     const int BH = a.B * a.H;
     const int r = L / BH;
-    bh = L - r * BH;
+    const int i = L - r * BH;
+    // With B*H a multiple of 8, XCD x takes the contiguous heads x*BH/8 .. (x+1)*BH/8-1,
+    // so the query heads of one key/value group share that XCD's L2.
+    bh = (BH & 7) ? i : (i & 7) * (BH >> 3) + (i >> 3);
     qb = nqb - 1 - r;
   } else {
     const int T = a.B * a.H * nqb;

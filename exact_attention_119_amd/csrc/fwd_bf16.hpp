@@ -185,7 +185,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   const int q0 = qb * 128;
   const int qrow = q0 + wave * 32 + l32;
   const bool qvalid = qrow < N;
-  const size_t head_row0 = (size_t)bh * N;
+  const size_t head_row0 = (size_t)bh * N;                 // Q, O, LSE rows of this head
+  const int bkv = kv_head(a, bh);                          // its key/value head
+  const size_t kv_row0 = (size_t)bkv * N;
 
   // ---- block-map lookups (scalar loads through the constant address space: the map
   //      is read-only here and every index is uniform over the workgroup) -------------
@@ -288,8 +290,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // The buffer descriptor of a step starts at its first key row and covers the rows
   // left in the head, so every row past N reads as zero (range-checked on the lane
   // offset; no address ever leaves the head).
-  const unsigned char* const kbase = (const unsigned char*)a.k + head_row0 * HROWB;
-  const unsigned char* const vbase = (const unsigned char*)a.v + head_row0 * HROWB;
+  const unsigned char* const kbase = (const unsigned char*)a.k + kv_row0 * HROWB;
+  const unsigned char* const vbase = (const unsigned char*)a.v + kv_row0 * HROWB;
   auto rsrc = [&](const unsigned char* base, int k0) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * HROWB), (short)0,
                                              max(N - k0, 0) * HROWB, 0x00020000);
@@ -421,12 +423,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   float lvs = 0.f, ivs = 1.f;
   float sq = 1.f, vs_max = 1.f;
   typedef const __attribute__((address_space(4))) float cfloat;
-  cfloat* const ksc = FP8 ? (cfloat*)a.k_scale + (size_t)bh * nqb : nullptr;
-  cfloat* const vsc = FP8 ? (cfloat*)a.v_scale + (size_t)bh * nqb : nullptr;
+  cfloat* const ksc = FP8 ? (cfloat*)a.k_scale + (size_t)bkv * nqb : nullptr;
+  cfloat* const vsc = FP8 ? (cfloat*)a.v_scale + (size_t)bkv * nqb : nullptr;
   if constexpr (FP8) {
     sq = ((cfloat*)a.q_scale)[(size_t)bh * nqb + qb];
     float mx = 0.f;
-    for (int i = lane; i < nqb; i += 64) mx = __builtin_fmaxf(mx, a.v_scale[(size_t)bh * nqb + i]);
+    for (int i = lane; i < nqb; i += 64) mx = __builtin_fmaxf(mx, a.v_scale[(size_t)bkv * nqb + i]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
     vs_max = mx > 0.f ? mx : 1.f;

@@ -176,7 +176,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   const int q0 = qb * 128;
   const int qrow = q0 + wave * 32 + l32;
   const bool qvalid = qrow < N;
-  const size_t head_row0 = (size_t)bh * N;
+  const size_t head_row0 = (size_t)bh * N;  // Q, O, LSE rows of this head
+  const int bkv = kv_head(a, bh);           // its key/value head
+  const size_t kv_row0 = (size_t)bkv * N;
 
   // ---- block-map lookups --------------------------------------------------------
   int nfull, npart;
@@ -250,7 +252,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   float vs_max = 1.f;
   if constexpr (FP8) {
     sq = a.q_scale[(size_t)bh * nqb + qb];
-    const float* vsr = a.v_scale + (size_t)bh * nqb;
+    const float* vsr = a.v_scale + (size_t)bkv * nqb;
     float mx = 0.f;
     for (int i = lane; i < nqb; i += 64) mx = __builtin_fmaxf(mx, vsr[i]);
 #pragma unroll
@@ -271,8 +273,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
   };
 
   // ---- K/V staging: HBM -> VGPRs -> LDS ---------------------------------------------
-  const unsigned char* kg = (const unsigned char*)a.k + head_row0 * KRB;
-  const unsigned char* vg = (const unsigned char*)a.v + head_row0 * KRB;
+  const unsigned char* kg = (const unsigned char*)a.k + kv_row0 * KRB;
+  const unsigned char* vg = (const unsigned char*)a.v + kv_row0 * KRB;
   typedef typename std::conditional<WIDEN_K, u32x2, u32x4>::type KRow;
   KRow kreg[KPASS];
   typedef typename std::conditional<FP8, u32x2, u32x4>::type VRow;
@@ -409,10 +411,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const FwdArgs a) {
     // ---- score modifiers, mask, row maximum ------------------------------------------
     float ct = a.c, sc2t = a.sc2, vs = 1.f, inv_vs = 1.f, log2_vs = 0.f;
     if constexpr (FP8) {
-      const float sk = a.k_scale[(size_t)bh * nqb + kb];
+      const float sk = a.k_scale[(size_t)bkv * nqb + kb];
       ct *= sq * sk;
       sc2t *= sq * sk;
-      vs = a.v_scale[(size_t)bh * nqb + kb] / vs_max;
+      vs = a.v_scale[(size_t)bkv * nqb + kb] / vs_max;
       inv_vs = 1.f / vs;
       log2_vs = log2f(vs);
     }

@@ -40,7 +40,8 @@ ATTN_QK_BF16 = 0
 ATTN_QK_E4M3 = 1
 
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
-           "attn_blockmap_status", "attn_check_args", "attn_fwd", "attn_fwd_kernel_name", "attn_status_str")
+           "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
+           "attn_fwd_kernel_name", "attn_status_str")
 
 
 class AttnError(RuntimeError):
@@ -92,6 +93,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask), vp, sz,
                              ctypes.POINTER(attn_fp8), f32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_check_args_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                        ctypes.POINTER(attn_mask), vp, sz, ctypes.POINTER(attn_fp8), f32]
+    lib.attn_check_args_gqa.restype = i32
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
+                                 vp, sz, ctypes.POINTER(attn_fp8), f32, vp]
+    lib.attn_fwd_gqa.restype = i32
     lib.attn_fwd_kernel_name.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(attn_fp8)]
     lib.attn_fwd_kernel_name.restype = ctypes.c_char_p
     _LIB = lib
@@ -165,6 +172,15 @@ def attn_check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, mask=None, blockm
                                   int(blockmap_bytes), ctypes.byref(fp8) if fp8 else None, float(rescale_tau))
 
 
+def attn_check_args_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask=None, blockmap=None,
+                        blockmap_bytes=0, fp8=None, rescale_tau=8.0) -> int:
+    """attn_check_args with H_kv key/value heads shared by groups of H / H_kv query heads."""
+    return load().attn_check_args_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, H_kv, N, d,
+                                      float(scale), int(dtype), ctypes.byref(mask) if mask else None,
+                                      _ptr(blockmap), int(blockmap_bytes), ctypes.byref(fp8) if fp8 else None,
+                                      float(rescale_tau))
+
+
 def attn_fwd_kernel_name(d: int, dtype: int = ATTN_BF16, mask: Optional[attn_mask] = None,
                          fp8: Optional[attn_fp8] = None) -> Optional[str]:
     """The compiled kernel variant attn_fwd selects (host logic only), or None."""
@@ -182,6 +198,18 @@ def attn_fwd(q, k, v, o, lse, *, scale: float, dtype: int = ATTN_BF16, mask: Opt
                            ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes,
                            ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
            "attn_fwd")
+
+
+def attn_fwd_gqa(q, k, v, o, lse, *, scale: float, dtype: int = ATTN_BF16, mask: Optional[attn_mask] = None,
+                 blockmap=None, fp8: Optional[attn_fp8] = None, rescale_tau: float = 8.0, stream=None) -> None:
+    """Grouped-query forward pass.  q, o: [B][H][N][d]; k, v: [B][H_kv][N][d]; lse: [B][H][N] fp32."""
+    B, H, N, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[1])
+    mbytes = 0 if blockmap is None else blockmap.numel() * blockmap.element_size()
+    _check(load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, H_kv, N, d, float(scale),
+                               int(dtype), ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes,
+                               ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
+           "attn_fwd_gqa")
 
 
 def read_blockmap(blockmap, B: int, N: int) -> dict:

@@ -197,6 +197,27 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      float rescale_tau, void* stream);
 
 /*
+ * Grouped-query attention (GQA; MQA with H_kv = 1), the case the page "FlashAttention 4:
+ * ... για LLMs" (el.linux-konsole.com) lists among FA4's gaps in its section
+ * "Συμβατότητα και τρέχουσα κατάσταση": several query heads share one key/value head.
+ * The same pass with H query heads and H_kv key/value heads, H_kv >= 1 dividing H;
+ * query head h reads key/value head h / (H / H_kv).
+ *   q, o : [B][H][N][d];  lse: [B][H][N];  k, v: [B][H_kv][N][d].
+ *   fp8  : q_scale [B][H][ceil(N/128)], k_scale and v_scale [B][H_kv][ceil(N/128)].
+ *   alibi_slopes: per query head, [H].
+ * attn_check_args / attn_fwd are the case H_kv = H.  Errors: ATTN_ERR_INVALID_ARG when
+ * H_kv < 1 or H_kv does not divide H, otherwise as attn_check_args / attn_fwd.
+ */
+attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale,
+                                int32_t dtype, const attn_mask* mask, const void* blockmap,
+                                size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau);
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                         int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
+                         const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                         const attn_fp8* fp8, float rescale_tau, void* stream);
+
+/*
  * Name of the compiled kernel variant attn_fwd selects for these arguments, e.g.
  * "bf16 d128 masked softcap" (host logic only, no HIP call, usable without a GPU);
  * NULL when the combination is unsupported.  The string is static.  A "masked"

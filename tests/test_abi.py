@@ -103,6 +103,24 @@ def test_check_args_ok_and_errors(L):
     assert ck(dtype=1, fp8=L.make_fp8(P, P, P, pv_mode=5)) == L.ATTN_ERR_UNSUPPORTED
 
 
+def test_check_args_grouped_heads(L):
+    """H_kv key/value heads: must be at least 1 and divide H; H_kv = H is the plain call."""
+    ck = lambda H_kv, **kw: L.attn_check_args_gqa(H_kv=H_kv, **_args(**kw))
+    assert ck(4) == L.ATTN_OK
+    assert ck(2) == L.ATTN_OK
+    assert ck(1) == L.ATTN_OK
+    assert ck(1, dtype=1, fp8=L.make_fp8(P, P, P)) == L.ATTN_OK
+    assert ck(0) == L.ATTN_ERR_INVALID_ARG
+    assert ck(-2) == L.ATTN_ERR_INVALID_ARG
+    assert ck(3) == L.ATTN_ERR_INVALID_ARG
+    assert ck(8) == L.ATTN_ERR_INVALID_ARG
+    assert ck(3, H=6) == L.ATTN_OK
+    assert ck(2, d=96) == L.ATTN_ERR_UNSUPPORTED
+    lib = L.load()
+    st = lib.attn_fwd_gqa(P, P, P, P, P, 1, 4, 3, 16, 64, 0.1, 0, None, None, 0, None, 8.0, None)
+    assert st == L.ATTN_ERR_INVALID_ARG
+
+
 def test_fwd_rejects_before_launch(L):
     """attn_fwd with bad arguments returns the validation error without touching the GPU."""
     lib = L.load()

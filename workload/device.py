@@ -66,8 +66,9 @@ def build_map(dp: DeviceProblem, stream=None) -> None:
 
 
 def forward(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None) -> None:
-    L.attn_fwd(dp.q, dp.k, dp.v, dp.o, dp.lse, scale=dp.p.scale, dtype=dp.dtype, mask=dp.mask,
-               blockmap=dp.blockmap, fp8=dp.fp8, rescale_tau=rescale_tau, stream=stream)
+    fwd = L.attn_fwd if dp.p.Hkv == dp.p.H else L.attn_fwd_gqa
+    fwd(dp.q, dp.k, dp.v, dp.o, dp.lse, scale=dp.p.scale, dtype=dp.dtype, mask=dp.mask,
+        blockmap=dp.blockmap, fp8=dp.fp8, rescale_tau=rescale_tau, stream=stream)
 
 
 def step(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None) -> None:
