@@ -33,5 +33,7 @@ from .attention import (  # noqa: F401
     scores_ref,
     attention_ref,
     attention_problem,
+    attention_varlen_ref,
+    varlen_doc_ids_ref,
 )
 from .blockmap import blockmap_ref, row_intervals_ref, visible_pairs_ref  # noqa: F401

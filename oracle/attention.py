@@ -23,10 +23,16 @@ Game-Changer", liora.io):
   heads, H_kv dividing H, and query head h reads key/value head h // (H / H_kv)
   (same page, section "Συμβατότητα και τρέχουσα κατάσταση": several query heads
   share one key/value projection).
+  variable-length batches (same section: sequences of different lengths batched
+  without padding): sequences packed back to back along one token axis, given by
+  cumulative offsets cu[0] = 0 <= cu[1] <= ... <= cu[nseq] = total; each sequence
+  is the definition above applied to its own tokens, positions counted from its
+  first token.
 
 Readings where the pages are silent: scale first, then softcap, then ALiBi,
 then the mask; default ALiBi slopes 2^(-8(h+1)/H) for heads h = 0..H-1;
-natural-log LSE; under GQA consecutive query heads share a key/value head.
+natural-log LSE; under GQA consecutive query heads share a key/value head;
+a packed batch keeps the head-major [H][total][d] layout of one batch row.
 """
 
 from __future__ import annotations
@@ -123,6 +129,46 @@ def attention_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, *, scale: float, 
     return O, L
 
 
+def varlen_doc_ids_ref(cu_seqlens: np.ndarray, total: int) -> np.ndarray:
+    """int32 [total]: the index of the sequence each packed token belongs to (the last
+    sequence starting at or before it, so empty sequences own no token)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    ids = np.zeros(total, dtype=np.int32)
+    for i in range(len(cu) - 1):
+        ids[cu[i]:cu[i + 1]] = i
+    return ids
+
+
+def attention_varlen_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_seqlens, *, scale: float,
+                         flags: int = 0, window: int = 0, softcap: float = 0.0,
+                         alibi_slopes: Optional[Sequence[float]] = None, rows: Optional[np.ndarray] = None,
+                         heads: Optional[Sequence[int]] = None):
+    """O [H][R][d] and LSE [H][R] of a packed variable-length batch: every sequence on
+    its own (attention_ref on its slice, positions local to it), results placed back
+    at the packed rows.  Q: [H][total][d]; K, V: [H_kv][total][d]; cu_seqlens:
+    [nseq + 1].  `rows` selects packed query rows, `heads` query heads (others NaN)."""
+    if flags & DOCUMENT:
+        raise ValueError("the sequences of a packed batch are its documents")
+    H, total, _ = Q.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must run from 0 to total without decreasing")
+    rows = np.arange(total) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.full((H, len(rows), V.shape[2]), np.nan)
+    L = np.full((H, len(rows)), np.nan)
+    hs = range(H) if heads is None else list(heads)
+    for i in range(len(cu) - 1):
+        a, e = int(cu[i]), int(cu[i + 1])
+        sel = np.nonzero((rows >= a) & (rows < e))[0]
+        if len(sel) == 0:
+            continue
+        o, l = attention_ref(Q[None, :, a:e], K[None, :, a:e], V[None, :, a:e], scale=scale, flags=flags,
+                             window=window, softcap=softcap, alibi_slopes=alibi_slopes, rows=rows[sel] - a,
+                             heads=[(0, h) for h in hs])
+        O[:, sel], L[:, sel] = o[0], l[0]
+    return O, L
+
+
 # ---------------------------------------------------------------------------
 # Whole-problem driver (optionally over a process pool: one task per (b, h))
 # ---------------------------------------------------------------------------
@@ -147,6 +193,12 @@ def attention_problem(p, rows: Optional[np.ndarray] = None, heads: Optional[Sequ
     per worker.
     """
     Q, K, V = decode_problem(p)
+    if getattr(p, "cu_seqlens", None) is not None:
+        hs = None if heads is None else sorted({h for (_, h) in heads})
+        o, l = attention_varlen_ref(Q[0], K[0], V[0], p.cu_seqlens, scale=p.scale, flags=p.flags,
+                                    window=p.window, softcap=p.softcap, alibi_slopes=p.alibi_slopes, rows=rows,
+                                    heads=hs)
+        return o[None], l[None]
     kw = dict(scale=p.scale, flags=p.flags, window=p.window, softcap=p.softcap, doc_id=p.doc_id,
               alibi_slopes=p.alibi_slopes, rows=rows)
     if workers <= 1:

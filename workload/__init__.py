@@ -20,5 +20,6 @@ from .gen import (  # noqa: F401
     draw_doc_lengths,
     e4m3_codes_from_f64,
     make_problem,
+    make_varlen_problem,
     quantize_e4m3_blocks,
 )

@@ -79,6 +79,7 @@ class Problem:
     outlier_channels: Optional[np.ndarray] = None
     alibi_slopes: Optional[np.ndarray] = None
     H_kv: Optional[int] = None
+    cu_seqlens: Optional[np.ndarray] = None  # packed variable-length batch (B = 1): int32 [nseq + 1]
 
     @property
     def Hkv(self) -> int:
@@ -88,7 +89,7 @@ class Problem:
     def digests(self) -> dict:
         """sha256 of every generated buffer (hex)."""
         out = {}
-        for key in ("q", "k", "v", "q_scale", "k_scale", "v_scale", "doc_id"):
+        for key in ("q", "k", "v", "q_scale", "k_scale", "v_scale", "doc_id", "cu_seqlens"):
             arr = getattr(self, key)
             if arr is not None:
                 out[key] = hashlib.sha256(np.ascontiguousarray(arr).tobytes()).hexdigest()
@@ -265,3 +266,29 @@ def make_problem(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", flags: 
     name = f"B{B}H{H}N{N}d{d}" + ("" if H_kv is None else f"Hkv{H_kv}")
     return _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale,
                   doc_lengths, n_outliers, outlier_gain, alibi_slopes, H_kv)
+
+
+def make_varlen_problem(lengths: Sequence[int], H: int, d: int, *, dtype: str = "bf16", flags: int = 0,
+                        window: int = 0, softcap: float = 0.0, scale: Optional[float] = None,
+                        seed: Union[int, Tuple[int, ...]] = 0, n_outliers: int = 0, outlier_gain: float = 20.0,
+                        alibi_slopes: Optional[np.ndarray] = None, H_kv: Optional[int] = None) -> Problem:
+    """A packed variable-length batch: sequences of the given lengths (zeros allowed)
+    back to back in one batch row of N = sum(lengths) tokens, drawn with
+    ``default_rng([119, 2000, *seed])``; cu_seqlens = [0, l0, l0 + l1, ...]."""
+    if flags & ATTN_DOCUMENT:
+        raise ValueError("the sequences of a packed batch are its documents")
+    lengths = [int(x) for x in lengths]
+    if not lengths or min(lengths) < 0 or sum(lengths) < 1:
+        raise ValueError("need at least one token")
+    seed_t = (seed,) if isinstance(seed, int) else tuple(seed)
+    rng = np.random.default_rng([119, 2000, *seed_t])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if alibi_slopes is not None:
+        alibi_slopes = np.asarray(alibi_slopes, dtype=np.float32)
+    N = sum(lengths)
+    name = f"varlen{len(lengths)}H{H}N{N}d{d}" + ("" if H_kv is None else f"Hkv{H_kv}")
+    p = _build(name, rng, 1, H, N, d, dtype, flags, window, softcap, scale, None, n_outliers, outlier_gain,
+               alibi_slopes, H_kv)
+    p.cu_seqlens = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return p
