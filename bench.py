@@ -12,7 +12,8 @@ Default workload: B=4 H=16 N=2048 d=128, causal, bf16 (configuration 2).  Other
 3: B2 H32 N8192 d128 causal+window 1024+softcap 50; 4: B1 H16 N16384 d128
 document-causal+ALiBi; 5: B1 H16 N16384 d128 fp8 plain), --plain-causal the
 configuration-3 shape with a plain causal mask, and --shape B,H,N,d [--mask causal] any
-other bf16 shape (--kv-heads H_kv for grouped-query attention).
+other bf16 shape (--kv-heads H_kv for grouped-query attention), --varlen a packed batch of
+causal sequences of different lengths.
 
 Printed on stdout: ONE JSON line.  Extra diagnostics go to stderr.
 """
@@ -51,6 +52,8 @@ def kernel_source_hash() -> str:
 
 def workload_name(p) -> str:
     mods = []
+    if p.cu_seqlens is not None:
+        mods.append(f"varlen{len(p.cu_seqlens) - 1}")
     if p.flags & 4:
         mods.append("document")
     if p.flags & 1:
@@ -78,8 +81,12 @@ def visible_pairs(p) -> int:
             lo = np.maximum(lo, q - (p.window - 1))
             if not p.flags & 1:
                 hi = np.minimum(hi, q + (p.window - 1))
+        d = None
         if p.flags & 4:
             d = p.doc_id[b]
+        elif p.cu_seqlens is not None:
+            d = np.repeat(np.arange(len(p.cu_seqlens) - 1), np.diff(p.cu_seqlens))
+        if d is not None:
             first = np.searchsorted(d, d, side="left")
             last = np.searchsorted(d, d, side="right") - 1
             lo, hi = np.maximum(lo, first), np.minimum(hi, last)
@@ -135,6 +142,9 @@ def main(argv=None):
                     help="supplementary bf16 workload B,H,N,d (with --mask, --kv-heads), instead of a "
                          "configuration")
     ap.add_argument("--mask", choices=["none", "causal"], default="none", help="mask of a --shape workload")
+    ap.add_argument("--varlen", action="store_true",
+                    help="packed variable-length batch: 16384 tokens in causal sequences of 512..4096, "
+                         "H16 d128 (with --kv-heads)")
     ap.add_argument("--kv-heads", type=int, default=None,
                     help="key/value heads of a --shape workload (grouped-query attention)")
     ap.add_argument("--tau", type=float, default=8.0)
@@ -167,7 +177,11 @@ def main(argv=None):
     import workload as W
     from workload import device as WD
 
-    if args.shape:
+    if args.varlen:
+        import numpy as np
+        lengths = W.draw_doc_lengths(np.random.default_rng([119, 78]), 16384, 512, 4096)
+        p = W.make_varlen_problem(lengths, 16, 128, flags=W.ATTN_CAUSAL, seed=78, H_kv=args.kv_heads)
+    elif args.shape:
         B, H, N, d = (int(x) for x in args.shape.split(","))
         p = W.make_problem(B, H, N, d, flags=W.ATTN_CAUSAL if args.mask == "causal" else 0, seed=4,
                            H_kv=args.kv_heads)

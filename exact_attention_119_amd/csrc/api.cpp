@@ -14,7 +14,8 @@
 
 namespace attn119 {
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
-                           const int32_t* doc_id, hipStream_t stream);
+                           const int32_t* doc_id, const int32_t* cu, int nseq, hipStream_t stream);
+hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t* doc, hipStream_t stream);
 template <int D, int IN>
 hipError_t launch_fwd_family(const FwdArgs& a, bool masked, bool alibi, bool softcap, hipStream_t st);
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
@@ -103,6 +104,28 @@ attn_status check_shape(int32_t B, int32_t N) {
   return ATTN_OK;
 }
 
+// Variable-length workspace: the block map of (B = 1, N = total), then the doc ids.
+size_t varlen_doc_offset(int32_t total) { return map_layout(1, total).total; }
+size_t varlen_bytes(int32_t total) { return varlen_doc_offset(total) + align256((size_t)total * 4); }
+
+attn_status check_varlen_mask(const attn_mask* mask) {
+  const attn_status st = check_mask(mask);
+  if (st != ATTN_OK) return st;
+  if (mask && (mask->flags & ATTN_DOCUMENT)) return ATTN_ERR_INVALID_ARG;  // the sequences are the documents
+  return ATTN_OK;
+}
+
+// The mask a variable-length call runs with: the caller's flags plus the document mask
+// over the workspace's doc ids.
+attn_mask varlen_mask(const attn_mask* mask, const void* workspace, int32_t total) {
+  attn_mask m;
+  std::memset(&m, 0, sizeof(m));
+  if (mask) m = *mask;
+  m.flags |= ATTN_DOCUMENT;
+  m.doc_id = (const int32_t*)((const unsigned char*)workspace + varlen_doc_offset(total));
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,7 +178,8 @@ attn_status attn_blockmap_build(int32_t B, int32_t N, const attn_mask* mask, voi
   const uint32_t flags = mask ? mask->flags : 0u;
   const int window = (mask && (flags & ATTN_WINDOW)) ? mask->window : 0;
   const int32_t* doc = (mask && (flags & ATTN_DOCUMENT)) ? mask->doc_id : nullptr;
-  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, (hipStream_t)stream) != hipSuccess)
+  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, (hipStream_t)stream) !=
+      hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -296,6 +320,49 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      void* stream) {
   return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, dtype, mask, blockmap, blockmap_bytes, fp8,
                       rescale_tau, stream);
+}
+
+attn_status attn_varlen_workspace_bytes(int32_t total, const attn_mask* mask, size_t* bytes) {
+  if (!bytes) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_shape(1, total);
+  if (st != ATTN_OK) return st;
+  st = check_varlen_mask(mask);
+  if (st != ATTN_OK) return st;
+  *bytes = varlen_bytes(total);
+  return ATTN_OK;
+}
+
+attn_status attn_varlen_prepare(const int32_t* cu_seqlens, int32_t nseq, int32_t total, const attn_mask* mask,
+                                void* workspace, size_t bytes, void* stream) {
+  size_t need = 0;
+  const attn_status st = attn_varlen_workspace_bytes(total, mask, &need);
+  if (st != ATTN_OK) return st;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) || nseq < 1 || nseq == INT32_MAX)
+    return ATTN_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
+  const attn_mask m = varlen_mask(mask, workspace, total);
+  const hipStream_t s = (hipStream_t)stream;
+  if (launch_varlen_doc_ids(cu_seqlens, nseq, total, (int32_t*)m.doc_id, s) != hipSuccess) return ATTN_ERR_HIP;
+  const int window = (m.flags & ATTN_WINDOW) ? m.window : 0;
+  if (launch_blockmap((unsigned char*)workspace, 1, total, m.flags, window, m.doc_id, cu_seqlens, nseq, s) !=
+      hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int32_t H,
+                            int32_t H_kv, int32_t total, int32_t d, float scale, int32_t dtype,
+                            const attn_mask* mask, const void* workspace, size_t bytes, const attn_fp8* fp8,
+                            float rescale_tau, void* stream) {
+  size_t need = 0;
+  const attn_status st = attn_varlen_workspace_bytes(total, mask, &need);
+  if (st != ATTN_OK) return st;
+  if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
+  const attn_mask m = varlen_mask(mask, workspace, total);
+  return attn_fwd_gqa(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace,
+                      varlen_doc_offset(total), fp8, rescale_tau, stream);
 }
 
 }  // extern "C"

@@ -9,8 +9,9 @@
 // 128-row query block:
 //   its rows (one thread each): the interval, and a flag for any place where doc_id
 //          decreases (documents must be contiguous runs), giving the block's status
-//          word: 1 if doc_id decreases at one of its rows (a batch row with any such
-//          word is invalid);
+//          word: 1 if doc_id decreases at one of its rows, or, for a packed batch, if
+//          its share of the sequence offsets is out of order (a batch row with any
+//          such word is invalid);
 //   its row of blocks: the class of every 128x128 block, the ascending lists of FULL
 //          and PARTIAL key blocks and the visible-pair count of the query block.
 // No atomics, no memset: every byte of every section is written, so the result is
@@ -26,6 +27,8 @@ struct MapArgs {
   int B, N, nb;
   uint32_t flags;  // positional flags only
   int window;
+  const int32_t* cu;  // packed variable-length batch (B = 1): offsets [nseq + 1], else null
+  int nseq;
 };
 
 // First index i in [0, N) with row[i] >= v (row non-decreasing).
@@ -80,7 +83,16 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
     s_lo[tid] = lo;
     s_hi[tid] = hi;
   }
-  // status: 1 if doc_id decreases between one of this block's rows and the next row
+  // Packed batches: the doc ids came from cu by binary search, which is exact only for
+  // offsets that run from 0 to N without decreasing.  The workgroups share the check of
+  // that: workgroup qb takes the pairs (cu[i], cu[i+1]) with i = qb*256 + tid + k*nb*256.
+  if (a.cu) {
+    for (int i = qb * 256 + tid; i < a.nseq; i += nb * 256)
+      if (a.cu[i] > a.cu[i + 1]) bad = 1;
+    if (qb == 0 && tid == 0 && (a.cu[0] != 0 || a.cu[a.nseq] != N)) bad = 1;
+  }
+  // status: 1 if doc_id decreases between one of this block's rows and the next row (or
+  // the offsets this workgroup checked are out of order)
   const int bad_any = __syncthreads_or(bad);  // (also orders the interval writes above)
   if (tid == 0) ((int32_t*)(a.map + a.lay.status))[(size_t)b * nb + qb] = bad_any ? 1 : 0;
 
@@ -149,8 +161,31 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   }
 }
 
+// Packed variable-length batch: token t belongs to sequence i when cu[i] <= t < cu[i+1].
+// The id is the number of interior boundaries cu[1..nseq-1] at or below t (a binary
+// search; cu[0] and cu[nseq] are not read here).  Every read stays inside cu[1..nseq-1]
+// whatever the values; the block-map kernel checks that the offsets are in order and
+// marks the batch row invalid when they are not.
+__global__ void __launch_bounds__(256) varlen_doc_ids_kernel(const int32_t* cu, int nseq, int total,
+                                                             int32_t* doc) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  int lo = 1, hi = nseq;  // first index in [1, nseq) with cu[index] > t
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid + 1; else hi = mid;
+  }
+  doc[t] = lo - 1;
+}
+
+hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t* doc, hipStream_t stream) {
+  hipLaunchKernelGGL(varlen_doc_ids_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, cu, nseq, total,
+                     doc);
+  return hipGetLastError();
+}
+
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
-                           const int32_t* doc_id, hipStream_t stream) {
+                           const int32_t* doc_id, const int32_t* cu, int nseq, hipStream_t stream) {
   MapArgs a;
   a.map = map;
   a.lay = map_layout(B, N);
@@ -160,6 +195,8 @@ hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int
   a.nb = (N + kBlock - 1) / kBlock;
   a.flags = flags & kPositional;
   a.window = window;
+  a.cu = cu;
+  a.nseq = nseq;
   hipLaunchKernelGGL(blockmap_kernel, dim3(a.nb, B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -41,7 +41,8 @@ ATTN_QK_E4M3 = 1
 
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
-           "attn_fwd_kernel_name", "attn_status_str")
+           "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
+           "attn_fwd_varlen")
 
 
 class AttnError(RuntimeError):
@@ -99,6 +100,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
                                  vp, sz, ctypes.POINTER(attn_fp8), f32, vp]
     lib.attn_fwd_gqa.restype = i32
+    lib.attn_varlen_workspace_bytes.argtypes = [i32, ctypes.POINTER(attn_mask), ctypes.POINTER(sz)]
+    lib.attn_varlen_workspace_bytes.restype = i32
+    lib.attn_varlen_prepare.argtypes = [vp, i32, i32, ctypes.POINTER(attn_mask), vp, sz, vp]
+    lib.attn_varlen_prepare.restype = i32
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
+                                    vp, sz, ctypes.POINTER(attn_fp8), f32, vp]
+    lib.attn_fwd_varlen.restype = i32
     lib.attn_fwd_kernel_name.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(attn_fp8)]
     lib.attn_fwd_kernel_name.restype = ctypes.c_char_p
     _LIB = lib
@@ -210,6 +218,36 @@ def attn_fwd_gqa(q, k, v, o, lse, *, scale: float, dtype: int = ATTN_BF16, mask:
                                int(dtype), ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes,
                                ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
            "attn_fwd_gqa")
+
+
+def attn_varlen_workspace_bytes(total: int, mask: Optional[attn_mask] = None) -> int:
+    n = ctypes.c_size_t()
+    _check(load().attn_varlen_workspace_bytes(int(total), ctypes.byref(mask) if mask else None, ctypes.byref(n)),
+           "attn_varlen_workspace_bytes")
+    return n.value
+
+
+def attn_varlen_prepare(cu_seqlens, total: int, mask: Optional[attn_mask], workspace, stream=None) -> None:
+    """Sequence ids and block map of a packed batch; cu_seqlens: int32 device [nseq + 1]."""
+    nseq = int(cu_seqlens.numel()) - 1
+    _check(load().attn_varlen_prepare(_ptr(cu_seqlens), nseq, int(total), ctypes.byref(mask) if mask else None,
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)),
+           "attn_varlen_prepare")
+
+
+def attn_fwd_varlen(q, k, v, o, lse, *, scale: float, workspace, dtype: int = ATTN_BF16,
+                    mask: Optional[attn_mask] = None, fp8: Optional[attn_fp8] = None, rescale_tau: float = 8.0,
+                    stream=None) -> None:
+    """Packed variable-length forward pass.  q, o: [H][total][d]; k, v: [H_kv][total][d];
+    lse: [H][total]; workspace prepared by attn_varlen_prepare."""
+    H, total, d = (int(x) for x in q.shape[-3:])
+    H_kv = int(k.shape[-3])
+    _check(load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), H, H_kv, total, d, float(scale),
+                                  int(dtype), ctypes.byref(mask) if mask else None, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
+           "attn_fwd_varlen")
 
 
 def read_blockmap(blockmap, B: int, N: int) -> dict:

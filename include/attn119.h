@@ -134,7 +134,9 @@ typedef struct attn_fp8 {
  *   row_hi   : int32  [B][N]            largest visible key of each query
  *   pairs    : int64  [B][nqb]          visible (q, k) pairs of each query block
  *   status   : int32  [B][nqb]          1 if doc_id[b] decreases from a row of this block to
- *                                       the next row, else 0 (a batch row with any 1 is invalid)
+ *                                       the next row (packed batches: or the share of the
+ *                                       sequence offsets this block checks is out of order),
+ *                                       else 0 (a batch row with any 1 is invalid)
  */
 typedef struct attn_blockmap_header {
   uint32_t magic; /* 0x39313141 */
@@ -216,6 +218,40 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
                          int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
                          const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
                          const attn_fp8* fp8, float rescale_tau, void* stream);
+
+/*
+ * Variable-length batches (varlen): sequences of different lengths packed one after
+ * another without padding, the other gap the page "FlashAttention 4: ... για LLMs"
+ * (el.linux-konsole.com) names in its section "Συμβατότητα και τρέχουσα κατάσταση".
+ * Each sequence attends only to itself, so a packed batch is the pass with B = 1,
+ * N = total and the document mask whose documents are the sequences; the mask's
+ * other flags (ATTN_CAUSAL, ATTN_WINDOW, ATTN_ALIBI, ATTN_SOFTCAP) act inside each
+ * sequence exactly as on a separate batch row (positions are only ever compared
+ * within one sequence, and differences of packed positions equal differences of
+ * positions in the sequence).  ATTN_DOCUMENT itself is not accepted (INVALID_ARG).
+ *   cu_seqlens: device int32 [nseq + 1], non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[nseq] = total; sequence i is tokens cu_seqlens[i] ..
+ *               cu_seqlens[i+1]-1 (empty sequences allowed).  An offset array that
+ *               breaks this (a decrease, a first entry other than 0, a last entry other
+ *               than total) is reported by attn_blockmap_status(workspace,
+ *               attn_blockmap_bytes(1, total, mask)) as ATTN_ERR_BAD_DOC_ID, and O and
+ *               LSE are then NaN.
+ *   q, o : [H][total][d];  k, v : [H_kv][total][d];  lse : [H][total]   (B = 1 layout)
+ *   fp8 scales: q_scale [H][ceil(total/128)], k_scale and v_scale [H_kv][ceil(total/128)],
+ *               one scale per 128 tokens of the packed stream.
+ *   workspace : caller-owned device memory of attn_varlen_workspace_bytes, 16-byte
+ *               aligned: the block map of (1, total), then the int32 sequence id of
+ *               every token.  attn_varlen_prepare fills it once per batch; any number
+ *               of attn_fwd_varlen calls (say, one per layer) then read it.
+ * Errors as attn_check_args_gqa; a workspace of the wrong size is ATTN_ERR_BAD_BLOCKMAP.
+ */
+attn_status attn_varlen_workspace_bytes(int32_t total, const attn_mask* mask, size_t* bytes);
+attn_status attn_varlen_prepare(const int32_t* cu_seqlens, int32_t nseq, int32_t total, const attn_mask* mask,
+                                void* workspace, size_t bytes, void* stream);
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int32_t H,
+                            int32_t H_kv, int32_t total, int32_t d, float scale, int32_t dtype,
+                            const attn_mask* mask, const void* workspace, size_t bytes, const attn_fp8* fp8,
+                            float rescale_tau, void* stream);
 
 /*
  * Name of the compiled kernel variant attn_fwd selects for these arguments, e.g.

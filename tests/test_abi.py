@@ -121,6 +121,35 @@ def test_check_args_grouped_heads(L):
     assert st == L.ATTN_ERR_INVALID_ARG
 
 
+def test_varlen_validation(L):
+    """Packed variable-length batches: workspace = block map of (1, total), then int32 ids."""
+    m = L.make_mask(L.ATTN_CAUSAL)
+    for total in (1, 300, 4096):
+        mb = L.attn_blockmap_bytes(1, total, m)
+        assert L.attn_varlen_workspace_bytes(total, m) == mb + ((4 * total + 255) // 256) * 256
+        assert L.attn_varlen_workspace_bytes(total, None) == L.attn_varlen_workspace_bytes(total, m)
+    with pytest.raises(L.AttnError):
+        L.attn_varlen_workspace_bytes(300, L.make_mask(L.ATTN_DOCUMENT, doc_id=P))
+    with pytest.raises(L.AttnError):
+        L.attn_varlen_workspace_bytes(0, m)
+    lib = L.load()
+    ws = L.attn_varlen_workspace_bytes(300, m)
+    prep = lambda cu, nseq, total, bytes_, wsp=P: lib.attn_varlen_prepare(cu, nseq, total, ctypes.byref(m), wsp,
+                                                                         bytes_, None)
+    assert prep(None, 2, 300, ws) == L.ATTN_ERR_INVALID_ARG
+    assert prep(P + 2, 2, 300, ws) == L.ATTN_ERR_INVALID_ARG
+    assert prep(P, 0, 300, ws) == L.ATTN_ERR_INVALID_ARG
+    assert prep(P, 2, 0, ws) == L.ATTN_ERR_INVALID_ARG
+    assert prep(P, 2, 300, ws - 1) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert prep(P, 2, 300, ws, P + 8) == L.ATTN_ERR_INVALID_ARG
+    fwd = lambda H, H_kv, bytes_, mask=m: lib.attn_fwd_varlen(P, P, P, P, P, H, H_kv, 300, 128, 0.1, 0,
+                                                             ctypes.byref(mask) if mask else None, P, bytes_,
+                                                             None, 8.0, None)
+    assert fwd(4, 2, ws + 256) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert fwd(4, 3, ws) == L.ATTN_ERR_INVALID_ARG
+    assert fwd(4, 2, ws, L.make_mask(L.ATTN_DOCUMENT, doc_id=P)) == L.ATTN_ERR_INVALID_ARG
+
+
 def test_fwd_rejects_before_launch(L):
     """attn_fwd with bad arguments returns the validation error without touching the GPU."""
     lib = L.load()

@@ -28,8 +28,9 @@ class DeviceProblem:
     dtype: int
     mask: Optional[L.attn_mask]
     fp8: Optional[L.attn_fp8]
-    blockmap: Optional[torch.Tensor]
+    blockmap: Optional[torch.Tensor]  # the block map, or the variable-length workspace
     keep: tuple  # device tensors the mask / fp8 structs point to
+    cu_seqlens: Optional[torch.Tensor] = None  # packed variable-length batch
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -54,6 +55,11 @@ def to_device(p: Problem, device="cuda", pv_mode: int = L.ATTN_PV_F16,
     o = torch.empty((p.B, p.H, p.N, p.d), dtype=torch.bfloat16, device=device)
     lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=device)
     blockmap = None
+    if p.cu_seqlens is not None:
+        cu = _dev(p.cu_seqlens, device)
+        nbytes = L.attn_varlen_workspace_bytes(p.N, mask)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return DeviceProblem(p, q, k, v, o, lse, dtype, mask, fp8, ws, keep, cu)
     if p.flags & L.POSITIONAL:
         nbytes = L.attn_blockmap_bytes(p.B, p.N, mask)
         blockmap = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -61,11 +67,17 @@ def to_device(p: Problem, device="cuda", pv_mode: int = L.ATTN_PV_F16,
 
 
 def build_map(dp: DeviceProblem, stream=None) -> None:
-    if dp.blockmap is not None:
+    if dp.cu_seqlens is not None:
+        L.attn_varlen_prepare(dp.cu_seqlens, dp.p.N, dp.mask, dp.blockmap, stream)
+    elif dp.blockmap is not None:
         L.attn_blockmap_build(dp.p.B, dp.p.N, dp.mask, dp.blockmap, stream)
 
 
 def forward(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None) -> None:
+    if dp.cu_seqlens is not None:
+        L.attn_fwd_varlen(dp.q[0], dp.k[0], dp.v[0], dp.o[0], dp.lse[0], scale=dp.p.scale, workspace=dp.blockmap,
+                          dtype=dp.dtype, mask=dp.mask, fp8=dp.fp8, rescale_tau=rescale_tau, stream=stream)
+        return
     fwd = L.attn_fwd if dp.p.Hkv == dp.p.H else L.attn_fwd_gqa
     fwd(dp.q, dp.k, dp.v, dp.o, dp.lse, scale=dp.p.scale, dtype=dp.dtype, mask=dp.mask,
         blockmap=dp.blockmap, fp8=dp.fp8, rescale_tau=rescale_tau, stream=stream)
