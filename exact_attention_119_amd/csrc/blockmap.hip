@@ -107,19 +107,39 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   int32_t* idx_full = (int32_t*)(a.map + a.lay.idx) + ((size_t)b * nb + qb) * 2 * nb;
   int32_t* idx_part = idx_full + nb;
 
-  // classes and ascending CSR lists, 256 key blocks per round (64 per wave)
+  // classes and ascending CSR lists, up to 256 key blocks per round (64 per wave).  With
+  // K < 256 key blocks in a round, the rows are split into 256/K chunks so that every
+  // thread scans a share of them (a short serial loop over LDS instead of 128 rows).
+  __shared__ unsigned char s_any[256], s_all[256];
   int full_base = 0, part_base = 0;
   for (int kb0 = 0; kb0 < nb; kb0 += 256) {
+    const int K = min(256, nb - kb0);
+    const int C = 256 / K;              // row chunks per key block
+    const int R = (nrows + C - 1) / C;  // rows per chunk
+    {
+      const int kl = tid % K, ch = tid / K;
+      bool any = false, all = true;
+      if (ch < C) {
+        const int k0 = (kb0 + kl) * kBlock, k1 = min(N, k0 + kBlock) - 1;
+        const int r1 = min(nrows, ch * R + R);
+        for (int r = ch * R; r < r1; ++r) {
+          const int lo = s_lo[r], hi = s_hi[r];
+          any |= (max(lo, k0) <= min(hi, k1));
+          all &= (lo <= k0) && (hi >= k1);
+        }
+      }
+      s_any[tid] = any;
+      s_all[tid] = all;
+    }
+    __syncthreads();
     const int kb = kb0 + tid;
     int c = 0;
-    if (kb < nb) {
+    if (tid < K) {
       const int k0 = kb * kBlock, k1 = min(N, k0 + kBlock) - 1;
-      const bool whole = (nrows == kBlock) && (k1 - k0 + 1 == kBlock);
-      bool any = false, all = whole;
-      for (int r = 0; r < nrows; ++r) {
-        const int lo = s_lo[r], hi = s_hi[r];
-        any |= (max(lo, k0) <= min(hi, k1));
-        all &= (lo <= k0) && (hi >= k1);
+      bool any = false, all = (nrows == kBlock) && (k1 - k0 + 1 == kBlock);
+      for (int ch = 0; ch < C; ++ch) {
+        any |= s_any[ch * K + tid] != 0;
+        all &= s_all[ch * K + tid] != 0;
       }
       c = !any ? 0 : (all ? 2 : 1);
       cls[kb] = (unsigned char)c;

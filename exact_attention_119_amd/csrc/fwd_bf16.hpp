@@ -196,6 +196,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   cint* flist = nullptr;
   cint* plist = nullptr;
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
+  int kb_first = 0;  // first block of the order (masked: read beside the counts)
   bool invalid = false;
   if constexpr (MASKED) {
     const __attribute__((address_space(4))) MapHeader* hd =
@@ -207,6 +208,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     npart = min(max(cnt[1], 0), nqb - nfull);
     flist = (cint*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
     plist = flist + nqb;
+    {
+      // both list heads are loaded with the counts, so the first tiles can be requested
+      // without waiting for the block order below
+      const int p0 = plist[0], f0 = flist[0];
+      kb_first = min(max(npart > 0 ? p0 : f0, 0), nqb - 1);
+    }
     if (qvalid) {
       lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
       hi_q = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
@@ -262,6 +269,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     }
     return kb * 128 + (s & 1) * BN;
   };
+  // the same for the steps of the first block, without reading the block order
+  auto step_k0_first = [&](int s) -> int {
+    if constexpr (MASKED) return s < 2 ? kb_first * 128 + (s & 1) * BN : step_k0(s);
+    else return step_k0(s);
+  };
 
   // ---- Q tile -> VGPRs (B operand of S^T = K Q^T) ----------------------------------------
   bf16x8 qf[NQC];
@@ -305,13 +317,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     koff[r] = row * ROWB + (pos ^ kswz(row)) * 16;
     voff[r] = row * ROWB + (pos ^ vswz(row)) * 16;
   }
-  auto issue_k = [&](int s, lds_u8* dst) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, step_k0(s));
+  auto issue_k = [&](int k0, lds_u8* dst) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
 #pragma unroll
     for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, koff[r]);
   };
-  auto issue_v = [&](int s, lds_u8* dst) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, step_k0(s));
+  auto issue_v = [&](int k0, lds_u8* dst) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
 #pragma unroll
     for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, voff[r]);
   };
@@ -327,17 +339,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   constexpr int SCH = CPT / 8;     // 16-byte 16-bit chunks per thread per tile
   u32x4 kst[FP8 ? SLD : 1], vst[FP8 ? SLD : 1];
   const int srow = tid >> 2;
-  auto stage_k = [&](int s) {
+  auto stage_k = [&](int k0) {
     if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, step_k0(s));
+      const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
 #pragma unroll
       for (int j = 0; j < SLD; ++j)
         kst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, srow * D + (tid & 3) * CPT + 16 * j, 0, 0));
     }
   };
-  auto stage_v = [&](int s) {
+  auto stage_v = [&](int k0) {
     if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, step_k0(s));
+      const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
 #pragma unroll
       for (int j = 0; j < SLD; ++j)
         vst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, srow * D + (tid & 3) * CPT + 16 * j, 0, 0));
@@ -690,17 +702,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   const int np_steps = 2 * npart;
   if (nsteps > 0) {
     if constexpr (FP8) {
-      stage_k(0);
-      stage_v(0);
+      stage_k(step_k0_first(0));
+      stage_v(step_k0_first(0));
       commit_k(kl0);
       commit_v(vl0);
       if (1 < nsteps) {
-        stage_k(1);
-        stage_v(1);
+        stage_k(step_k0_first(1));
+        stage_v(step_k0_first(1));
       }
     } else {
-      issue_k(0, kl0);
-      issue_v(0, vl0);
+      issue_k(step_k0_first(0), kl0);
+      issue_v(step_k0_first(0), vl0);
     }
   }
   for (int s = 0; s < np_steps; ++s) {
@@ -713,15 +725,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
         commit_k((s & 1) ? kl0 : kl1);
         commit_v((s & 1) ? vl0 : vl1);
         if (s + 2 < nsteps) {
-          stage_k(s + 2);
-          stage_v(s + 2);
+          stage_k(step_k0(s + 2));
+          stage_v(step_k0(s + 2));
         }
       } else {
-        issue_k(s + 1, (s & 1) ? kl0 : kl1);
-        issue_v(s + 1, (s & 1) ? vl0 : vl1);
+        issue_k(step_k0_first(s + 1), (s & 1) ? kl0 : kl1);
+        issue_v(step_k0_first(s + 1), (s & 1) ? vl0 : vl1);
       }
     }
     const int k0 = step_k0(s);
+    // A wave none of whose rows sees a key of this step skips its arithmetic: its scores
+    // would all be hidden, p = 0, and the running state would stay as it is.
+    if (__builtin_amdgcn_ballot_w64(lo_q <= k0 + 63 && hi_q >= k0) == 0) continue;
     scales_p(k0);
     scales_e(k0);
     qk_sched(kc, sa);
@@ -774,21 +789,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       if constexpr (FP8 && ISSUE_K && i >= E && i < E + SCH) {
         commit_k_chunk(kcur, i - E);
         if constexpr (i == E + SCH - 1) {
-          if (s + 3 < nsteps) stage_k(s + 3);
+          if (s + 3 < nsteps) stage_k(step_k0(s + 3));
         }
       }
       if constexpr (FP8 && NEXT && i >= E + SCH && i < E + 2 * SCH) {
         commit_v_chunk(vnext, i - E - SCH);
         if constexpr (i == E + 2 * SCH - 1) {
-          if (s + 2 < nsteps) stage_v(s + 2);
+          if (s + 2 < nsteps) stage_v(step_k0(s + 2));
         }
       }
     };
     auto loads_and_rescale = [&]() {
       if constexpr (FP8) {
       } else {
-        if constexpr (ISSUE_K) issue_k(s + 2, kcur);
-        if constexpr (NEXT) issue_v(s + 1, vnext);
+        if constexpr (ISSUE_K) issue_k(step_k0(s + 2), kcur);
+        if constexpr (NEXT) issue_v(step_k0(s + 1), vnext);
       }
       scales_e(step_k0(s));
       moff = rescale(mcur, step_k0(s));
@@ -892,9 +907,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     if (t + 1 < nsteps) {
       if constexpr (FP8) {
         commit_k(kl1);
-        if (t + 2 < nsteps) stage_k(t + 2);
+        if (t + 2 < nsteps) stage_k(step_k0(t + 2));
       } else {
-        issue_k(t + 1, kl1);
+        issue_k(step_k0_first(t + 1), kl1);
       }
     }
     qk_full(kl0, sa);
