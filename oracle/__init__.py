@@ -20,7 +20,8 @@ Sources (pages, cited by title and section):
     Einschränkungen": block sparsity (skipping fully masked blocks).
   * "FlashAttention-3: Rekordverdächtige Geschwindigkeit und Präzision bei
     AI-Modellen" (ctol-digital.de) -- section "Analyse": FP8 with block
-    quantisation.
+    quantisation, and the processing against outlier features read as
+    incoherent processing (quant.py).
 
 Every function is pinned by the CPU tests (brute force, library special cases,
 closed forms and invariants); see tests/test_oracle_*.py.
@@ -37,3 +38,4 @@ from .attention import (  # noqa: F401
     varlen_doc_ids_ref,
 )
 from .blockmap import blockmap_ref, row_intervals_ref, visible_pairs_ref  # noqa: F401
+from .quant import e4m3_encode, fwht_f32, quantize_blocks_ref, signs_from_bits  # noqa: F401
