@@ -131,6 +131,73 @@ def traffic_record(name: str):
     return rec.get("bytes_per_launch")
 
 
+QUANT_SIGNS = [0x9E3779B9, 0x7F4A7C15, 0x2545F491, 0x4F6CDD1D]
+
+
+def bench_quant(args):
+    """One step = block-quantise Q and K (rotated, one sign vector) and V (plain) from bf16."""
+    import numpy as np
+    import torch
+    import workload as W
+    from exact_attention_119_amd import lib as L
+    p = W.make_problem(1, 16, 16384, 128, n_outliers=4, outlier_gain=20.0, seed=55)
+    nblk = (p.N + 127) // 128
+    xs = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in (p.q, p.k, p.v)]
+    codes = [torch.empty(x.shape, dtype=torch.uint8, device="cuda") for x in xs]
+    scales = [torch.empty((p.B, p.H, nblk), dtype=torch.float32, device="cuda") for _ in xs]
+    signs = [QUANT_SIGNS, QUANT_SIGNS, None]
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        for i in range(3):
+            if evs is not None:
+                evs[i][0].record(stream)
+            L.attn_fp8_quantize(xs[i], codes[i], scales[i], signs[i])
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rot = sorted(e[i][0].elapsed_time(e[i][1]) for e in evs for i in (0, 1))
+    rot_avg = sum(rot) / len(rot)
+    elems = p.B * p.H * p.N * p.d
+    bytes_launch = elems * 3 + 4 * p.B * p.H * nblk
+    step_ms = wall * 1e3 / args.steps
+    achieved = bytes_launch / (rot_avg * 1e-3) / 1e9
+    log(f"bench: quantise step {step_ms:.4f} ms (3 launches), rotated launch avg {rot_avg:.4f} ms")
+    out = {"metric": "fp8 block quantisation with incoherent processing, GB/s of algorithmic HBM traffic",
+           "value": round(3 * bytes_launch / (step_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8",
+           "data": "synthetic (seeded N(0,1), four channels x20)",
+           "config": {"workload": "quantise Q, K (rotated) and V: B1 H16 N16384 d128 bf16", "elements_per_launch": elems,
+                      "bytes_per_launch": bytes_launch, "parallelism": "single GPU"},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "quant_kernel<128> (rotated)", "kernel_avg_ms": round(rot_avg, 5)}}
+    if not args.no_cpu:
+        from oracle import quant as Qz
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 10.0) and n < p.H:
+            Qz.quantize_blocks_ref(p.q[:, n:n + 1], np.array(QUANT_SIGNS, np.uint32))
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n * p.N * p.d * 3 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n} of {p.H} heads of Q, rotated, float32 numpy, "
+                                                           f"{dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +217,9 @@ def main(argv=None):
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    ap.add_argument("--quant", action="store_true",
+                    help="instead: the device fp8 quantiser (Q and K rotated, V plain) on the fp8 workload's "
+                         "shape B1 H16 N16384 d128 from bf16")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="instead: run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -176,6 +246,9 @@ def main(argv=None):
 
     import workload as W
     from workload import device as WD
+
+    if args.quant:
+        return bench_quant(args)
 
     if args.varlen:
         import numpy as np

@@ -16,6 +16,8 @@ namespace attn119 {
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
                            const int32_t* doc_id, const int32_t* cu, int nseq, hipStream_t stream);
 hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t* doc, hipStream_t stream);
+hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N, int d, const uint32_t* signs,
+                        hipStream_t stream);
 template <int D, int IN>
 hipError_t launch_fwd_family(const FwdArgs& a, bool masked, bool alibi, bool softcap, hipStream_t st);
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
@@ -363,6 +365,19 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   const attn_mask m = varlen_mask(mask, workspace, total);
   return attn_fwd_gqa(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace,
                       varlen_doc_offset(total), fp8, rescale_tau, stream);
+}
+
+attn_status attn_fp8_quantize(const void* x, void* codes, float* scales, int32_t B, int32_t H, int32_t N,
+                              int32_t d, const uint32_t* rotate_signs, void* stream) {
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H * ((N + 127) / 128) > (int64_t)INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if (launch_quant(x, codes, scales, B * H, N, d, rotate_signs, (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 }  // extern "C"

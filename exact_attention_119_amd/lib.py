@@ -42,7 +42,7 @@ ATTN_QK_E4M3 = 1
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
-           "attn_fwd_varlen")
+           "attn_fwd_varlen", "attn_fp8_quantize")
 
 
 class AttnError(RuntimeError):
@@ -107,6 +107,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
                                     vp, sz, ctypes.POINTER(attn_fp8), f32, vp]
     lib.attn_fwd_varlen.restype = i32
+    lib.attn_fp8_quantize.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.attn_fp8_quantize.restype = i32
     lib.attn_fwd_kernel_name.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(attn_fp8)]
     lib.attn_fwd_kernel_name.restype = ctypes.c_char_p
     _LIB = lib
@@ -248,6 +250,20 @@ def attn_fwd_varlen(q, k, v, o, lse, *, scale: float, workspace, dtype: int = AT
                                   workspace.numel() * workspace.element_size(),
                                   ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
            "attn_fwd_varlen")
+
+
+def attn_fp8_quantize(x, codes, scales, rotate_signs=None, stream=None) -> None:
+    """Block-quantise bf16 x [B][H][N][d] to e4m3 codes (uint8, same shape) and fp32 scales
+    [B][H][ceil(N/128)] on the device; rotate_signs: d/32 sign words (host) or None."""
+    B, H, N, d = (int(t) for t in x.shape)
+    sg = None
+    if rotate_signs is not None:
+        words = [int(w) & 0xFFFFFFFF for w in rotate_signs]
+        if len(words) != d // 32:
+            raise ValueError(f"rotate_signs needs {d // 32} words")
+        sg = (ctypes.c_uint32 * len(words))(*words)
+    _check(load().attn_fp8_quantize(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, sg, _stream(stream)),
+           "attn_fp8_quantize")
 
 
 def read_blockmap(blockmap, B: int, N: int) -> dict:

@@ -254,6 +254,29 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             float rescale_tau, void* stream);
 
 /*
+ * FP8 block quantisation on the device, with optional incoherent processing: the step
+ * before an ATTN_FP8_E4M3 call.  The FlashAttention-3 news (ctol-digital.de), section
+ * "Analyse", names block quantisation and a processing step against outlier features
+ * (read as incoherent processing: Q and K multiplied by one random orthogonal matrix,
+ * which keeps Q.K^T).  For every (b, h, 128-row block) of x:
+ *   y = x, or with rotate_signs: y = (x * signs) H, H the Sylvester Walsh-Hadamard
+ *       matrix of order d, computed in fp32 by the fast transform (strides 1, 2, ...,
+ *       d/2), signs[j] = -1 when bit j % 32 of rotate_signs[j / 32] is set, else +1;
+ *   s = fp32(max|y| / 448) and g = fp32(448 / max|y|), both 1 for an all-zero block;
+ *   codes = OCP e4m3fn of fp32(y * g), round to nearest even, saturated at +-448;
+ *   scales[b][h][block] = s, or with rotation fp32(s * fp32(1/sqrt(d))), so that
+ *       code * scale approximates x R with R = D H / sqrt(d) orthogonal.
+ * Give Q and K the same signs (and V none) to keep Q.K^T and the output unchanged.
+ *   x      : device bf16 [B][H][N][d];  codes: device uint8 [B][H][N][d];
+ *   scales : device fp32 [B][H][ceil(N/128)];  d = 64 or 128;
+ *   rotate_signs: HOST array of d/32 words, read during the call, or NULL (no rotation).
+ * x and codes 16-byte aligned.  Errors: ATTN_ERR_INVALID_ARG (null or misaligned
+ * pointer, B, H or N < 1), ATTN_ERR_UNSUPPORTED (d), ATTN_ERR_HIP (launch).
+ */
+attn_status attn_fp8_quantize(const void* x, void* codes, float* scales, int32_t B, int32_t H, int32_t N,
+                              int32_t d, const uint32_t* rotate_signs, void* stream);
+
+/*
  * Name of the compiled kernel variant attn_fwd selects for these arguments, e.g.
  * "bf16 d128 masked softcap" (host logic only, no HIP call, usable without a GPU);
  * NULL when the combination is unsupported.  The string is static.  A "masked"

@@ -17,9 +17,12 @@ same precision as the device):
   2. with rotation: y = x H by the fast Walsh-Hadamard transform in fp32, stages
      of stride 1, 2, 4, ..., d/2, each mapping the pair (x[i], x[i+h]) of every
      2h-aligned group to (x[i] + x[i+h], x[i] - x[i+h]); without: y = x.
-  3. amax = max |y| over the block; s = fp32(amax / 448), or 1 for an all-zero block.
-  4. code = the e4m3 value nearest to fp32(y / s), ties to the even code,
-     magnitudes above 448 saturated to 448.
+  3. amax = max |y| over the block; s = fp32(amax / 448) and g = fp32(448 / amax),
+     both 1 for an all-zero block.
+  4. code = the e4m3 value nearest to fp32(y * g), ties to the even code,
+     magnitudes above 448 saturated to 448 (a multiplication by the block's inverse
+     scale, the usual form of block quantisation; y * g and y / s can differ in the
+     last fp32 bit, and so, at an e4m3 tie, in the code).
   5. stored scale: s * fp32(1/sqrt(d)) (fp32 product) with rotation, else s, so
      that code * scale approximates x R (or x).
 """
@@ -102,6 +105,8 @@ def quantize_blocks_ref(x_bits: np.ndarray, sign_bits: Optional[np.ndarray] = No
         y = x[:, :, r0:r1, :]
         amax = np.abs(y).max(axis=(2, 3))
         s = np.where(amax > 0, amax / E4M3_MAX, np.float32(1.0)).astype(np.float32)
-        codes[:, :, r0:r1, :] = e4m3_encode(y / s[:, :, None, None])
+        with np.errstate(divide="ignore"):
+            g = np.where(amax > 0, E4M3_MAX / amax, np.float32(1.0)).astype(np.float32)
+        codes[:, :, r0:r1, :] = e4m3_encode(y * g[:, :, None, None])
         scales[:, :, j] = (s * rnorm).astype(np.float32) if sign_bits is not None else s
     return codes, scales

@@ -150,6 +150,17 @@ def test_varlen_validation(L):
     assert fwd(4, 2, ws, L.make_mask(L.ATTN_DOCUMENT, doc_id=P)) == L.ATTN_ERR_INVALID_ARG
 
 
+def test_fp8_quantize_validation(L):
+    lib = L.load()
+    q = lambda x=P, c=P, s=P, B=1, H=2, N=300, d=128: lib.attn_fp8_quantize(x, c, s, B, H, N, d, None, None)
+    assert q(x=None) == L.ATTN_ERR_INVALID_ARG
+    assert q(c=P + 8) == L.ATTN_ERR_INVALID_ARG
+    assert q(s=P + 2) == L.ATTN_ERR_INVALID_ARG
+    assert q(d=96) == L.ATTN_ERR_UNSUPPORTED
+    assert q(B=0) == L.ATTN_ERR_INVALID_ARG
+    assert q(N=0) == L.ATTN_ERR_INVALID_ARG
+
+
 def test_fwd_rejects_before_launch(L):
     """attn_fwd with bad arguments returns the validation error without touching the GPU."""
     lib = L.load()

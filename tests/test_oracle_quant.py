@@ -66,10 +66,9 @@ def _bf16(x):
 
 
 def test_quantize_unrotated_agrees_with_the_generators_quantiser():
-    """The input generator quantises with an fp64 division; this side divides in fp32.
-    With bf16 inputs and 448 = 7 * 2^6 the quotient often lies within an fp32 rounding
-    of an exact e4m3 tie: only there may the two differ, by one code, the fp32 side
-    taking the even one."""
+    """The input generator quantises with an fp64 division; this side multiplies by the
+    fp32 inverse scale.  With bf16 inputs and 448 = 7 * 2^6 the exact quotient often
+    lies at or next to an e4m3 tie: only there may the two differ, by one code."""
     rng = np.random.default_rng(3)
     x = rng.standard_normal((2, 3, 300, 64)).astype(np.float32)
     bits = _bf16(x)
@@ -79,12 +78,11 @@ def test_quantize_unrotated_agrees_with_the_generators_quantiser():
     diff = decode_e4m3(codes) != decode_e4m3(gcodes)
     assert diff.mean() < 1e-3
     s = np.repeat(scales, 128, axis=2)[:, :, :300, None]
-    v32 = (decode_bf16(bits).astype(np.float32) / s)[diff].astype(np.float64)
     v64 = (decode_bf16(bits) / s.astype(np.float64))[diff]
     a, b = decode_e4m3(codes)[diff], decode_e4m3(gcodes)[diff]
-    np.testing.assert_array_equal(v32, (a + b) / 2)  # an exact tie in fp32
-    assert np.all(np.abs(v64 - v32) <= np.abs(v32) * 2.0 ** -23)
-    assert np.all(codes[diff] % 2 == 0) and np.all(np.abs(codes.astype(int)[diff] - gcodes.astype(int)[diff]) == 1)
+    tie = (a + b) / 2
+    assert np.all(np.abs(v64 - tie) <= np.abs(tie) * 2.0 ** -21)  # within fp32 rounding of a tie
+    assert np.all(np.abs(codes.astype(int)[diff] - gcodes.astype(int)[diff]) == 1)
 
 
 @pytest.mark.parametrize("rotate", [False, True])
@@ -113,8 +111,8 @@ def test_quantize_block_properties(rotate):
             i = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
             assert c[i] & 0x7F == 0x7E
             # every code is within half an e4m3 step (relative 2^-4, or 2^-10 absolute
-            # in the subnormal range) of y / s
-            v = blk / s
+            # in the subnormal range) of y * 448 / amax
+            v = blk * 448.0 / np.abs(blk).max()
             err = np.abs(decode_e4m3(c) - v)
             assert np.all(err <= np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10) * 1.0001)
 
