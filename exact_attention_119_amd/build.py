@@ -33,6 +33,7 @@ SOURCES = [
     "fwd_fp8qk8_d128.hip",
     "fwd_fp8qk8_d64.hip",
     "quant.hip",
+    "bwd.hip",
 ]
 
 # -packed-fp32-ops: hipcc must not emit v_pk_{add,mul,fma}_f32 (the host pass warns

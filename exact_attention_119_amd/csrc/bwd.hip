@@ -1,0 +1,461 @@
+// Backward pass of the fused attention for bf16 inputs (gfx950): dQ, dK, dV from Q, K,
+// V, O, dO and the forward pass's LSE, with the same masks and score modifiers.
+//
+// The page "FlashAttention 4: ... για LLMs" (el.linux-konsole.com), sections "Κύρια
+// Συμπεράσματα" and "Συμβατότητα και τρέχουσα κατάσταση", names the backward pass as
+// the piece FA4 still lacks.  It is the chain rule through the forward definition:
+//   P = exp(s - LSE) (recomputed from Q, K and the saved LSE), dV = P^T dO,
+//   dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D), dR = dS * ds/dr,
+//   dQ = dR K, dK = dR^T Q   (ds/dr = scale, or scale * (1 - tanh^2) with softcap).
+// Deterministic: no atomics.  Three launches:
+//   delta_kernel : D for every query row (one thread per row).
+//   dq_kernel    : one workgroup per (b*H + h, 128 query rows), a wave per 32 rows; it
+//                  walks the row block's non-empty key blocks in 64-key steps:
+//                  S^T = K Q^T and dP^T = V dO^T (Q and dO of the wave resident as
+//                  B operands), dR^T elementwise, dQ^T += K^T dR^T.
+//   dkdv_kernel  : one workgroup per (b*H_kv + g, 128 keys), a wave per 32 keys; it
+//                  walks the query heads sharing the key/value head and their
+//                  non-empty query blocks in 32-row steps: S = Q K^T and dP = dO V^T
+//                  (K and V of the wave resident), dV^T += dO^T P, dK^T += Q^T dR.
+// MFMA v_mfma_f32_32x32x16_bf16 throughout, with the forward pass's operand layouts:
+// row fragments of a row-major LDS tile as A operands, transposed fragments
+// (ds_read_b64_tr_b16) as A operands of the T^T products, and accumulators packed to
+// bf16 as B operands in the contraction order those transposed reads produce.
+#include <type_traits>
+
+#include "../../include/attn119.h"
+#include "common.hpp"
+
+namespace attn119 {
+namespace bwd {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const bf16* dout;
+  const float* lse;  // [B][H][N] natural log
+  float* delta;      // [B][H][N] rowsum(dO * O)
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  int B, H, Hkv, N, nqb;
+  float scale;
+  float cap;        // softcap (flags & kSoftcap)
+  float sc_cap;     // scale / cap
+  float alibi_exp;  // default slopes 2^(alibi_exp (h+1)), alibi_exp = -8/H
+  const float* alibi_slopes;
+  uint32_t flags;   // every mask and modifier flag
+  int window;
+  const unsigned char* map;  // block map (positional masks)
+  MapLayout lay;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int PADB = 16;  // LDS row padding (bytes)
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ bf16x2 to_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_convertvector(v, bf16x2);
+}
+// registers 8g .. 8g+7 of an accumulator as a bf16 B operand
+__device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int g) {
+  const bf16x2 a = to_bf16x2(acc[8 * g + 0], acc[8 * g + 1]), b = to_bf16x2(acc[8 * g + 2], acc[8 * g + 3]);
+  const bf16x2 c = to_bf16x2(acc[8 * g + 4], acc[8 * g + 5]), d = to_bf16x2(acc[8 * g + 6], acc[8 * g + 7]);
+  const u32x4 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                   __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// row offset (minus 4*hh) of accumulator register r: 8*(r>>2) + (r&3)
+__device__ __forceinline__ constexpr int acc_row(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// A fragment of a row-major tile (stride STR): row r0 + l32, 8 values at column 16c + 8hh
+template <int STR>
+__device__ __forceinline__ bf16x8 row_frag(const lds_u8* t, int r0, int l32, int hh, int c) {
+  return *(const lds_bf16x8*)(t + (r0 + l32) * STR + 32 * c + 16 * hh);
+}
+// A fragment of the transpose of a row-major tile: columns 32db .. 32db+31 as rows, the
+// 16 tile rows 16ks .. 16ks+15 as k, in the order 4hh+e, 8+4hh+e (e = 0..3) that the
+// accumulator registers 8g .. 8g+7 carry; off = this lane's offset for block db.
+template <int STR>
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* t, int ks, int off) {
+  const lds_u8* base = t + ks * 16 * STR + off;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * STR));
+  const short __attribute__((ext_vector_type(8))) w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+template <int STR>
+__device__ __forceinline__ int tr_off(int lane, int db) {
+  const int e = (lane & 15) >> 2, aa = lane & 3, dh = (lane >> 4) & 1, hh = lane >> 5;
+  const int chunk = 4 * db + 2 * dh + (aa >> 1);
+  return (4 * hh + e) * STR + chunk * 16 + (aa & 1) * 8;
+}
+
+// score, and its derivative in the raw dot product, of one (q, k) element
+__device__ __forceinline__ void score(const BwdArgs& a, float raw, int q, int k, float slope, float& s, float& dsdr) {
+  if (a.flags & kSoftcap) {
+    const float y = raw * a.sc_cap;
+    const float t = 1.f - 2.f * rcp_(exp2_(2.f * kLog2e * y) + 1.f);
+    s = a.cap * t;
+    dsdr = a.scale * (1.f - t * t);
+  } else {
+    s = raw * a.scale;
+    dsdr = a.scale;
+  }
+  if (a.flags & kAlibi) s -= slope * (float)(q > k ? q - k : k - q);
+}
+
+__device__ __forceinline__ float head_slope(const BwdArgs& a, int h) {
+  return a.alibi_slopes ? a.alibi_slopes[h] : exp2_(a.alibi_exp * (float)(h + 1));
+}
+
+// header of the block map matches the call, and (document masks) no batch row is
+// marked invalid; uniform over the workgroup
+__device__ bool map_invalid(const BwdArgs& a, int b) {
+  const MapHeader* hd = (const MapHeader*)a.map;
+  bool bad = hd->magic != kMapMagic || hd->B != a.B || hd->N != a.N || hd->flags != (a.flags & kPositional) ||
+             hd->window != ((a.flags & kWindow) ? a.window : 0);
+  int st = 0;
+  if (a.flags & kDocument) {
+    const int* s = (const int*)(a.map + a.lay.status) + (size_t)b * a.nqb;
+    for (int i = threadIdx.x; i < a.nqb; i += 256) st |= s[i];
+  }
+  return __syncthreads_or(st) != 0 || bad;
+}
+
+// ---- D = rowsum(dO * O) ------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (size_t)a.B * a.H * a.N) return;
+  const uint4* o = (const uint4*)(a.o + row * D);
+  const uint4* g = (const uint4*)(a.dout + row * D);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const uint4 x = o[c], y = g[c];
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc = __builtin_fmaf(__uint_as_float(xs[t] << 16), __uint_as_float(ys[t] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(xs[t] & 0xFFFF0000u), __uint_as_float(ys[t] & 0xFFFF0000u), acc);
+    }
+  }
+  a.delta[row] = acc;
+}
+
+// ---- dQ ----------------------------------------------------------------------------------
+template <int D, bool MASKED>
+__global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
+  constexpr int ROWB = 2 * D, STR = ROWB + PADB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
+  constexpr int BN = 64;
+  __shared__ __attribute__((aligned(16))) unsigned char k_sh[BN * STR];
+  __shared__ __attribute__((aligned(16))) unsigned char v_sh[BN * STR];
+  const lds_u8* kt = (const lds_u8*)k_sh;
+  const lds_u8* vt = (const lds_u8*)v_sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int N = a.N, nqb = a.nqb;
+  const int bh = blockIdx.x / nqb, qb = blockIdx.x - bh * nqb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int bkv = b * a.Hkv + h / (a.H / a.Hkv);
+  const int qrow = qb * 128 + wave * 32 + l32;
+  const bool qvalid = qrow < N;
+  const size_t qoff = ((size_t)bh * N + (qvalid ? qrow : 0)) * D;
+
+  bf16x8 qf[NQC], gf[NQC];
+#pragma unroll
+  for (int c = 0; c < NQC; ++c) {
+    qf[c] = qvalid ? *(const bf16x8*)(a.q + qoff + 16 * c + 8 * hh) : bf16x8{};
+    gf[c] = qvalid ? *(const bf16x8*)(a.dout + qoff + 16 * c + 8 * hh) : bf16x8{};
+  }
+  const float lse2 = qvalid ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float dl = qvalid ? a.delta[(size_t)bh * N + qrow] : 0.f;
+  const float slope = (a.flags & kAlibi) ? head_slope(a, h) : 0.f;
+
+  int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
+  int nblk = nqb, npart = 0;
+  const int* flist = nullptr;
+  const int* plist = nullptr;
+  bool invalid = false;
+  if constexpr (MASKED) {
+    invalid = map_invalid(a, b);
+    const int* cnt = (const int*)(a.map + a.lay.counts) + ((size_t)b * nqb + qb) * 2;
+    const int nfull = min(max(cnt[0], 0), nqb);
+    npart = min(max(cnt[1], 0), nqb - nfull);
+    nblk = invalid ? 0 : nfull + npart;
+    flist = (const int*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
+    plist = flist + nqb;
+    if (qvalid) {
+      lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
+      hi_q = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
+    }
+  }
+  int troff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) troff[db] = tr_off<STR>(lane, db);
+
+  f32x16 dacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dacc[db] = f32x16{};
+
+  for (int i = 0; i < nblk; ++i) {
+    int kb = i;
+    if constexpr (MASKED) kb = min(max(i < npart ? plist[i] : flist[i - npart], 0), nqb - 1);
+    for (int hs = 0; hs < 2; ++hs) {
+      const int k0 = kb * 128 + hs * BN;
+      if (k0 >= N) break;
+      __syncthreads();  // the previous step's reads are done
+      for (int t = tid; t < BN * CPR; t += 256) {
+        const int r = t / CPR, c = t - r * CPR;
+        const int key = k0 + r;
+        uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = kx;
+        if (key < N) {
+          const size_t off = ((size_t)bkv * N + key) * D + c * 8;
+          kx = *(const uint4*)(a.k + off);
+          vx = *(const uint4*)(a.v + off);
+        }
+        *(uint4*)(k_sh + r * STR + c * 16) = kx;
+        *(uint4*)(v_sh + r * STR + c * 16) = vx;
+      }
+      __syncthreads();
+      f32x16 st[2], dp[2];
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        st[bk] = f32x16{};
+        dp[bk] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NQC; ++c) {
+          st[bk] = mfma(row_frag<STR>(kt, 32 * bk, l32, hh, c), qf[c], st[bk]);
+          dp[bk] = mfma(row_frag<STR>(vt, 32 * bk, l32, hh, c), gf[c], dp[bk]);
+        }
+      }
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * bk + 4 * hh + acc_row(r);
+          float s, dsdr;
+          score(a, st[bk][r], qrow, key, slope, s, dsdr);
+          const bool vis = key >= lo_q && key <= hi_q;
+          const float p = vis ? exp2_(s * kLog2e - lse2) : 0.f;
+          st[bk][r] = p * (dp[bk][r] - dl) * dsdr;
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 bop = pack8(st[ks >> 1], ks & 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dacc[db] = mfma(tr_frag<STR>(kt, ks, troff[db]), bop, dacc[db]);
+      }
+    }
+  }
+  if (!qvalid) return;
+  const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
+  bf16* dst = a.dq + qoff;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16& x = dacc[db];
+      const bf16x2 v01 = invalid ? to_bf16x2(nanv, nanv) : to_bf16x2(x[4 * i], x[4 * i + 1]);
+      const bf16x2 v23 = invalid ? to_bf16x2(nanv, nanv) : to_bf16x2(x[4 * i + 2], x[4 * i + 3]);
+      const u32x2 w = {__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
+      *(u32x2*)(dst + db * 32 + 8 * i + 4 * hh) = w;
+    }
+}
+
+// ---- dK, dV ------------------------------------------------------------------------------
+template <int D, bool MASKED>
+__global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
+  constexpr int ROWB = 2 * D, STR = ROWB + PADB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
+  constexpr int BM = 32;  // query rows per step
+  __shared__ __attribute__((aligned(16))) unsigned char q_sh[BM * STR];
+  __shared__ __attribute__((aligned(16))) unsigned char g_sh[BM * STR];
+  __shared__ float lse_s[BM], dl_s[BM];
+  __shared__ int lo_s[BM], hi_s[BM];
+  const lds_u8* qt = (const lds_u8*)q_sh;
+  const lds_u8* gt = (const lds_u8*)g_sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int N = a.N, nqb = a.nqb;
+  const int bkv = blockIdx.x / nqb, kb = blockIdx.x - bkv * nqb;
+  const int b = bkv / a.Hkv, kvh = bkv - b * a.Hkv;
+  const int grp = a.H / a.Hkv;
+  const int key = kb * 128 + wave * 32 + l32;
+  const bool kvalid = key < N;
+  const size_t koff = ((size_t)bkv * N + (kvalid ? key : 0)) * D;
+
+  bf16x8 kf[NQC], vf[NQC];
+#pragma unroll
+  for (int c = 0; c < NQC; ++c) {
+    kf[c] = kvalid ? *(const bf16x8*)(a.k + koff + 16 * c + 8 * hh) : bf16x8{};
+    vf[c] = kvalid ? *(const bf16x8*)(a.v + koff + 16 * c + 8 * hh) : bf16x8{};
+  }
+  bool invalid = false;
+  if constexpr (MASKED) invalid = map_invalid(a, b);
+  int troff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) troff[db] = tr_off<STR>(lane, db);
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+  const unsigned char* cls = MASKED ? a.map + a.lay.cls + (size_t)b * nqb * nqb + kb : nullptr;
+
+  for (int hq = 0; hq < grp && !invalid; ++hq) {
+    const int h = kvh * grp + hq;
+    const int bh = b * a.H + h;
+    const float slope = (a.flags & kAlibi) ? head_slope(a, h) : 0.f;
+    for (int qb = 0; qb < nqb; ++qb) {
+      if constexpr (MASKED) {
+        if (cls[(size_t)qb * nqb] == 0) continue;  // EMPTY block
+      }
+      for (int sub = 0; sub < 128 / BM; ++sub) {
+        const int q0 = qb * 128 + sub * BM;
+        if (q0 >= N) break;
+        __syncthreads();  // the previous step's reads are done
+        for (int t = tid; t < BM * CPR; t += 256) {
+          const int r = t / CPR, c = t - r * CPR;
+          const int q = q0 + r;
+          uint4 qx = make_uint4(0u, 0u, 0u, 0u), gx = qx;
+          if (q < N) {
+            const size_t off = ((size_t)bh * N + q) * D + c * 8;
+            qx = *(const uint4*)(a.q + off);
+            gx = *(const uint4*)(a.dout + off);
+          }
+          *(uint4*)(q_sh + r * STR + c * 16) = qx;
+          *(uint4*)(g_sh + r * STR + c * 16) = gx;
+        }
+        if (tid < BM) {
+          const int q = q0 + tid;
+          const bool ok = q < N;
+          lse_s[tid] = ok ? a.lse[(size_t)bh * N + q] * kLog2e : 0.f;
+          dl_s[tid] = ok ? a.delta[(size_t)bh * N + q] : 0.f;
+          int lo = 0, hi = ok ? N - 1 : -1;
+          if constexpr (MASKED) {
+            if (ok) {
+              lo = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + q];
+              hi = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + q];
+            }
+          }
+          lo_s[tid] = lo;
+          hi_s[tid] = hi;
+        }
+        __syncthreads();
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NQC; ++c) {
+          s = mfma(row_frag<STR>(qt, 0, l32, hh, c), kf[c], s);
+          dp = mfma(row_frag<STR>(gt, 0, l32, hh, c), vf[c], dp);
+        }
+        f32x16 pm, dr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 4 * hh + acc_row(r);
+          const int q = q0 + qi;
+          float sv, dsdr;
+          score(a, s[r], q, key, slope, sv, dsdr);
+          const bool vis = key >= lo_s[qi] && key <= hi_s[qi];
+          const float p = vis ? exp2_(sv * kLog2e - lse_s[qi]) : 0.f;
+          pm[r] = p;
+          dr[r] = p * (dp[r] - dl_s[qi]) * dsdr;
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const bf16x8 pb = pack8(pm, g), rb = pack8(dr, g);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dvacc[db] = mfma(tr_frag<STR>(gt, g, troff[db]), pb, dvacc[db]);
+            dkacc[db] = mfma(tr_frag<STR>(qt, g, troff[db]), rb, dkacc[db]);
+          }
+        }
+      }
+    }
+  }
+  if (!kvalid) return;
+  const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
+  bf16* dk = a.dk + koff;
+  bf16* dv = a.dv + koff;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16& x = dkacc[db];
+      const f32x16& y = dvacc[db];
+      const bf16x2 k01 = invalid ? to_bf16x2(nanv, nanv) : to_bf16x2(x[4 * i], x[4 * i + 1]);
+      const bf16x2 k23 = invalid ? to_bf16x2(nanv, nanv) : to_bf16x2(x[4 * i + 2], x[4 * i + 3]);
+      const bf16x2 v01 = invalid ? to_bf16x2(nanv, nanv) : to_bf16x2(y[4 * i], y[4 * i + 1]);
+      const bf16x2 v23 = invalid ? to_bf16x2(nanv, nanv) : to_bf16x2(y[4 * i + 2], y[4 * i + 3]);
+      *(u32x2*)(dk + db * 32 + 8 * i + 4 * hh) = u32x2{__builtin_bit_cast(uint32_t, k01), __builtin_bit_cast(uint32_t, k23)};
+      *(u32x2*)(dv + db * 32 + 8 * i + 4 * hh) = u32x2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
+    }
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, bool masked, hipStream_t st) {
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+  const dim3 gq((unsigned)(a.B * a.H * a.nqb)), gk((unsigned)(a.B * a.Hkv * a.nqb)), blk(256);
+  if (masked) {
+    hipLaunchKernelGGL((dq_kernel<D, true>), gq, blk, 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, true>), gk, blk, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((dq_kernel<D, false>), gq, blk, 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, false>), gk, blk, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bwd
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
+                      uint32_t flags, int window, float softcap, const float* slopes, const void* map,
+                      hipStream_t stream) {
+  bwd::BwdArgs a;
+  a.q = (const bf16*)q;
+  a.k = (const bf16*)k;
+  a.v = (const bf16*)v;
+  a.o = (const bf16*)o;
+  a.dout = (const bf16*)dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = (bf16*)dq;
+  a.dk = (bf16*)dk;
+  a.dv = (bf16*)dv;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.nqb = (N + 127) / 128;
+  a.scale = scale;
+  a.cap = softcap;
+  a.sc_cap = (flags & kSoftcap) ? (float)((double)scale / (double)softcap) : 0.f;
+  a.alibi_exp = (float)(-8.0 / (double)H);
+  a.alibi_slopes = slopes;
+  a.flags = flags;
+  a.window = window;
+  a.map = (const unsigned char*)map;
+  a.lay = map_layout(B, N);
+  const bool masked = (flags & kPositional) != 0;
+  if (masked && !map) return hipErrorInvalidValue;
+  return d == 128 ? bwd::launch_d<128>(a, masked, stream) : bwd::launch_d<64>(a, masked, stream);
+}
+
+}  // namespace attn119

@@ -42,7 +42,7 @@ ATTN_QK_E4M3 = 1
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
-           "attn_fwd_varlen", "attn_fp8_quantize")
+           "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa")
 
 
 class AttnError(RuntimeError):
@@ -109,6 +109,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_varlen.restype = i32
     lib.attn_fp8_quantize.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.attn_fp8_quantize.restype = i32
+    lib.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                 ctypes.POINTER(attn_mask), vp, sz, vp]
+    lib.attn_bwd_gqa.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, ctypes.POINTER(attn_mask),
+                             vp, sz, vp]
+    lib.attn_bwd.restype = i32
     lib.attn_fwd_kernel_name.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(attn_fp8)]
     lib.attn_fwd_kernel_name.restype = ctypes.c_char_p
     _LIB = lib
@@ -264,6 +270,19 @@ def attn_fp8_quantize(x, codes, scales, rotate_signs=None, stream=None) -> None:
         sg = (ctypes.c_uint32 * len(words))(*words)
     _check(load().attn_fp8_quantize(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, sg, _stream(stream)),
            "attn_fp8_quantize")
+
+
+def attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, *, scale: float, mask: Optional[attn_mask] = None,
+                 blockmap=None, stream=None) -> None:
+    """Backward pass (bf16).  q, o, dout, dq: [B][H][N][d]; k, v, dk, dv: [B][H_kv][N][d];
+    lse: the forward call's [B][H][N] fp32; delta: [B][H][N] fp32 scratch."""
+    B, H, N, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[1])
+    mbytes = 0 if blockmap is None else blockmap.numel() * blockmap.element_size()
+    _check(load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(delta), B, H, H_kv, N, d, float(scale),
+                               ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes, _stream(stream)),
+           "attn_bwd_gqa")
 
 
 def read_blockmap(blockmap, B: int, N: int) -> dict:

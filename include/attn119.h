@@ -277,6 +277,31 @@ attn_status attn_fp8_quantize(const void* x, void* codes, float* scales, int32_t
                               int32_t d, const uint32_t* rotate_signs, void* stream);
 
 /*
+ * Backward pass (bf16): the gradients of L = sum(O * dO) for the same mask, modifiers
+ * and grouped heads as the forward call -- the piece the page "FlashAttention 4: ...
+ * για LLMs" (el.linux-konsole.com) lists as missing from FA4 in its sections "Κύρια
+ * Συμπεράσματα" and "Συμβατότητα και τρέχουσα κατάσταση".  With P = exp(s - LSE):
+ *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dR = dS * ds/dr (ds/dr = scale, or scale * (1 - tanh^2) under ATTN_SOFTCAP),
+ *   dQ = dR K,  dK = dR^T Q;  dK and dV summed over the query heads sharing them.
+ *   q, o, dout, dq : bf16 [B][H][N][d];  k, v, dk, dv : bf16 [B][H_kv][N][d];
+ *   lse  : fp32 [B][H][N], the forward call's output for the same q, k, v;
+ *   delta: fp32 [B][H][N] caller-owned scratch, overwritten with D;
+ *   mask, blockmap: as for the forward call (positional masks need the block map).
+ * Deterministic (no atomics): equal inputs give equal bits.  Errors as attn_check_args_gqa,
+ * plus ATTN_ERR_INVALID_ARG for a null or misaligned dout, dq, dk, dv (16 B) or delta (4 B).
+ * attn_bwd is the case H_kv = H.
+ */
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int32_t B, int32_t H,
+                         int32_t H_kv, int32_t N, int32_t d, float scale, const attn_mask* mask,
+                         const void* blockmap, size_t blockmap_bytes, void* stream);
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, float* delta, int32_t B, int32_t H, int32_t N, int32_t d,
+                     float scale, const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                     void* stream);
+
+/*
  * Name of the compiled kernel variant attn_fwd selects for these arguments, e.g.
  * "bf16 d128 masked softcap" (host logic only, no HIP call, usable without a GPU);
  * NULL when the combination is unsupported.  The string is static.  A "masked"

@@ -1,0 +1,95 @@
+"""GPU parity for the backward pass (attn_bwd_gqa): dQ, dK, dV of the HIP path, fed the
+HIP forward pass's O and LSE, against the fp64 oracle's gradients of the definition."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as W
+from workload import device as WD
+from exact_attention_119_amd import lib as L
+
+pytestmark = pytest.mark.gpu
+
+C, WI, DOC, AL, SC = W.ATTN_CAUSAL, W.ATTN_WINDOW, W.ATTN_DOCUMENT, W.ATTN_ALIBI, W.ATTN_SOFTCAP
+
+VARIANTS = {
+    "plain": dict(flags=0),
+    "causal": dict(flags=C),
+    "window": dict(flags=C | WI, window=37),
+    "bidir_window": dict(flags=WI, window=50),
+    "doc_causal": dict(flags=C | DOC),
+    "alibi_causal": dict(flags=C | AL),
+    "softcap": dict(flags=SC, softcap=2.0),
+    "cfg3like": dict(flags=C | WI | SC, window=100, softcap=3.0),
+    "everything": dict(flags=C | WI | DOC | AL | SC, window=70, softcap=2.5),
+}
+# gradients: bf16 operands (P, dS, inputs) and bf16 outputs; error relative to the
+# largest reference magnitude of each tensor
+TOL = 2e-2
+
+
+def _announce(*a):
+    print("CASE", *a, flush=True)
+
+
+def _bwd(p, dout_bits):
+    dp = WD.to_device(p)
+    WD.step(dp)
+    dout = torch.from_numpy(dout_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    dq = torch.full_like(dp.q, float("nan"))
+    dk = torch.full_like(dp.k, float("nan"))
+    dv = torch.full_like(dp.v, float("nan"))
+    delta = torch.empty_like(dp.lse)
+    L.attn_bwd_gqa(dp.q, dp.k, dp.v, dp.o, dp.lse, dout, dq, dk, dv, delta, scale=p.scale, mask=dp.mask,
+                   blockmap=dp.blockmap)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return f(dq), f(dk), f(dv), delta.cpu().numpy().astype(np.float64)
+
+
+def _check(got, ref, what):
+    # a gradient can vanish analytically (dQ, dK of a one-key row are exactly zero) while
+    # its rounding noise follows the other gradients: floor the scale at 5% of the largest
+    gmax = max(np.abs(r).max() for r in ref[:3])
+    for g, r, name in zip(got, ref, ("dQ", "dK", "dV", "D")):
+        assert np.isfinite(g).all(), f"{what} {name}: non-finite"
+        scale = max(np.abs(r).max(), 0.05 * gmax, 1e-30)
+        e = np.abs(g - r).max() / scale
+        print(f"{what} {name}: max|err|/max|ref| = {e:.2e}", flush=True)
+        assert e <= TOL, f"{what} {name}: {e:.3e} > {TOL}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 129, 300])
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_small_shapes(variant, N, d):
+    heads = [(2, 2), (4, 2), (3, 1)][(N + d) % 3]
+    p = W.make_problem(2, heads[0], N, d, seed=(N, d, sorted(VARIANTS).index(variant)), H_kv=heads[1],
+                       doc_len_range=(1, max(1, N // 2)), **VARIANTS[variant])
+    dO = W.make_dout(p, seed=(N, d))
+    _announce("bwd", variant, N, d, heads)
+    got = _bwd(p, dO)
+    ref = oracle.attention_bwd_problem(p, dO)
+    _check(got, ref, f"bwd {variant} N={N} d={d} H={heads}")
+
+
+def test_deterministic():
+    p = W.make_problem(1, 4, 700, 128, seed=3, H_kv=2, flags=C)
+    dO = W.make_dout(p, seed=3)
+    _announce("bwd determinism")
+    a, b = _bwd(p, dO), _bwd(p, dO)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("variant", ["causal", "cfg3like", "doc_causal"])
+def test_larger(variant):
+    p = W.make_problem(1, 4, 1500, 128, seed=(15, sorted(VARIANTS).index(variant)), H_kv=2,
+                       doc_len_range=(200, 700), **VARIANTS[variant])
+    dO = W.make_dout(p, seed=15)
+    _announce("bwd larger", variant)
+    got = _bwd(p, dO)
+    ref = oracle.attention_bwd_problem(p, dO)
+    _check(got, ref, f"bwd {variant} N=1500")

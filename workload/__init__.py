@@ -21,5 +21,6 @@ from .gen import (  # noqa: F401
     e4m3_codes_from_f64,
     make_problem,
     make_varlen_problem,
+    make_dout,
     quantize_e4m3_blocks,
 )

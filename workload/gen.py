@@ -292,3 +292,11 @@ def make_varlen_problem(lengths: Sequence[int], H: int, d: int, *, dtype: str = 
                alibi_slopes, H_kv)
     p.cu_seqlens = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     return p
+
+
+def make_dout(p: Problem, seed: Union[int, Tuple[int, ...]] = 0) -> np.ndarray:
+    """bf16 output gradients [B][H][N][d] for a problem's backward pass, drawn N(0, 1) with
+    ``default_rng([119, 3000, *seed])``."""
+    seed_t = (seed,) if isinstance(seed, int) else tuple(seed)
+    rng = np.random.default_rng([119, 3000, *seed_t])
+    return bf16_bits_from_f32(rng.standard_normal((p.B, p.H, p.N, p.d), dtype=np.float32))
