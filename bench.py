@@ -131,6 +131,70 @@ def traffic_record(name: str):
     return rec.get("bytes_per_launch")
 
 
+def bench_bwd(args):
+    """One step = the three backward launches for the configuration's workload."""
+    import numpy as np
+    import torch
+    import workload as W
+    from workload import device as WD
+    from exact_attention_119_amd import lib as L
+    p = W.config_problem(args.config)
+    if p.dtype != "bf16":
+        raise SystemExit("the backward pass takes bf16 inputs")
+    dp = WD.to_device(p)
+    WD.step(dp)
+    dout = torch.from_numpy(W.make_dout(p, seed=2).view(np.int16)).cuda().view(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(dp.q), torch.empty_like(dp.k), torch.empty_like(dp.v)
+    delta = torch.empty_like(dp.lse)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.attn_bwd_gqa(dp.q, dp.k, dp.v, dp.o, dp.lse, dout, dq, dk, dv, delta, scale=p.scale, mask=dp.mask,
+                       blockmap=dp.blockmap)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg = sum(ms) / len(ms)
+    pairs = visible_pairs(p)
+    flop = 10.0 * p.d * p.H * pairs  # five products of 2*d flop per visible pair
+    step_ms = wall * 1e3 / args.steps
+    name = workload_name(p)
+    log(f"bench: backward step {step_ms:.4f} ms (wall), three launches avg {avg:.4f} ms (events)")
+    out = {"metric": "attention bwd TFLOP/s (five products of 2d flop per visible pair)",
+           "value": round(flop / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+           "config": {"workload": name + " backward", "visible_pairs": pairs, "flop_per_step": flop,
+                      "step": "row sums + dQ + dK/dV, given O and LSE", "parallelism": "single GPU"},
+           "roofline": {"bound": "mfma", "achieved": round(flop / (avg * 1e-3) / 1e12, 3), "peak": PEAK_TFLOPS["bf16"],
+                        "unit": "TFLOP/s", "frac": round(flop / (avg * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                        "traffic": None, "kernel": "delta + dq + dkdv (three launches)",
+                        "kernel_avg_ms": round(avg, 5)}}
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 10.0) and n < p.B * p.H:
+            oracle.attention_bwd_problem(p, W.make_dout(p, seed=2), heads=[divmod(n, p.H)])
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(flop * n / (p.B * p.H) / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n} of {p.B * p.H} (b,h) heads, fp64 numpy, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 QUANT_SIGNS = [0x9E3779B9, 0x7F4A7C15, 0x2545F491, 0x4F6CDD1D]
 
 
@@ -217,6 +281,9 @@ def main(argv=None):
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    ap.add_argument("--bwd", action="store_true",
+                    help="instead: the backward pass (row sums, dQ, dK/dV) on the configuration's workload "
+                         "(bf16), given the forward pass's O and LSE")
     ap.add_argument("--quant", action="store_true",
                     help="instead: the device fp8 quantiser (Q and K rotated, V plain) on the fp8 workload's "
                          "shape B1 H16 N16384 d128 from bf16")
@@ -249,6 +316,8 @@ def main(argv=None):
 
     if args.quant:
         return bench_quant(args)
+    if args.bwd:
+        return bench_bwd(args)
 
     if args.varlen:
         import numpy as np

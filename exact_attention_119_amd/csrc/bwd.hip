@@ -15,7 +15,7 @@
 //                  B operands), dR^T elementwise, dQ^T += K^T dR^T.
 //   dkdv_kernel  : one workgroup per (b*H_kv + g, 128 keys), a wave per 32 keys; it
 //                  walks the query heads sharing the key/value head and their
-//                  non-empty query blocks in 32-row steps: S = Q K^T and dP = dO V^T
+//                  non-empty query blocks in 64-row steps: S = Q K^T and dP = dO V^T
 //                  (K and V of the wave resident), dV^T += dO^T P, dK^T += Q^T dR.
 // MFMA v_mfma_f32_32x32x16_bf16 throughout, with the forward pass's operand layouts:
 // row fragments of a row-major LDS tile as A operands, transposed fragments
@@ -33,6 +33,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef const __attribute__((address_space(4))) int cint;  // read-only, uniform: scalar loads
+typedef const __attribute__((address_space(4))) unsigned char cu8;
 
 struct BwdArgs {
   const bf16* q;
@@ -104,9 +106,11 @@ __device__ __forceinline__ int tr_off(int lane, int db) {
   return (4 * hh + e) * STR + chunk * 16 + (aa & 1) * 8;
 }
 
-// score, and its derivative in the raw dot product, of one (q, k) element
+// score, and its derivative in the raw dot product, of one (q, k) element (the modifiers
+// are template parameters: no branch per element)
+template <bool SOFTCAP, bool ALIBI>
 __device__ __forceinline__ void score(const BwdArgs& a, float raw, int q, int k, float slope, float& s, float& dsdr) {
-  if (a.flags & kSoftcap) {
+  if constexpr (SOFTCAP) {
     const float y = raw * a.sc_cap;
     const float t = 1.f - 2.f * rcp_(exp2_(2.f * kLog2e * y) + 1.f);
     s = a.cap * t;
@@ -115,7 +119,11 @@ __device__ __forceinline__ void score(const BwdArgs& a, float raw, int q, int k,
     s = raw * a.scale;
     dsdr = a.scale;
   }
-  if (a.flags & kAlibi) s -= slope * (float)(q > k ? q - k : k - q);
+  if constexpr (ALIBI) s -= slope * (float)(q > k ? q - k : k - q);
+}
+// p = exp(s - LSE) for a visible element, 0 for a hidden one (exp2 of -inf: no branch)
+__device__ __forceinline__ float prob(bool vis, float s, float lse2) {
+  return exp2_(vis ? s * kLog2e - lse2 : -__builtin_inff());
 }
 
 __device__ __forceinline__ float head_slope(const BwdArgs& a, int h) {
@@ -158,7 +166,7 @@ __global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
 }
 
 // ---- dQ ----------------------------------------------------------------------------------
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
 __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
   constexpr int ROWB = 2 * D, STR = ROWB + PADB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
   constexpr int BN = 64;
@@ -184,20 +192,20 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
   }
   const float lse2 = qvalid ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   const float dl = qvalid ? a.delta[(size_t)bh * N + qrow] : 0.f;
-  const float slope = (a.flags & kAlibi) ? head_slope(a, h) : 0.f;
+  const float slope = ALIBI ? head_slope(a, h) : 0.f;
 
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
   int nblk = nqb, npart = 0;
-  const int* flist = nullptr;
-  const int* plist = nullptr;
+  cint* flist = nullptr;
+  cint* plist = nullptr;
   bool invalid = false;
   if constexpr (MASKED) {
     invalid = map_invalid(a, b);
-    const int* cnt = (const int*)(a.map + a.lay.counts) + ((size_t)b * nqb + qb) * 2;
+    cint* cnt = (cint*)(a.map + a.lay.counts) + ((size_t)b * nqb + qb) * 2;
     const int nfull = min(max(cnt[0], 0), nqb);
     npart = min(max(cnt[1], 0), nqb - nfull);
     nblk = invalid ? 0 : nfull + npart;
-    flist = (const int*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
+    flist = (cint*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
     plist = flist + nqb;
     if (qvalid) {
       lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
@@ -212,26 +220,46 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dacc[db] = f32x16{};
 
-  for (int i = 0; i < nblk; ++i) {
-    int kb = i;
-    if constexpr (MASKED) kb = min(max(i < npart ? plist[i] : flist[i - npart], 0), nqb - 1);
-    for (int hs = 0; hs < 2; ++hs) {
-      const int k0 = kb * 128 + hs * BN;
-      if (k0 >= N) break;
-      __syncthreads();  // the previous step's reads are done
-      for (int t = tid; t < BN * CPR; t += 256) {
-        const int r = t / CPR, c = t - r * CPR;
-        const int key = k0 + r;
-        uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = kx;
-        if (key < N) {
-          const size_t off = ((size_t)bkv * N + key) * D + c * 8;
-          kx = *(const uint4*)(a.k + off);
-          vx = *(const uint4*)(a.v + off);
-        }
-        *(uint4*)(k_sh + r * STR + c * 16) = kx;
-        *(uint4*)(v_sh + r * STR + c * 16) = vx;
+  // Steps s = 0 .. 2*nblk-1 (64 keys each).  The tiles of step s+1 are loaded into
+  // registers while step s computes, and written to LDS between two barriers.
+  constexpr int PF = BN * CPR / 256;  // 16-byte chunks per thread per tile
+  uint4 pk[PF], pv[PF];
+  auto step_k0 = [&](int st_) -> int {
+    int kb = st_ >> 1;
+    if constexpr (MASKED) {
+      const int i = st_ >> 1;
+      kb = min(max(i < npart ? plist[i] : flist[i - npart], 0), nqb - 1);
+    }
+    return kb * 128 + (st_ & 1) * BN;
+  };
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
+      const int key = k0 + r;
+      pk[j] = make_uint4(0u, 0u, 0u, 0u);
+      pv[j] = pk[j];
+      if (key < N) {
+        const size_t off = ((size_t)bkv * N + key) * D + c * 8;
+        pk[j] = *(const uint4*)(a.k + off);
+        pv[j] = *(const uint4*)(a.v + off);
       }
-      __syncthreads();
+    }
+  };
+  const int nsteps = 2 * nblk;
+  if (nsteps > 0) fetch(step_k0(0));
+  for (int st_ = 0; st_ < nsteps; ++st_) {
+    const int k0 = step_k0(st_);
+    __syncthreads();  // the previous step's reads are done
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
+      *(uint4*)(k_sh + r * STR + c * 16) = pk[j];
+      *(uint4*)(v_sh + r * STR + c * 16) = pv[j];
+    }
+    __syncthreads();
+    if (st_ + 1 < nsteps) fetch(step_k0(st_ + 1));
+    {
       f32x16 st[2], dp[2];
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk) {
@@ -249,9 +277,8 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * bk + 4 * hh + acc_row(r);
           float s, dsdr;
-          score(a, st[bk][r], qrow, key, slope, s, dsdr);
-          const bool vis = key >= lo_q && key <= hi_q;
-          const float p = vis ? exp2_(s * kLog2e - lse2) : 0.f;
+          score<SOFTCAP, ALIBI>(a, st[bk][r], qrow, key, slope, s, dsdr);
+          const float p = prob(key >= lo_q && key <= hi_q, s, lse2);
           st[bk][r] = p * (dp[bk][r] - dl) * dsdr;
         }
 #pragma unroll
@@ -278,14 +305,17 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
 }
 
 // ---- dK, dV ------------------------------------------------------------------------------
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
 __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   constexpr int ROWB = 2 * D, STR = ROWB + PADB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
-  constexpr int BM = 32;  // query rows per step
+  constexpr int BM = 64;  // query rows per step
+  constexpr int NBQ = BM / 32;
   __shared__ __attribute__((aligned(16))) unsigned char q_sh[BM * STR];
   __shared__ __attribute__((aligned(16))) unsigned char g_sh[BM * STR];
-  __shared__ float lse_s[BM], dl_s[BM];
-  __shared__ int lo_s[BM], hi_s[BM];
+  __shared__ __attribute__((aligned(16))) float lse_s[BM];
+  __shared__ __attribute__((aligned(16))) float dl_s[BM];
+  __shared__ __attribute__((aligned(16))) int lo_s[BM];
+  __shared__ __attribute__((aligned(16))) int hi_s[BM];
   const lds_u8* qt = (const lds_u8*)q_sh;
   const lds_u8* gt = (const lds_u8*)g_sh;
 
@@ -316,77 +346,133 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     dkacc[db] = f32x16{};
     dvacc[db] = f32x16{};
   }
-  const unsigned char* cls = MASKED ? a.map + a.lay.cls + (size_t)b * nqb * nqb + kb : nullptr;
-
-  for (int hq = 0; hq < grp && !invalid; ++hq) {
-    const int h = kvh * grp + hq;
-    const int bh = b * a.H + h;
-    const float slope = (a.flags & kAlibi) ? head_slope(a, h) : 0.f;
-    for (int qb = 0; qb < nqb; ++qb) {
-      if constexpr (MASKED) {
-        if (cls[(size_t)qb * nqb] == 0) continue;  // EMPTY block
+  cu8* cls = MASKED ? (cu8*)(a.map + a.lay.cls) + (size_t)b * nqb * nqb + kb : nullptr;
+  // Steps: (query head of the group, non-empty query block, 32-row sub-block), in that
+  // nesting.  next() advances a step state; the next step's rows and per-row values are
+  // loaded into registers while the current step computes.
+  auto next = [&](int& hq, int& qb, int& sub) -> bool {
+    ++sub;
+    if (sub == 128 / BM || qb * 128 + sub * BM >= N) {
+      sub = 0;
+      for (;;) {
+        if (++qb == nqb) {
+          qb = 0;
+          if (++hq == grp) return false;
+        }
+        if constexpr (MASKED) {
+          if (cls[(size_t)qb * nqb] == 0) continue;  // EMPTY block
+        }
+        break;
       }
-      for (int sub = 0; sub < 128 / BM; ++sub) {
-        const int q0 = qb * 128 + sub * BM;
-        if (q0 >= N) break;
-        __syncthreads();  // the previous step's reads are done
-        for (int t = tid; t < BM * CPR; t += 256) {
-          const int r = t / CPR, c = t - r * CPR;
-          const int q = q0 + r;
-          uint4 qx = make_uint4(0u, 0u, 0u, 0u), gx = qx;
-          if (q < N) {
-            const size_t off = ((size_t)bh * N + q) * D + c * 8;
-            qx = *(const uint4*)(a.q + off);
-            gx = *(const uint4*)(a.dout + off);
-          }
-          *(uint4*)(q_sh + r * STR + c * 16) = qx;
-          *(uint4*)(g_sh + r * STR + c * 16) = gx;
-        }
-        if (tid < BM) {
-          const int q = q0 + tid;
-          const bool ok = q < N;
-          lse_s[tid] = ok ? a.lse[(size_t)bh * N + q] * kLog2e : 0.f;
-          dl_s[tid] = ok ? a.delta[(size_t)bh * N + q] : 0.f;
-          int lo = 0, hi = ok ? N - 1 : -1;
-          if constexpr (MASKED) {
-            if (ok) {
-              lo = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + q];
-              hi = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + q];
-            }
-          }
-          lo_s[tid] = lo;
-          hi_s[tid] = hi;
-        }
-        __syncthreads();
-        f32x16 s = f32x16{}, dp = f32x16{};
+    }
+    return true;
+  };
+  constexpr int PF = BM * CPR / 256;
+  uint4 pq[PF], pg[PF];
+  float p_lse = 0.f, p_dl = 0.f;
+  int p_lo = 0, p_hi = -1;
+  auto fetch = [&](int hq, int qb, int sub) {
+    const int bh = b * a.H + kvh * grp + hq;
+    const int q0 = qb * 128 + sub * BM;
 #pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-          s = mfma(row_frag<STR>(qt, 0, l32, hh, c), kf[c], s);
-          dp = mfma(row_frag<STR>(gt, 0, l32, hh, c), vf[c], dp);
-        }
-        f32x16 pm, dr;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 4 * hh + acc_row(r);
-          const int q = q0 + qi;
-          float sv, dsdr;
-          score(a, s[r], q, key, slope, sv, dsdr);
-          const bool vis = key >= lo_s[qi] && key <= hi_s[qi];
-          const float p = vis ? exp2_(sv * kLog2e - lse_s[qi]) : 0.f;
-          pm[r] = p;
-          dr[r] = p * (dp[r] - dl_s[qi]) * dsdr;
-        }
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const bf16x8 pb = pack8(pm, g), rb = pack8(dr, g);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dvacc[db] = mfma(tr_frag<STR>(gt, g, troff[db]), pb, dvacc[db]);
-            dkacc[db] = mfma(tr_frag<STR>(qt, g, troff[db]), rb, dkacc[db]);
-          }
+    for (int j = 0; j < PF; ++j) {
+      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
+      const int q = q0 + r;
+      pq[j] = make_uint4(0u, 0u, 0u, 0u);
+      pg[j] = pq[j];
+      if (q < N) {
+        const size_t off = ((size_t)bh * N + q) * D + c * 8;
+        pq[j] = *(const uint4*)(a.q + off);
+        pg[j] = *(const uint4*)(a.dout + off);
+      }
+    }
+    if (tid < BM) {
+      const int q = q0 + tid;
+      const bool ok = q < N;  // (tid < BM: one row per thread)
+      p_lse = ok ? a.lse[(size_t)bh * N + q] * kLog2e : 0.f;
+      p_dl = ok ? a.delta[(size_t)bh * N + q] : 0.f;
+      p_lo = 0;
+      p_hi = ok ? N - 1 : -1;
+      if constexpr (MASKED) {
+        if (ok) {
+          p_lo = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + q];
+          p_hi = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + q];
         }
       }
     }
+  };
+  int hq = 0, qb = -1, sub = 128 / BM - 1;
+  bool have = !invalid && next(hq, qb, sub);
+  if (have) fetch(hq, qb, sub);
+  while (have) {
+    const int h = kvh * grp + hq;
+    const int q0 = qb * 128 + sub * BM;
+    const float slope = ALIBI ? head_slope(a, h) : 0.f;
+    __syncthreads();  // the previous step's reads are done
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
+      *(uint4*)(q_sh + r * STR + c * 16) = pq[j];
+      *(uint4*)(g_sh + r * STR + c * 16) = pg[j];
+    }
+    if (tid < BM) {
+      lse_s[tid] = p_lse;
+      dl_s[tid] = p_dl;
+      lo_s[tid] = p_lo;
+      hi_s[tid] = p_hi;
+    }
+    __syncthreads();
+    int nh = hq, nq = qb, ns = sub;
+    const bool more = next(nh, nq, ns);
+    if (more) fetch(nh, nq, ns);
+    f32x16 s[NBQ], dp[NBQ];
+#pragma unroll
+    for (int bq = 0; bq < NBQ; ++bq) {
+      s[bq] = f32x16{};
+      dp[bq] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NQC; ++c) {
+        s[bq] = mfma(row_frag<STR>(qt, 32 * bq, l32, hh, c), kf[c], s[bq]);
+        dp[bq] = mfma(row_frag<STR>(gt, 32 * bq, l32, hh, c), vf[c], dp[bq]);
+      }
+    }
+#pragma unroll
+    for (int bq = 0; bq < NBQ; ++bq) {
+      f32x16 pm, dr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // rows 32bq + 4hh + 8j .. +3 of the step: one 16-byte LDS read per per-row array
+        const int q4 = 32 * bq + 4 * hh + 8 * j;
+        const float4 l4 = *(const float4*)&lse_s[q4];
+        const float4 d4 = *(const float4*)&dl_s[q4];
+        const int4 lo4 = *(const int4*)&lo_s[q4];
+        const int4 hi4 = *(const int4*)&hi_s[q4];
+        const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
+        const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          float sv, dsdr;
+          score<SOFTCAP, ALIBI>(a, s[bq][r], q0 + q4 + e, key, slope, sv, dsdr);
+          const float p = prob(key >= los[e] && key <= his[e], sv, ls[e]);
+          pm[r] = p;
+          dr[r] = p * (dp[bq][r] - ds[e]) * dsdr;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bf16x8 pb = pack8(pm, g), rb = pack8(dr, g);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = mfma(tr_frag<STR>(gt, 2 * bq + g, troff[db]), pb, dvacc[db]);
+          dkacc[db] = mfma(tr_frag<STR>(qt, 2 * bq + g, troff[db]), rb, dkacc[db]);
+        }
+      }
+    }
+    hq = nh;
+    qb = nq;
+    sub = ns;
+    have = more;
   }
   if (!kvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
@@ -407,18 +493,26 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     }
 }
 
+template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
+void launch_v(const BwdArgs& a, hipStream_t st) {
+  const dim3 gq((unsigned)(a.B * a.H * a.nqb)), gk((unsigned)(a.B * a.Hkv * a.nqb)), blk(256);
+  hipLaunchKernelGGL((dq_kernel<D, MASKED, SOFTCAP, ALIBI>), gq, blk, 0, st, a);
+  hipLaunchKernelGGL((dkdv_kernel<D, MASKED, SOFTCAP, ALIBI>), gk, blk, 0, st, a);
+}
+template <int D, bool MASKED>
+void launch_m(const BwdArgs& a, hipStream_t st) {
+  const bool sc = a.flags & kSoftcap, al = a.flags & kAlibi;
+  if (sc && al) launch_v<D, MASKED, true, true>(a, st);
+  else if (sc) launch_v<D, MASKED, true, false>(a, st);
+  else if (al) launch_v<D, MASKED, false, true>(a, st);
+  else launch_v<D, MASKED, false, false>(a, st);
+}
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool masked, hipStream_t st) {
   const size_t rows = (size_t)a.B * a.H * a.N;
   hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
-  const dim3 gq((unsigned)(a.B * a.H * a.nqb)), gk((unsigned)(a.B * a.Hkv * a.nqb)), blk(256);
-  if (masked) {
-    hipLaunchKernelGGL((dq_kernel<D, true>), gq, blk, 0, st, a);
-    hipLaunchKernelGGL((dkdv_kernel<D, true>), gk, blk, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((dq_kernel<D, false>), gq, blk, 0, st, a);
-    hipLaunchKernelGGL((dkdv_kernel<D, false>), gk, blk, 0, st, a);
-  }
+  if (masked) launch_m<D, true>(a, st);
+  else launch_m<D, false>(a, st);
   return hipGetLastError();
 }
 

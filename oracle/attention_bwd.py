@@ -32,8 +32,11 @@ from .decode import decode_bf16
 
 def attention_bwd_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, *, scale: float,
                       flags: int = 0, window: int = 0, softcap: float = 0.0,
-                      doc_id: Optional[np.ndarray] = None, alibi_slopes: Optional[Sequence[float]] = None):
-    """(dQ [B][H][N][d], dK [B][H_kv][N][d], dV [B][H_kv][N][d], D [B][H][N]) in float64."""
+                      doc_id: Optional[np.ndarray] = None, alibi_slopes: Optional[Sequence[float]] = None,
+                      heads: Optional[Sequence[tuple]] = None):
+    """(dQ [B][H][N][d], dK [B][H_kv][N][d], dV [B][H_kv][N][d], D [B][H][N]) in float64.
+    `heads`, if given, restricts the work to those (b, h) query heads; the gradients of a
+    key/value head are then complete only if every query head sharing it is listed."""
     B, H, N, d = Q.shape
     H_kv = K.shape[1]
     if H_kv < 1 or H % H_kv:
@@ -47,9 +50,12 @@ def attention_bwd_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
     dK = np.zeros(K.shape)
     dV = np.zeros(V.shape)
     Dr = np.zeros((B, H, N))
+    todo = {(b, h) for b in range(B) for h in range(H)} if heads is None else set(heads)
     for b in range(B):
         vis = visible(pos, pos, flags, window, None if doc_id is None else doc_id[b])
         for h in range(H):
+            if (b, h) not in todo:
+                continue
             kv = h // g
             r = Q[b, h] @ K[b, kv].T
             if flags & SOFTCAP:
@@ -78,10 +84,10 @@ def attention_bwd_ref(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
     return dQ, dK, dV, Dr
 
 
-def attention_bwd_problem(p, dO_bits: np.ndarray):
+def attention_bwd_problem(p, dO_bits: np.ndarray, heads: Optional[Sequence[tuple]] = None):
     """Gradients for a bf16 workload.Problem and bf16 output gradients dO [B][H][N][d]."""
     if p.dtype != "bf16":
         raise ValueError("the backward pass takes bf16 inputs")
     Q, K, V = decode_bf16(p.q), decode_bf16(p.k), decode_bf16(p.v)
     return attention_bwd_ref(Q, K, V, decode_bf16(dO_bits), scale=p.scale, flags=p.flags, window=p.window,
-                             softcap=p.softcap, doc_id=p.doc_id, alibi_slopes=p.alibi_slopes)
+                             softcap=p.softcap, doc_id=p.doc_id, alibi_slopes=p.alibi_slopes, heads=heads)

@@ -93,3 +93,15 @@ def test_larger(variant):
     got = _bwd(p, dO)
     ref = oracle.attention_bwd_problem(p, dO)
     _check(got, ref, f"bwd {variant} N=1500")
+
+
+def test_full_size_sampled_heads():
+    """B4 H16 N2048 d128 causal (the default forward workload): eight whole heads."""
+    p = W.config_problem(2)
+    dO = W.make_dout(p, seed=2)
+    _announce("bwd full size")
+    got = _bwd(p, dO)
+    heads = [(b, h) for b, h in ((0, 0), (0, 7), (1, 3), (1, 15), (2, 1), (2, 8), (3, 5), (3, 14))]
+    ref = oracle.attention_bwd_problem(p, dO, heads=heads)
+    sel = lambda t, hs: np.stack([t[b, h] for b, h in hs])
+    _check([sel(g, heads) for g in got], [sel(r, heads) for r in ref], "bwd B4 H16 N2048 causal")
