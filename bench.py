@@ -35,6 +35,9 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["exact_attention_119_amd/csrc/fwd_bf16.hpp", "exact_attention_119_amd/csrc/fwd_kernel.hpp",
                   "exact_attention_119_amd/csrc/fwd_args.hpp", "exact_attention_119_amd/csrc/common.hpp",
                   "exact_attention_119_amd/build.py"]
+QUANT_SOURCES = ["exact_attention_119_amd/csrc/quant.hip", "exact_attention_119_amd/csrc/common.hpp",
+                 "exact_attention_119_amd/build.py"]
+QUANT_WORKLOAD = "quantise B1 H16 N16384 d128 bf16, rotated"
 METRIC = "attention fwd TFLOP/s (unmasked FLOPs) and % of MI355X bf16/fp8 MFMA peak"
 
 
@@ -42,9 +45,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if files is None else files):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -118,15 +121,15 @@ def cpu_baseline(p, budget_s: float):
                       f"{dt:.1f} s wall"}
 
 
-def traffic_record(name: str):
-    """HBM bytes per forward launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources."""
+def traffic_record(name: str, files=None):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(name)
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -245,7 +248,8 @@ def bench_quant(args):
            "config": {"workload": "quantise Q, K (rotated) and V: B1 H16 N16384 d128 bf16", "elements_per_launch": elems,
                       "bytes_per_launch": bytes_launch, "parallelism": "single GPU"},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": traffic_record(QUANT_WORKLOAD, QUANT_SOURCES),
                         "kernel": "quant_kernel<128> (rotated)", "kernel_avg_ms": round(rot_avg, 5)}}
     if not args.no_cpu:
         from oracle import quant as Qz
