@@ -329,47 +329,55 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   };
 
   // ---- fp8: staging through VGPRs ------------------------------------------------------
-  // Thread t stages row t/4 of a 64-row tile, codes (t%4)*CPT .. +CPT: stage_* loads the
-  // codes of a step into registers (range-checked: rows past N read as zero codes), and
-  // commit_*_chunk widens 8 of them (one 16-byte chunk of the 16-bit row) and writes the
-  // chunk to the tile in the same swizzled layouts as above.  A tile is staged one step
-  // before it is committed, so the load latency is spent under a whole step.
-  constexpr int CPT = D / 4;       // codes per thread per tile
-  constexpr int SLD = CPT / 16;    // 16-byte loads per thread per tile
-  constexpr int SCH = CPT / 8;     // 16-byte 16-bit chunks per thread per tile
-  u32x4 kst[FP8 ? SLD : 1], vst[FP8 ? SLD : 1];
+  // Thread t stages SCH 8-code chunks of row t/4 of a 64-row tile: stage_* loads them into
+  // registers (range-checked: rows past N read as zero codes), commit_*_chunk widens one
+  // (8 codes -> one 16-byte chunk of the 16-bit row) and writes it to the tile in the
+  // swizzled layouts above.  A tile is staged one step before it is committed, so the load
+  // latency is spent under a whole step.
+  // Which chunk a thread commits in slot j is chosen by its LDS position, not its index:
+  // LDS serves a 16-byte write to 8 lanes per cycle, so the 8 lanes of a group (2 rows x 4
+  // threads) must hit 8 different 16-byte slots of a 128-byte line (and the 16 lanes of 4
+  // rows 16 different slots of 256 bytes).  Slot j of thread (row r, q = t%4) writes
+  // position p = 4(j ^ (r%4)) + q (d = 128) or 2q + (j ^ r0 ^ r1) (d = 64, r0 r1 the low
+  // bits of r); for a fixed row these cover every position once, and the chunk that
+  // belongs there, p ^ swizzle(r), is the one the thread loads for slot j.
+  constexpr int SCH = D / 32;      // 8-code chunks per thread per tile
+  u32x2 kst[FP8 ? SCH : 1], vst[FP8 ? SCH : 1];
+  int kldo[FP8 ? SCH : 1], vldo[FP8 ? SCH : 1], stpos[FP8 ? SCH : 1];
   const int srow = tid >> 2;
+  if constexpr (FP8) {
+    const int q = tid & 3;
+#pragma unroll
+    for (int j = 0; j < SCH; ++j) {
+      const int p = D == 128 ? 4 * (j ^ (srow & 3)) + q : 2 * q + (j ^ (srow & 1) ^ ((srow >> 1) & 1));
+      stpos[j] = srow * ROWB + p * 16;
+      kldo[j] = srow * D + (p ^ kswz(srow)) * 8;
+      vldo[j] = srow * D + (p ^ vswz(srow)) * 8;
+    }
+  }
   auto stage_k = [&](int k0) {
     if constexpr (FP8) {
       const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
 #pragma unroll
-      for (int j = 0; j < SLD; ++j)
-        kst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, srow * D + (tid & 3) * CPT + 16 * j, 0, 0));
+      for (int j = 0; j < SCH; ++j)
+        kst[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, kldo[j], 0, 0));
     }
   };
   auto stage_v = [&](int k0) {
     if constexpr (FP8) {
       const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
 #pragma unroll
-      for (int j = 0; j < SLD; ++j)
-        vst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, srow * D + (tid & 3) * CPT + 16 * j, 0, 0));
+      for (int j = 0; j < SCH; ++j)
+        vst[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vldo[j], 0, 0));
     }
   };
   auto commit_k_chunk = [&](lds_u8* dst, int j) {
-    if constexpr (FP8) {
-      const u32x4& w = kst[j >> 1];
-      const u32x4 v = (j & 1) ? e4m3x8_to_bf16x8(w.z, w.w) : e4m3x8_to_bf16x8(w.x, w.y);
-      const int ch = (tid & 3) * SCH + j;
-      *(__attribute__((address_space(3))) u32x4*)(dst + srow * ROWB + (ch ^ kswz(srow)) * 16) = v;
-    }
+    if constexpr (FP8)
+      *(__attribute__((address_space(3))) u32x4*)(dst + stpos[j]) = e4m3x8_to_bf16x8(kst[j].x, kst[j].y);
   };
   auto commit_v_chunk = [&](lds_u8* dst, int j) {
-    if constexpr (FP8) {
-      const u32x4& w = vst[j >> 1];
-      const u32x4 v = (j & 1) ? e4m3x8_to_f16x8(w.z, w.w) : e4m3x8_to_f16x8(w.x, w.y);
-      const int ch = (tid & 3) * SCH + j;
-      *(__attribute__((address_space(3))) u32x4*)(dst + srow * ROWB + (ch ^ vswz(srow)) * 16) = v;
-    }
+    if constexpr (FP8)
+      *(__attribute__((address_space(3))) u32x4*)(dst + stpos[j]) = e4m3x8_to_f16x8(vst[j].x, vst[j].y);
   };
   auto commit_k = [&](lds_u8* dst) {
 #pragma unroll
