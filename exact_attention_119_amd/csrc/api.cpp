@@ -160,6 +160,7 @@ attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* 
   layout->row_hi = m.row_hi;
   layout->pairs = m.pairs;
   layout->status = m.status;
+  layout->order = m.order;
   layout->total = m.total;
   return ATTN_OK;
 }
@@ -305,6 +306,9 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   constexpr long kSlots = 2 * 256;
   const long items = (long)B * H * a.nqb;
   a.order = ((flags & ATTN_CAUSAL) && items < 4 * kSlots) ? kOrderHeavyFirst : kOrderHeadMajor;
+  // Under a document mask a row block's work depends on its place in its document: take
+  // the heaviest-first order the map builder derived from the block lists.
+  if (masked && (flags & ATTN_DOCUMENT)) a.order = kOrderMapSorted;
   hipError_t e;
   const hipStream_t s = (hipStream_t)stream;
   const FwdVariant var = select_variant(d, dtype, mask, fp8);

@@ -14,6 +14,10 @@
 //          such word is invalid);
 //   its row of blocks: the class of every 128x128 block, the ascending lists of FULL
 //          and PARTIAL key blocks and the visible-pair count of the query block.
+// A second launch, for document masks only, fills the work-order section: the
+// (batch row, query block) pairs heaviest-first by the work of their block lists (other
+// masks keep the identity order the first launch writes; their work is known from the
+// row index).
 // No atomics, no memset: every byte of every section is written, so the result is
 // byte-identical for equal inputs and the calls are safe to capture in a graph.
 #include "common.hpp"
@@ -178,7 +182,33 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
     counts[1] = part_base;
     long long* pairs = (long long*)(a.map + a.lay.pairs) + (size_t)b * nb + qb;
     *pairs = s_pairs[0] + s_pairs[1] + s_pairs[2] + s_pairs[3];
+    ((int32_t*)(a.map + a.lay.order))[(size_t)b * nb + qb] = b * nb + qb;  // identity order
   }
+}
+
+// Work order for document masks: entry e = b * nb + qb has the work estimate
+// w(e) = kOrderFullCost * #FULL + kOrderPartialCost * #PARTIAL, and goes to position
+// rank(e) = #{e' : w(e') > w(e), or w(e') == w(e) and e' < e} -- a permutation of
+// 0 .. M-1 (heaviest first, ties in index order).  One thread per entry; every
+// workgroup streams all M estimates through LDS in chunks.
+__global__ void __launch_bounds__(256) order_kernel(const int32_t* counts, int32_t* order, int M) {
+  constexpr int CH = 1024;
+  __shared__ int s_w[CH];
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  auto work = [&](int i) { return kOrderFullCost * counts[2 * i] + kOrderPartialCost * counts[2 * i + 1]; };
+  const int we = e < M ? work(e) : 0;
+  int rank = 0;
+  for (int c0 = 0; c0 < M; c0 += CH) {
+    const int n = min(CH, M - c0);
+    for (int i = threadIdx.x; i < n; i += 256) s_w[i] = work(c0 + i);
+    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+      const int w = s_w[i];
+      rank += (w > we) | ((w == we) & (c0 + i < e));
+    }
+    __syncthreads();
+  }
+  if (e < M) order[rank] = e;
 }
 
 // Packed variable-length batch: token t belongs to sequence i when cu[i] <= t < cu[i+1].
@@ -218,6 +248,11 @@ hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int
   a.cu = cu;
   a.nseq = nseq;
   hipLaunchKernelGGL(blockmap_kernel, dim3(a.nb, B), dim3(256), 0, stream, a);
+  if (a.flags & kDocument) {
+    const int M = B * a.nb;
+    hipLaunchKernelGGL(order_kernel, dim3((M + 255) / 256), dim3(256), 0, stream,
+                       (const int32_t*)(map + a.lay.counts), (int32_t*)(map + a.lay.order), M);
+  }
   return hipGetLastError();
 }
 

@@ -22,12 +22,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kMapMagic = 0x39313141u;  // "A119"
 constexpr int kBlock = 128;                  // block-map granularity (queries and keys)
 
+// Work estimate of a query block in the work-order section of the map: a FULL key block
+// is two 64-key steps, a PARTIAL one costs about 2.5 times as much (its mask code).
+constexpr int kOrderFullCost = 2, kOrderPartialCost = 5;
+
 constexpr uint32_t kCausal = 1, kWindow = 2, kDocument = 4, kAlibi = 8, kSoftcap = 16;
 constexpr uint32_t kPositional = kCausal | kWindow | kDocument;
 
 // Byte offsets of the block-map sections (see attn_blockmap_header in attn119.h).
 struct MapLayout {
-  size_t cls, counts, idx, row_lo, row_hi, pairs, status, total;
+  size_t cls, counts, idx, row_lo, row_hi, pairs, status, order, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -49,6 +53,8 @@ __host__ __device__ inline MapLayout map_layout(int B, int N) {
   m.pairs = off;
   off = align256(off + (size_t)B * nb * 8);
   m.status = off;
+  off = align256(off + (size_t)B * nb * 4);
+  m.order = off;
   off = align256(off + (size_t)B * nb * 4);
   m.total = off;
   return m;

@@ -41,7 +41,12 @@ struct FwdArgs {
 //                    when there are only a few workgroups per slot.  With B*H a multiple
 //                    of 8 a head still stays on one XCD, and so does a run of
 //                    consecutive heads.
-constexpr int kOrderHeadMajor = 0, kOrderHeavyFirst = 1;
+//  kOrderMapSorted : document masks, where a row block's work depends on where it sits
+//                    in its document: the block map's work-order section lists the
+//                    (batch row, row block) pairs heaviest-first, and workgroup L takes
+//                    pair order[L / H] of head L % H (H a multiple of 8: XCD x takes the
+//                    contiguous heads x*H/8 .. (x+1)*H/8-1 of every batch row).
+constexpr int kOrderHeadMajor = 0, kOrderHeavyFirst = 1, kOrderMapSorted = 2;
 
 // Flat key/value head index (b * Hkv + key/value head) of flat query head bh = b * H + h.
 __device__ __forceinline__ int kv_head(const FwdArgs& a, int bh) {
@@ -51,7 +56,22 @@ __device__ __forceinline__ int kv_head(const FwdArgs& a, int bh) {
 
 __device__ __forceinline__ void work_item(const FwdArgs& a, int L, int& bh, int& qb) {
   const int nqb = a.nqb;
-  if (a.order == kOrderHeavyFirst) {
+  if (a.order == kOrderMapSorted) {
+    const int H = a.H, M = a.B * nqb;
+    const int r = L / H;
+    const int i = L - r * H;
+    const int h = (H & 7) ? i : (i & 7) * (H >> 3) + (i >> 3);
+    // a map that fails its header check (it is then ignored and the outputs poisoned)
+    // falls back to the identity order, so every work item is still visited once
+    typedef const __attribute__((address_space(4))) int cint;
+    const __attribute__((address_space(4))) MapHeader* hd =
+        (const __attribute__((address_space(4))) MapHeader*)a.map;
+    const bool ok = hd->magic == kMapMagic && hd->B == a.B && hd->N == a.N;
+    const int e = ok ? min(max(((cint*)(a.map + a.lay.order))[r], 0), M - 1) : r;
+    const int b = e / nqb;
+    bh = b * H + h;
+    qb = e - b * nqb;
+  } else if (a.order == kOrderHeavyFirst) {
     const int BH = a.B * a.H;
     const int r = L / BH;
     const int i = L - r * BH;

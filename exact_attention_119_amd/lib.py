@@ -62,7 +62,7 @@ class attn_fp8(ctypes.Structure):
 
 
 class attn_blockmap_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status",
+    _fields_ = [(n, ctypes.c_size_t) for n in ("cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status", "order",
                                                "total")]
 
 
@@ -302,4 +302,4 @@ def read_blockmap(blockmap, B: int, N: int) -> dict:
                 cls=sec("cls", np.uint8, (B, nb, nb)), counts=sec("counts", np.int32, (B, nb, 2)),
                 idx=sec("idx", np.int32, (B, nb, 2, nb)), row_lo=sec("row_lo", np.int32, (B, N)),
                 row_hi=sec("row_hi", np.int32, (B, N)), pairs=sec("pairs", np.int64, (B, nb)),
-                status=sec("status", np.int32, (B, nb)))
+                status=sec("status", np.int32, (B, nb)), order=sec("order", np.int32, (B * nb,)))

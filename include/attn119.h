@@ -137,6 +137,11 @@ typedef struct attn_fp8 {
  *                                       the next row (packed batches: or the share of the
  *                                       sequence offsets this block checks is out of order),
  *                                       else 0 (a batch row with any 1 is invalid)
+ *   order    : int32  [B * nqb]         work order of the forward pass (scheduling only; it
+ *                                       never changes a result): with ATTN_DOCUMENT the
+ *                                       entries e = b * nqb + qb sorted by decreasing work
+ *                                       2 * #FULL + 5 * #PARTIAL, equal work in increasing e;
+ *                                       without it the identity 0 .. B*nqb-1
  */
 typedef struct attn_blockmap_header {
   uint32_t magic; /* 0x39313141 */
@@ -147,7 +152,7 @@ typedef struct attn_blockmap_header {
 } attn_blockmap_header;
 
 typedef struct attn_blockmap_layout {
-  size_t cls, counts, idx, row_lo, row_hi, pairs, status, total;
+  size_t cls, counts, idx, row_lo, row_hi, pairs, status, order, total;
 } attn_blockmap_layout;
 
 /* Size in bytes of the block-map workspace for (B, N, mask).  Host only. */

@@ -44,7 +44,7 @@ def test_blockmap_layout(L):
     lay = L.attn_blockmap_layout_of(2, 300)
     nb = 3
     assert lay["cls"] == 256
-    order = ["cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status", "total"]
+    order = ["cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status", "order", "total"]
     for a, b in zip(order, order[1:]):
         assert lay[a] < lay[b] and lay[b] % 256 == 0
     assert lay["counts"] - lay["cls"] >= 2 * nb * nb

@@ -73,7 +73,7 @@ def _check_prepared(dp):
     ref = oracle.blockmap_ref(1, p.N, flags, p.window, ids_ref[None])
     assert (got["header"]["B"], got["header"]["N"], got["header"]["flags"]) == (1, p.N, flags)
     np.testing.assert_array_equal(got["status"], ref["status"])
-    for key in ("cls", "counts", "idx", "row_lo", "row_hi"):
+    for key in ("cls", "counts", "idx", "row_lo", "row_hi", "order"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
     np.testing.assert_array_equal(got["pairs"], ref["qb_pairs"])
     assert L.attn_blockmap_status(dp.blockmap[:mb]) == L.ATTN_OK

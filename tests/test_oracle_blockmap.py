@@ -124,3 +124,22 @@ def test_qb_pairs_and_doc_status():
     assert m["status"][0].tolist() == [0, 0, 0]
     assert m["status"][1].tolist() == [0, 1, 0]  # the decrease 2 -> 1 is at row 139
     assert O.blockmap_ref(2, 320, CAUSAL, 0, doc)["status"].sum() == 0
+
+
+def test_work_order_properties():
+    """The work order is a permutation of the (b, qb) entries; under a document mask the
+    work 2 * #FULL + 5 * #PARTIAL never increases along it and equal work keeps index
+    order; other masks keep the identity."""
+    rng = np.random.default_rng(7)
+    lengths = rng.integers(40, 700, size=12)
+    doc = np.repeat(np.arange(len(lengths)), lengths)[:1500].astype(np.int32)
+    doc = np.stack([doc, np.sort(rng.integers(0, 5, size=1500)).astype(np.int32)])
+    m = O.blockmap_ref(2, 1500, CAUSAL | DOCUMENT, 0, doc)
+    order = m["order"]
+    nb = m["counts"].shape[1]
+    assert sorted(order.tolist()) == list(range(2 * nb))
+    work = [2 * int(m["counts"][e // nb, e % nb, 0]) + 5 * int(m["counts"][e // nb, e % nb, 1]) for e in order]
+    assert len(set(work)) > 3  # the workload does spread the work
+    for i in range(len(order) - 1):
+        assert work[i] > work[i + 1] or (work[i] == work[i + 1] and order[i] < order[i + 1])
+    assert O.blockmap_ref(2, 1500, CAUSAL, 0, doc)["order"].tolist() == list(range(2 * nb))
