@@ -35,12 +35,22 @@ struct MapArgs {
   int nseq;
 };
 
-// First index i in [0, N) with row[i] >= v (row non-decreasing).
-__device__ inline int lower_bound_i32(const int32_t* row, int N, int v) {
-  int lo = 0, hi = N;
+// First index i in [0, N] with row[i] >= v (row non-decreasing), found by the whole
+// workgroup: each round the 256 threads probe evenly spaced positions of the interval
+// left and keep the gap where the predicate row[i] < v turns false (two rounds of loads
+// for N <= 65536, instead of log2 N dependent loads in one thread).  Must be reached by
+// all threads with the same arguments.  For any row contents the result stays in [0, N]
+// and the loop ends (the interval shrinks to below 1/256 each round).
+__device__ int par_lower_bound(const int32_t* row, int N, int v) {
+  int lo = 0, hi = N;  // the answer lies in [lo, hi]
   while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (row[mid] < v) lo = mid + 1; else hi = mid;
+    const int step = (hi - lo + 255) / 256;
+    const int p = lo + (int)threadIdx.x * step;
+    const int c = __syncthreads_count(p < hi && row[p] < v);
+    if (c == 0) break;  // row[lo] >= v
+    const int base = lo;
+    lo = base + (c - 1) * step + 1;
+    hi = min(base + c * step, hi);
   }
   return lo;
 }
@@ -59,6 +69,40 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   __shared__ long long s_pairs[4];
 
   // ---- row intervals (threads 0..127, one query row each) and the status word ----------
+  // Documents: the rows' ids (and the next row's) go to LDS; a row's document starts at
+  // the first row of its run in the block, or, for the run that reaches the block's first
+  // row, where that document starts in the batch row (one search for the workgroup), and
+  // ends likewise.
+  __shared__ int s_doc[kBlock + 1];
+  __shared__ int s_run_f[4], s_run_g[4];
+  int first0 = 0, last1 = N - 1, run_first = 0, run_last = 0;
+  if (a.flags & kDocument) {
+    const int32_t* drow = a.doc_id + (size_t)b * N;
+    if (tid <= nrows && q0 + tid < N) s_doc[tid] = drow[q0 + tid];
+    __syncthreads();
+    const int v0 = s_doc[0], v1 = s_doc[nrows - 1];
+    first0 = par_lower_bound(drow, N, v0);
+    last1 = (v1 == INT32_MAX) ? N - 1 : par_lower_bound(drow, N, v1 + 1) - 1;
+    // runs of equal ids inside the block: the first row of this row's run is the
+    // largest run start at or before it (prefix max over the rows), the last row the
+    // smallest run end at or after it (suffix min); threads 0..127 are waves 0 and 1
+    int f = tid, g = tid;  // rows past the block's end count as runs of their own
+    if (tid < nrows) {
+      const int dq = s_doc[tid];
+      f = (tid == 0 || s_doc[tid - 1] != dq) ? tid : -1;
+      g = (tid == nrows - 1 || s_doc[tid + 1] != dq) ? tid : INT32_MAX;
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+      const int fu = __shfl_up(f, off), gd = __shfl_down(g, off);
+      if (lane >= off) f = max(f, fu);
+      if (lane + off < 64) g = min(g, gd);
+    }
+    if (lane == 63) s_run_f[wave] = f;
+    if (lane == 0) s_run_g[wave] = g;
+    __syncthreads();
+    run_first = wave == 1 ? max(f, s_run_f[0]) : f;
+    run_last = wave == 0 ? min(g, s_run_g[1]) : g;
+  }
   int bad = 0;
   if (tid < kBlock) {
     int lo = 0, hi = -1;
@@ -72,13 +116,9 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
         if (!(a.flags & kCausal)) hi = min(hi, q + (a.window - 1));
       }
       if (a.flags & kDocument) {
-        const int32_t* drow = a.doc_id + (size_t)b * N;
-        const int dq = drow[q];
-        if (q + 1 < N && drow[q + 1] < dq) bad = 1;
-        const int first = lower_bound_i32(drow, N, dq);
-        const int last = (dq == INT32_MAX) ? N - 1 : lower_bound_i32(drow, N, dq + 1) - 1;
-        lo = max(lo, first);
-        hi = min(hi, last);
+        if (q + 1 < N && s_doc[tid + 1] < s_doc[tid]) bad = 1;
+        lo = max(lo, run_first == 0 ? first0 : q0 + run_first);
+        hi = min(hi, run_last == nrows - 1 ? last1 : q0 + run_last);
       }
       if (hi < lo) { lo = 0; hi = -1; }
       ((int32_t*)(a.map + a.lay.row_lo))[(size_t)b * N + q] = lo;
@@ -111,40 +151,32 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   int32_t* idx_full = (int32_t*)(a.map + a.lay.idx) + ((size_t)b * nb + qb) * 2 * nb;
   int32_t* idx_part = idx_full + nb;
 
-  // classes and ascending CSR lists, up to 256 key blocks per round (64 per wave).  With
-  // K < 256 key blocks in a round, the rows are split into 256/K chunks so that every
-  // thread scans a share of them (a short serial loop over LDS instead of 128 rows).
-  __shared__ unsigned char s_any[256], s_all[256];
+  // classes and ascending CSR lists, up to 256 key blocks per round.  Wave w holds rows
+  // 64*(w%2) + lane (their intervals in registers) and tests the key blocks of parity w/2
+  // against all of them at once: one ballot for "some row sees a key of the block", one
+  // for "every row sees all of it".
+  __shared__ unsigned char s_any[2][256], s_all[2][256];
+  const int half = wave & 1;
+  const int my_lo = s_lo[64 * half + lane], my_hi = s_hi[64 * half + lane];
   int full_base = 0, part_base = 0;
   for (int kb0 = 0; kb0 < nb; kb0 += 256) {
     const int K = min(256, nb - kb0);
-    const int C = 256 / K;              // row chunks per key block
-    const int R = (nrows + C - 1) / C;  // rows per chunk
-    {
-      const int kl = tid % K, ch = tid / K;
-      bool any = false, all = true;
-      if (ch < C) {
-        const int k0 = (kb0 + kl) * kBlock, k1 = min(N, k0 + kBlock) - 1;
-        const int r1 = min(nrows, ch * R + R);
-        for (int r = ch * R; r < r1; ++r) {
-          const int lo = s_lo[r], hi = s_hi[r];
-          any |= (max(lo, k0) <= min(hi, k1));
-          all &= (lo <= k0) && (hi >= k1);
-        }
+    for (int kl = wave >> 1; kl < K; kl += 2) {
+      const int k0 = (kb0 + kl) * kBlock, k1 = min(N, k0 + kBlock) - 1;
+      const uint64_t any = __ballot(max(my_lo, k0) <= min(my_hi, k1));
+      const uint64_t all = __ballot(my_lo <= k0 && my_hi >= k1);
+      if (lane == 0) {
+        s_any[half][kl] = any != 0;
+        s_all[half][kl] = all == ~0ull;
       }
-      s_any[tid] = any;
-      s_all[tid] = all;
     }
     __syncthreads();
     const int kb = kb0 + tid;
     int c = 0;
     if (tid < K) {
       const int k0 = kb * kBlock, k1 = min(N, k0 + kBlock) - 1;
-      bool any = false, all = (nrows == kBlock) && (k1 - k0 + 1 == kBlock);
-      for (int ch = 0; ch < C; ++ch) {
-        any |= s_any[ch * K + tid] != 0;
-        all &= s_all[ch * K + tid] != 0;
-      }
+      const bool any = s_any[0][tid] | s_any[1][tid];
+      const bool all = s_all[0][tid] & s_all[1][tid] & (nrows == kBlock) & (k1 - k0 + 1 == kBlock);
       c = !any ? 0 : (all ? 2 : 1);
       cls[kb] = (unsigned char)c;
     }
