@@ -35,24 +35,48 @@ struct MapArgs {
   int nseq;
 };
 
-// First index i in [0, N] with row[i] >= v (row non-decreasing), found by the whole
-// workgroup: each round the 256 threads probe evenly spaced positions of the interval
-// left and keep the gap where the predicate row[i] < v turns false (two rounds of loads
-// for N <= 65536, instead of log2 N dependent loads in one thread).  Must be reached by
-// all threads with the same arguments.  For any row contents the result stays in [0, N]
-// and the loop ends (the interval shrinks to below 1/256 each round).
-__device__ int par_lower_bound(const int32_t* row, int N, int v) {
-  int lo = 0, hi = N;  // the answer lies in [lo, hi]
-  while (lo < hi) {
-    const int step = (hi - lo + 255) / 256;
-    const int p = lo + (int)threadIdx.x * step;
-    const int c = __syncthreads_count(p < hi && row[p] < v);
-    if (c == 0) break;  // row[lo] >= v
-    const int base = lo;
-    lo = base + (c - 1) * step + 1;
-    hi = min(base + c * step, hi);
+// Narrows a search interval [lo, hi] after a round whose probes lo + t*step (t < 256)
+// found the predicate true at c of them (a prefix when the row is sorted).
+__device__ inline void narrow(int& lo, int& hi, int step, int c, bool& done) {
+  if (c == 0) { done = true; return; }  // false already at lo
+  const int base = lo;
+  lo = base + (c - 1) * step + 1;
+  hi = min(base + c * step, hi);
+  done = lo >= hi;
+}
+
+// Two searches over one non-decreasing row, by the whole workgroup: lower = first index
+// with row[i] >= va, upper = first index with row[i] > vb (both in [0, N]).  Each round
+// the 256 threads probe evenly spaced positions of both intervals left and keep the gap
+// where the predicate turns false, so N <= 65536 takes two rounds of loads; the first
+// round's probes sit at fixed positions and come in with the caller's other loads
+// (pv0 = row[tid * ceil(N/256)] where that is < N).  Must be reached by all threads with
+// the same arguments; for any row contents both results stay in [0, N] and the loop ends
+// (each interval shrinks to below 1/256 per round).
+__device__ void par_bounds(const int32_t* row, int N, int pv0, int va, int vb, int& lower, int& upper) {
+  const int t = threadIdx.x;
+  int lo_a = 0, hi_a = N, lo_b = 0, hi_b = N;
+  bool da = false, db = false;
+  {
+    const int step = (N + 255) / 256;
+    const bool in = t * step < N;
+    const int ca = __syncthreads_count(in && pv0 < va);
+    const int cb = __syncthreads_count(in && pv0 <= vb);
+    narrow(lo_a, hi_a, step, ca, da);
+    narrow(lo_b, hi_b, step, cb, db);
   }
-  return lo;
+  while (!da || !db) {
+    const int sa = (hi_a - lo_a + 255) / 256, sb = (hi_b - lo_b + 255) / 256;
+    const int pa = lo_a + t * sa, pb = lo_b + t * sb;
+    const bool ia = !da && pa < hi_a, ib = !db && pb < hi_b;
+    const int xa = ia ? row[pa] : 0, xb = ib ? row[pb] : 0;
+    const int ca = __syncthreads_count(ia && xa < va);
+    const int cb = __syncthreads_count(ib && xb <= vb);
+    if (!da) narrow(lo_a, hi_a, sa, ca, da);
+    if (!db) narrow(lo_b, hi_b, sb, cb, db);
+  }
+  lower = lo_a;
+  upper = lo_b;
 }
 
 // One workgroup (256 threads, 4 waves) per (query block, batch row): the intervals and
@@ -78,11 +102,13 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   int first0 = 0, last1 = N - 1, run_first = 0, run_last = 0;
   if (a.flags & kDocument) {
     const int32_t* drow = a.doc_id + (size_t)b * N;
+    const int step0 = (N + 255) / 256;
+    const int pv0 = tid * step0 < N ? drow[tid * step0] : 0;
     if (tid <= nrows && q0 + tid < N) s_doc[tid] = drow[q0 + tid];
     __syncthreads();
-    const int v0 = s_doc[0], v1 = s_doc[nrows - 1];
-    first0 = par_lower_bound(drow, N, v0);
-    last1 = (v1 == INT32_MAX) ? N - 1 : par_lower_bound(drow, N, v1 + 1) - 1;
+    int past1;
+    par_bounds(drow, N, pv0, s_doc[0], s_doc[nrows - 1], first0, past1);
+    last1 = past1 - 1;
     // runs of equal ids inside the block: the first row of this row's run is the
     // largest run start at or before it (prefix max over the rows), the last row the
     // smallest run end at or after it (suffix min); threads 0..127 are waves 0 and 1
