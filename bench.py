@@ -5,7 +5,10 @@
 A step is one pass of the whole path over one batch of synthetic input already
 resident in HBM: the block-map build (when the mask needs one) followed by the
 forward pass, both on the current stream.  `value` is attention TFLOP/s over the
-unmasked FLOPs, 4*d*H*(visible (q, k) pairs) per step, divided by the step time.
+unmasked FLOPs, 4*d*H*(visible (q, k) pairs) per step, divided by the step time: the
+host clock around K steps launched back to back, synchronised on both sides.  The
+kernels' average durations (the roofline figures) come from a second pass that launches
+each kernel K times back to back between one pair of HIP events.
 
 Default workload: B=4 H=16 N=2048 d=128, causal, bf16 (configuration 2).  Other
 --config values are the other synthetic workloads (1: B1 H2 N256 d64 plain;
@@ -121,6 +124,18 @@ def cpu_baseline(p, budget_s: float):
                       f"{dt:.1f} s wall"}
 
 
+def loop_ms(torch, stream, n: int, launch) -> float:
+    """Average duration of `launch` over n back-to-back calls on `stream` (HIP events)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def traffic_record(name: str, files=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
     the current kernel sources."""
@@ -158,21 +173,17 @@ def bench_bwd(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
+    for _ in range(args.steps):
         step()
-        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
-    avg = sum(ms) / len(ms)
+    avg = loop_ms(torch, stream, args.steps, step)
     pairs = visible_pairs(p)
     flop = 10.0 * p.d * p.H * pairs  # five products of 2*d flop per visible pair
     step_ms = wall * 1e3 / args.steps
     name = workload_name(p)
-    log(f"bench: backward step {step_ms:.4f} ms (wall), three launches avg {avg:.4f} ms (events)")
+    log(f"bench: backward step {step_ms:.4f} ms (wall), three launches avg {avg:.4f} ms (back-to-back, events)")
     out = {"metric": "attention bwd TFLOP/s (five products of 2d flop per visible pair)",
            "value": round(flop / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
@@ -215,26 +226,19 @@ def bench_quant(args):
     signs = [QUANT_SIGNS, QUANT_SIGNS, None]
     stream = torch.cuda.current_stream()
 
-    def step(evs=None):
+    def step():
         for i in range(3):
-            if evs is not None:
-                evs[i][0].record(stream)
             L.attn_fp8_quantize(xs[i], codes[i], scales[i], signs[i])
-            if evs is not None:
-                evs[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
-           for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e in evs:
-        step(e)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    rot = sorted(e[i][0].elapsed_time(e[i][1]) for e in evs for i in (0, 1))
-    rot_avg = sum(rot) / len(rot)
+    rot_avg = loop_ms(torch, stream, 2 * args.steps, lambda: L.attn_fp8_quantize(xs[0], codes[0], scales[0], signs[0]))
     elems = p.B * p.H * p.N * p.d
     bytes_launch = elems * 3 + 4 * p.B * p.H * nblk
     step_ms = wall * 1e3 / args.steps
@@ -269,8 +273,8 @@ def bench_quant(args):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--plain-causal", action="store_true", help="configuration-3 shape, plain causal mask")
     ap.add_argument("--shape", type=str, default=None,
@@ -346,25 +350,19 @@ def main(argv=None):
         WD.step(dp, args.tau)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # The timed region: K whole steps back to back with nothing else on the stream.
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        WD.build_map(dp)
-        e1.record(stream)
-        WD.forward(dp, args.tau)
-        e2.record(stream)
+    for _ in range(args.steps):
+        WD.step(dp, args.tau)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sorted(e1.elapsed_time(e2) for _, e1, e2 in ev)
-    map_ms = sorted(e0.elapsed_time(e1) for e0, e1, _ in ev)
     step_ms = wall * 1e3 / args.steps
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    map_avg = sum(map_ms) / len(map_ms)
-    log(f"bench: step {step_ms:.4f} ms (wall), forward kernel avg {fwd_avg:.4f} ms "
-        f"(min {fwd_ms[0]:.4f}, median {fwd_ms[len(fwd_ms) // 2]:.4f}), block map avg {map_avg:.4f} ms")
+    # Average launch duration of each kernel: K launches of it back to back on the same
+    # stream, one event pair around them (events between launches would add their own gaps).
+    fwd_avg = loop_ms(torch, stream, args.steps, lambda: WD.forward(dp, args.tau))
+    map_avg = loop_ms(torch, stream, args.steps, lambda: WD.build_map(dp)) if dp.blockmap is not None else 0.0
+    log(f"bench: step {step_ms:.4f} ms (wall), forward kernel avg {fwd_avg:.4f} ms, block map build avg "
+        f"{map_avg:.4f} ms (back-to-back launches)")
 
     dtype = p.dtype
     achieved = flop_per_step / (fwd_avg * 1e-3) / 1e12
@@ -396,7 +394,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": kernel_name, "kernel_avg_ms": round(fwd_avg, 5),
-                     "kernel_median_ms": round(fwd_ms[len(fwd_ms) // 2], 5)},
+                     "map_build_avg_ms": round(map_avg, 5)},
     }
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a bounded sample ...")
