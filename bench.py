@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
 
 A step is one pass of the whole path over one batch of synthetic input already
-resident in HBM: the block-map build (when the mask needs one) followed by the
-forward pass, both on the current stream.  `value` is attention TFLOP/s over the
+resident in HBM: the block-map build (document masks and packed batches; causal and
+window masks have their block lists derived inside the forward kernel) followed by
+the forward pass, both on the current stream.  The map build is also timed on its own.  `value` is attention TFLOP/s over the
 unmasked FLOPs, 4*d*H*(visible (q, k) pairs) per step, divided by the step time: the
 host clock around K steps launched back to back, synchronised on both sides.  The
 kernels' average durations (the roofline figures) come from a second pass that launches
@@ -346,20 +347,23 @@ def main(argv=None):
     flop_per_step = 4.0 * p.d * p.H * pairs
     stream = torch.cuda.current_stream()
 
+    # A step builds the block map where the forward pass needs one (document masks, packed
+    # batches); causal and window masks go without, their block lists derived in the kernel.
+    map_in_step = WD.needs_map(dp)
     for _ in range(args.warmup):
-        WD.step(dp, args.tau)
+        WD.step(dp, args.tau, use_map=False)
     torch.cuda.synchronize()
 
     # The timed region: K whole steps back to back with nothing else on the stream.
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        WD.step(dp, args.tau)
+        WD.step(dp, args.tau, use_map=False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = wall * 1e3 / args.steps
     # Average launch duration of each kernel: K launches of it back to back on the same
     # stream, one event pair around them (events between launches would add their own gaps).
-    fwd_avg = loop_ms(torch, stream, args.steps, lambda: WD.forward(dp, args.tau))
+    fwd_avg = loop_ms(torch, stream, args.steps, lambda: WD.forward(dp, args.tau, use_map=False))
     map_avg = loop_ms(torch, stream, args.steps, lambda: WD.build_map(dp)) if dp.blockmap is not None else 0.0
     log(f"bench: step {step_ms:.4f} ms (wall), forward kernel avg {fwd_avg:.4f} ms, block map build avg "
         f"{map_avg:.4f} ms (back-to-back launches)")
@@ -390,7 +394,9 @@ def main(argv=None):
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": name, "B": p.B, "H": p.H, "N": p.N, "d": p.d, "visible_pairs": pairs,
                    "unmasked_flop_per_step": flop_per_step, "rescale_tau": args.tau,
-                   "step": "block-map build + forward pass", "parallelism": "single GPU"},
+                   "step": "block-map build + forward pass" if map_in_step else
+                           ("forward pass (block lists derived from the mask in the kernel)" if dp.blockmap is not None
+                            else "forward pass"), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": kernel_name, "kernel_avg_ms": round(fwd_avg, 5),

@@ -236,8 +236,13 @@ attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, voi
     if (fp8->qk_mode != ATTN_QK_BF16 && fp8->qk_mode != ATTN_QK_E4M3) return ATTN_ERR_UNSUPPORTED;
   }
   if (positional(mask)) {
-    if (!blockmap || !aligned16(blockmap)) return ATTN_ERR_BAD_BLOCKMAP;
-    if (blockmap_bytes != map_layout(B, N).total) return ATTN_ERR_BAD_BLOCKMAP;
+    // Causal and window masks may come without a map (the bf16-path kernel derives the
+    // block lists from the flags); a document mask, and Q.K^T on the e4m3 MFMA, need one.
+    const bool need = (mask->flags & ATTN_DOCUMENT) || (dtype == ATTN_FP8_E4M3 && fp8->qk_mode == ATTN_QK_E4M3);
+    if (blockmap || need) {
+      if (!blockmap || !aligned16(blockmap)) return ATTN_ERR_BAD_BLOCKMAP;
+      if (blockmap_bytes != map_layout(B, N).total) return ATTN_ERR_BAD_BLOCKMAP;
+    }
   }
   return ATTN_OK;
 }
@@ -395,6 +400,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
   attn_status st = attn_check_args_gqa(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, H_kv, N, d,
                                        scale, ATTN_BF16, mask, blockmap, blockmap_bytes, nullptr, 8.f);
   if (st != ATTN_OK) return st;
+  if (positional(mask) && !blockmap) return ATTN_ERR_BAD_BLOCKMAP;  // the backward kernels walk the map
   if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(delta) & 3u))

@@ -198,7 +198,40 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
   int kb_first = 0;  // first block of the order (masked: read beside the counts)
   bool invalid = false;
-  if constexpr (MASKED) {
+  // Without a map (causal and window masks, no documents) the lists follow from the
+  // flags.  Every row q sees the keys [lo(q), hi(q)], both ends non-decreasing in q and
+  // q itself inside, so the block's rows r0..r1 together see [lo(r0), hi(r1)] without a
+  // gap: the non-empty key blocks are the range ua..ub; a block is FULL when it lies in
+  // every row's interval, [lo(r1), hi(r0)], and the block has 128 rows; the PARTIAL ones
+  // are the pl blocks left of the FULL range and those right of it.  In the block order
+  // (PARTIAL ascending, then FULL ascending) entry j is block map_entry(j).
+  const bool derive = MASKED && a.map == nullptr;
+  int ua = 0, fa = 0, fb = -1, pl = 0;
+  auto map_entry = [&](int j) -> int {
+    return j < pl ? ua + j : (j < npart ? fb + 1 + (j - pl) : fa + (j - npart));
+  };
+  if (MASKED && derive) {
+    const int W = a.window;
+    const uint32_t mf = a.mflags;
+    auto lo_of = [&](int q) { return (mf & kWindow) ? max(0, q - (W - 1)) : 0; };
+    auto hi_of = [&](int q) {
+      return (mf & kCausal) ? q : ((mf & kWindow) ? min(N - 1, q + (W - 1)) : N - 1);
+    };
+    const int r0 = q0, r1 = min(N, q0 + 128) - 1;
+    ua = lo_of(r0) >> 7;
+    const int ub = hi_of(r1) >> 7;
+    fa = max(ua, (lo_of(r1) + 127) >> 7);
+    fb = min(ub, ((hi_of(r0) + 1) >> 7) - 1);
+    if (r1 - r0 != 127 || fa > fb) { fa = ub + 1; fb = ub; }  // no FULL block
+    nfull = fb - fa + 1;
+    npart = ub - ua + 1 - nfull;
+    pl = fa - ua;
+    if (qvalid) {
+      lo_q = lo_of(qrow);
+      hi_q = hi_of(qrow);
+    }
+    kb_first = map_entry(0);
+  } else if constexpr (MASKED) {
     const __attribute__((address_space(4))) MapHeader* hd =
         (const __attribute__((address_space(4))) MapHeader*)a.map;
     invalid = hd->magic != kMapMagic || hd->B != a.B || hd->N != N || hd->flags != a.mflags ||
@@ -245,7 +278,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     for (int r = 0; r < NKV; ++r) {
       const int j = 64 * r + lane;
       int kb = 0;
-      if (j < nblk) kb = j < npart ? plist[j] : flist[j - npart];
+      if (j < nblk) kb = derive ? map_entry(j) : (j < npart ? plist[j] : flist[j - npart]);
       kbv[r] = min(max(kb, 0), nqb - 1);  // a corrupted map never addresses outside the head
     }
   }
@@ -261,7 +294,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
         // (the empty asm keeps the compiler from hoisting this rare scalar load, and its
         // wait, above the branch into every step)
         asm volatile("" ::: "memory");
-        kb = blk < npart ? plist[blk] : flist[blk - npart];
+        kb = derive ? map_entry(blk) : (blk < npart ? plist[blk] : flist[blk - npart]);
         kb = min(max(kb, 0), nqb - 1);
       }
     } else {
@@ -959,11 +992,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 }
 
 // Launches the variant (masked, mode, generic modifiers) chosen on the host; a
-// masked variant is never launched without a block map.
+// document mask is never launched without a block map (causal and window masks may
+// come without one: the kernel derives their lists).
 template <int D, bool FP8>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st) {
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
-  if (masked && a.map == nullptr) return hipErrorInvalidValue;
+  if (masked && a.map == nullptr && (a.mflags & kDocument)) return hipErrorInvalidValue;
   if (FP8 && (!a.q_scale || !a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
   if (masked) {
     if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kLinear, false, false>), grid, block, 0, st, a);

@@ -189,8 +189,13 @@ attn_status attn_check_args(const void* q, const void* k, const void* v, void* o
  *   scale        : > 0 and finite (typically 1/sqrt(d)).
  *   dtype        : ATTN_BF16 or ATTN_FP8_E4M3 (then `fp8` is required).
  *   mask         : NULL for plain attention.
- *   blockmap     : built by attn_blockmap_build for the same (B, N, mask); required
- *                  iff the mask has CAUSAL, WINDOW or DOCUMENT; otherwise ignored.
+ *   blockmap     : built by attn_blockmap_build for the same (B, N, mask).  Required
+ *                  with DOCUMENT (and with fp8 qk_mode ATTN_QK_E4M3 under any
+ *                  CAUSAL/WINDOW mask).  With CAUSAL and/or WINDOW alone it may be
+ *                  NULL: every row then sees one interval of keys whose ends grow with
+ *                  the row, and the kernel derives the same block lists and row
+ *                  intervals from the flags (bit-identical results, no map launch).
+ *                  Ignored without a positional mask.
  *   rescale_tau  : online-softmax rescale threshold in log2 units, 0 <= tau <= 8:
  *                  the running maximum used as the exponent offset is replaced only
  *                  when a row's maximum exceeds it by more than tau.  The result

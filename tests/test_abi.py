@@ -86,10 +86,17 @@ def test_check_args_ok_and_errors(L):
     assert ck(mask=L.make_mask(L.ATTN_ALIBI | L.ATTN_SOFTCAP, softcap=30.0)) == L.ATTN_OK
     assert ck(mask=L.make_mask(L.ATTN_SOFTCAP, softcap=0.0)) == L.ATTN_ERR_INVALID_ARG
     assert ck(mask=L.make_mask(L.ATTN_SOFTCAP, softcap=float("inf"))) == L.ATTN_ERR_INVALID_ARG
-    # positional masks need a block map of exactly the right size
+    # a block map, when given, must have exactly the right size; causal and window masks
+    # may come without one, document masks (and e4m3 Q.K^T) may not
     m = L.make_mask(L.ATTN_CAUSAL)
     nbytes = L.attn_blockmap_bytes(2, 300, m)
-    assert ck(mask=m) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert ck(mask=m) == L.ATTN_OK
+    assert ck(mask=L.make_mask(L.ATTN_CAUSAL | L.ATTN_WINDOW, window=5)) == L.ATTN_OK
+    assert ck(mask=L.make_mask(L.ATTN_DOCUMENT | L.ATTN_CAUSAL, doc_id=P)) == L.ATTN_ERR_BAD_BLOCKMAP
+    f8 = L.make_fp8(P, P, P, qk_mode=L.ATTN_QK_E4M3)
+    assert ck(mask=m, dtype=1, fp8=f8) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert ck(mask=m, dtype=1, fp8=f8, blockmap=P, blockmap_bytes=nbytes) == L.ATTN_OK
+    assert ck(mask=m, dtype=1, fp8=L.make_fp8(P, P, P)) == L.ATTN_OK
     assert ck(mask=m, blockmap=P, blockmap_bytes=nbytes - 1) == L.ATTN_ERR_BAD_BLOCKMAP
     assert ck(mask=m, blockmap=P, blockmap_bytes=nbytes) == L.ATTN_OK
     assert ck(mask=L.make_mask(L.ATTN_WINDOW | L.ATTN_CAUSAL, window=0), blockmap=P,

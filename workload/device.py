@@ -73,20 +73,31 @@ def build_map(dp: DeviceProblem, stream=None) -> None:
         L.attn_blockmap_build(dp.p.B, dp.p.N, dp.mask, dp.blockmap, stream)
 
 
-def forward(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None) -> None:
+def needs_map(dp: DeviceProblem) -> bool:
+    """Whether the forward pass needs a block map: document masks and packed batches do;
+    causal and window masks on the bf16 path derive their block lists in the kernel."""
+    qk8 = dp.fp8 is not None and dp.fp8.qk_mode == L.ATTN_QK_E4M3
+    return dp.blockmap is not None and (dp.cu_seqlens is not None or bool(dp.p.flags & L.ATTN_DOCUMENT) or qk8)
+
+
+def forward(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None, use_map: bool = True) -> None:
+    """The forward pass; use_map=False leaves the block map out where the mask allows."""
     if dp.cu_seqlens is not None:
         L.attn_fwd_varlen(dp.q[0], dp.k[0], dp.v[0], dp.o[0], dp.lse[0], scale=dp.p.scale, workspace=dp.blockmap,
                           dtype=dp.dtype, mask=dp.mask, fp8=dp.fp8, rescale_tau=rescale_tau, stream=stream)
         return
     fwd = L.attn_fwd if dp.p.Hkv == dp.p.H else L.attn_fwd_gqa
     fwd(dp.q, dp.k, dp.v, dp.o, dp.lse, scale=dp.p.scale, dtype=dp.dtype, mask=dp.mask,
-        blockmap=dp.blockmap, fp8=dp.fp8, rescale_tau=rescale_tau, stream=stream)
+        blockmap=dp.blockmap if (use_map or needs_map(dp)) else None, fp8=dp.fp8, rescale_tau=rescale_tau,
+        stream=stream)
 
 
-def step(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None) -> None:
-    """One pass of the whole path: block map (if the mask needs one), then the forward pass."""
-    build_map(dp, stream)
-    forward(dp, rescale_tau, stream)
+def step(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None, use_map: bool = True) -> None:
+    """One pass of the whole path: block map (if the mask needs one), then the forward pass.
+    use_map=False builds and passes the map only where the forward pass needs it."""
+    if use_map or needs_map(dp):
+        build_map(dp, stream)
+    forward(dp, rescale_tau, stream, use_map)
 
 
 def outputs(dp: DeviceProblem):
