@@ -474,7 +474,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   float ct = a.c, sc2 = a.sc2, ctp = a.c, sc2p = a.sc2;
   // fp8: V block scale of the current step over the head's largest (log2 and inverse)
   float lvs = 0.f, ivs = 1.f;
-  float sq = 1.f, vs_max = 1.f;
+  float sq = 1.f, vs_max = 1.f, lvs_max = 0.f;
   typedef const __attribute__((address_space(4))) float cfloat;
   cfloat* const ksc = FP8 ? (cfloat*)a.k_scale + (size_t)bkv * nqb : nullptr;
   cfloat* const vsc = FP8 ? (cfloat*)a.v_scale + (size_t)bkv * nqb : nullptr;
@@ -485,6 +485,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
     vs_max = mx > 0.f ? mx : 1.f;
+    lvs_max = __builtin_amdgcn_logf(vs_max);
   }
   // the multipliers of the step whose first key is k0 (for the maximum / the exponentials)
   auto scales_p = [&](int k0) {
@@ -499,9 +500,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       const float f = sq * ksc[k0 >> 7];
       ct = a.c * f;
       sc2 = a.sc2 * f;
-      const float vr = vsc[k0 >> 7] / vs_max;
-      lvs = __builtin_amdgcn_logf(vr);  // log2
-      ivs = 1.f / vr;
+      // log2(vs_kb / vs_max) and vs_max / vs_kb without divisions (per step, per lane: the
+      // hardware reciprocal's 1-ulp error only scales this step's share of the LSE sum)
+      const float vk = vsc[k0 >> 7];
+      lvs = __builtin_amdgcn_logf(vk) - lvs_max;
+      ivs = vs_max * __builtin_amdgcn_rcpf(vk);
     }
   };
   const float ninf = -__builtin_inff();
