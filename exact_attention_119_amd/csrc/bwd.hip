@@ -60,7 +60,16 @@ struct BwdArgs {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int PADB = 16;  // LDS row padding (bytes)
+// LDS tiles: rows of 2D bytes, 16-byte chunk ch of row r stored at chunk position
+// ch ^ lds_swz(r).  The tiles are read two ways: row fragments (16 lanes: 16 consecutive
+// rows, one chunk) and transposed fragments (32 lanes: 4 consecutive rows, 4 consecutive
+// chunks); lds_swz spreads both over 16 different 16-byte slots of a 256-byte line (d =
+// 64: two rows per line), and the tile writes (8 lanes: 8 chunks of one row) over 8.  It
+// depends on the row's low 4 bits only, so per-lane offsets survive 16-row steps.
+template <int D>
+__device__ __forceinline__ constexpr int lds_swz(int r) {
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -84,26 +93,31 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ constexpr int acc_row(int r) { return 8 * (r >> 2) + (r & 3); }
 
 // A fragment of a row-major tile (stride STR): row r0 + l32, 8 values at column 16c + 8hh
+// (rsw = lds_swz(l32); r0 is a multiple of 32)
 template <int STR>
-__device__ __forceinline__ bf16x8 row_frag(const lds_u8* t, int r0, int l32, int hh, int c) {
-  return *(const lds_bf16x8*)(t + (r0 + l32) * STR + 32 * c + 16 * hh);
+__device__ __forceinline__ bf16x8 row_frag(const lds_u8* t, int r0, int l32, int hh, int c, int rsw) {
+  return *(const lds_bf16x8*)(t + (r0 + l32) * STR + (((2 * c + hh) ^ rsw) << 4));
 }
 // A fragment of the transpose of a row-major tile: columns 32db .. 32db+31 as rows, the
 // 16 tile rows 16ks .. 16ks+15 as k, in the order 4hh+e, 8+4hh+e (e = 0..3) that the
 // accumulator registers 8g .. 8g+7 carry; off = this lane's offset for block db.
 template <int STR>
-__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* t, int ks, int off) {
-  const lds_u8* base = t + ks * 16 * STR + off;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * STR));
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* t, int ks, int2 off) {
+  const lds_u8* base = t + ks * 16 * STR;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off.x));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off.y));
   const short __attribute__((ext_vector_type(8))) w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, w);
 }
-template <int STR>
-__device__ __forceinline__ int tr_off(int lane, int db) {
+// this lane's offsets (rows 4hh + e and 8 + 4hh + e of a 16-row group) for block db
+template <int D>
+__device__ __forceinline__ int2 tr_off(int lane, int db) {
+  constexpr int STR = 2 * D;
   const int e = (lane & 15) >> 2, aa = lane & 3, dh = (lane >> 4) & 1, hh = lane >> 5;
   const int chunk = 4 * db + 2 * dh + (aa >> 1);
-  return (4 * hh + e) * STR + chunk * 16 + (aa & 1) * 8;
+  const int r = 4 * hh + e;
+  return make_int2(r * STR + ((chunk ^ lds_swz<D>(r)) << 4) + (aa & 1) * 8,
+                   (r + 8) * STR + ((chunk ^ lds_swz<D>(r + 8)) << 4) + (aa & 1) * 8);
 }
 
 // score, and its derivative in the raw dot product, of one (q, k) element (the modifiers
@@ -168,7 +182,7 @@ __global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
 // ---- dQ ----------------------------------------------------------------------------------
 template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
 __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
-  constexpr int ROWB = 2 * D, STR = ROWB + PADB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
+  constexpr int ROWB = 2 * D, STR = ROWB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
   constexpr int BN = 64;
   __shared__ __attribute__((aligned(16))) unsigned char k_sh[BN * STR];
   __shared__ __attribute__((aligned(16))) unsigned char v_sh[BN * STR];
@@ -212,9 +226,10 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
       hi_q = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
     }
   }
-  int troff[NDB];
+  int2 troff[NDB];
+  const int rsw = lds_swz<D>(l32);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) troff[db] = tr_off<STR>(lane, db);
+  for (int db = 0; db < NDB; ++db) troff[db] = tr_off<D>(lane, db);
 
   f32x16 dacc[NDB];
 #pragma unroll
@@ -254,8 +269,8 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
-      *(uint4*)(k_sh + r * STR + c * 16) = pk[j];
-      *(uint4*)(v_sh + r * STR + c * 16) = pv[j];
+      *(uint4*)(k_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pk[j];
+      *(uint4*)(v_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pv[j];
     }
     __syncthreads();
     if (st_ + 1 < nsteps) fetch(step_k0(st_ + 1));
@@ -267,8 +282,8 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
         dp[bk] = f32x16{};
 #pragma unroll
         for (int c = 0; c < NQC; ++c) {
-          st[bk] = mfma(row_frag<STR>(kt, 32 * bk, l32, hh, c), qf[c], st[bk]);
-          dp[bk] = mfma(row_frag<STR>(vt, 32 * bk, l32, hh, c), gf[c], dp[bk]);
+          st[bk] = mfma(row_frag<STR>(kt, 32 * bk, l32, hh, c, rsw), qf[c], st[bk]);
+          dp[bk] = mfma(row_frag<STR>(vt, 32 * bk, l32, hh, c, rsw), gf[c], dp[bk]);
         }
       }
 #pragma unroll
@@ -307,7 +322,7 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
 // ---- dK, dV ------------------------------------------------------------------------------
 template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
 __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
-  constexpr int ROWB = 2 * D, STR = ROWB + PADB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
+  constexpr int ROWB = 2 * D, STR = ROWB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
   constexpr int BM = 64;  // query rows per step
   constexpr int NBQ = BM / 32;
   __shared__ __attribute__((aligned(16))) unsigned char q_sh[BM * STR];
@@ -336,9 +351,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   }
   bool invalid = false;
   if constexpr (MASKED) invalid = map_invalid(a, b);
-  int troff[NDB];
+  int2 troff[NDB];
+  const int rsw = lds_swz<D>(l32);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) troff[db] = tr_off<STR>(lane, db);
+  for (int db = 0; db < NDB; ++db) troff[db] = tr_off<D>(lane, db);
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -412,8 +428,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
-      *(uint4*)(q_sh + r * STR + c * 16) = pq[j];
-      *(uint4*)(g_sh + r * STR + c * 16) = pg[j];
+      *(uint4*)(q_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pq[j];
+      *(uint4*)(g_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pg[j];
     }
     if (tid < BM) {
       lse_s[tid] = p_lse;
@@ -432,8 +448,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
       dp[bq] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NQC; ++c) {
-        s[bq] = mfma(row_frag<STR>(qt, 32 * bq, l32, hh, c), kf[c], s[bq]);
-        dp[bq] = mfma(row_frag<STR>(gt, 32 * bq, l32, hh, c), vf[c], dp[bq]);
+        s[bq] = mfma(row_frag<STR>(qt, 32 * bq, l32, hh, c, rsw), kf[c], s[bq]);
+        dp[bq] = mfma(row_frag<STR>(gt, 32 * bq, l32, hh, c, rsw), vf[c], dp[bq]);
       }
     }
 #pragma unroll
