@@ -205,6 +205,7 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
     gf[c] = qvalid ? *(const bf16x8*)(a.dout + qoff + 16 * c + 8 * hh) : bf16x8{};
   }
   const float lse2 = qvalid ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float sl2 = a.scale * kLog2e;
   const float dl = qvalid ? a.delta[(size_t)bh * N + qrow] : 0.f;
   const float slope = ALIBI ? head_slope(a, h) : 0.f;
 
@@ -286,16 +287,29 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
           dp[bk] = mfma(row_frag<STR>(vt, 32 * bk, l32, hh, c, rsw), gf[c], dp[bk]);
         }
       }
+      // dR = P (dP - D) ds/dr; without softcap ds/dr is the scale, applied to dQ at the end.
+      // A FULL block (and every step without a positional mask: keys past N are zero rows
+      // of K and V, so they add nothing to dQ) needs no mask.
+      auto elementwise = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
+        for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * bk + 4 * hh + acc_row(r);
-          float s, dsdr;
-          score<SOFTCAP, ALIBI>(a, st[bk][r], qrow, key, slope, s, dsdr);
-          const float p = prob(key >= lo_q && key <= hi_q, s, lse2);
-          st[bk][r] = p * (dp[bk][r] - dl) * dsdr;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * bk + 4 * hh + acc_row(r);
+            float p, dsdr = 1.f;
+            if constexpr (!SOFTCAP && !ALIBI && !MASK) {
+              p = exp2_(__builtin_fmaf(st[bk][r], sl2, -lse2));
+            } else {
+              float s;
+              score<SOFTCAP, ALIBI>(a, st[bk][r], qrow, key, slope, s, dsdr);
+              p = MASK ? prob(key >= lo_q && key <= hi_q, s, lse2) : exp2_(s * kLog2e - lse2);
+            }
+            st[bk][r] = SOFTCAP ? p * (dp[bk][r] - dl) * dsdr : p * (dp[bk][r] - dl);
+          }
+      };
+      if (!MASKED || st_ >= 2 * npart) elementwise(std::false_type{});
+      else elementwise(std::true_type{});
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 bop = pack8(st[ks >> 1], ks & 1);
@@ -307,6 +321,10 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
   if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
   bf16* dst = a.dq + qoff;
+  if constexpr (!SOFTCAP) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dacc[db] *= a.scale;
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -363,6 +381,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     dvacc[db] = f32x16{};
   }
   cu8* cls = MASKED ? (cu8*)(a.map + a.lay.cls) + (size_t)b * nqb * nqb + kb : nullptr;
+  const float sl2 = a.scale * kLog2e;
   // Steps: (query head of the group, non-empty query block, 32-row sub-block), in that
   // nesting.  next() advances a step state; the next step's rows and per-row values are
   // loaded into registers while the current step computes.
@@ -452,29 +471,47 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
         dp[bq] = mfma(row_frag<STR>(gt, 32 * bq, l32, hh, c, rsw), vf[c], dp[bq]);
       }
     }
-#pragma unroll
-    for (int bq = 0; bq < NBQ; ++bq) {
-      f32x16 pm, dr;
+    // P and dR = P (dP - D) ds/dr of 32 query rows (without softcap ds/dr is the scale,
+    // applied to dK at the end).  A FULL block (and every step without a positional mask:
+    // rows past N are zero rows of Q and dO, so they add nothing) needs no mask.
+    const bool full = !MASKED || cls[(size_t)qb * nqb] == 2;
+    auto elementwise = [&](auto mask_tag, int bq, f32x16& pm, f32x16& dr) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // rows 32bq + 4hh + 8j .. +3 of the step: one 16-byte LDS read per per-row array
         const int q4 = 32 * bq + 4 * hh + 8 * j;
         const float4 l4 = *(const float4*)&lse_s[q4];
         const float4 d4 = *(const float4*)&dl_s[q4];
-        const int4 lo4 = *(const int4*)&lo_s[q4];
-        const int4 hi4 = *(const int4*)&hi_s[q4];
         const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
-        const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+        int los[4] = {0, 0, 0, 0}, his[4] = {0, 0, 0, 0};
+        if constexpr (MASK) {
+          const int4 lo4 = *(const int4*)&lo_s[q4];
+          const int4 hi4 = *(const int4*)&hi_s[q4];
+          los[0] = lo4.x; los[1] = lo4.y; los[2] = lo4.z; los[3] = lo4.w;
+          his[0] = hi4.x; his[1] = hi4.y; his[2] = hi4.z; his[3] = hi4.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
-          float sv, dsdr;
-          score<SOFTCAP, ALIBI>(a, s[bq][r], q0 + q4 + e, key, slope, sv, dsdr);
-          const float p = prob(key >= los[e] && key <= his[e], sv, ls[e]);
+          float p, dsdr = 1.f;
+          if constexpr (!SOFTCAP && !ALIBI && !MASK) {
+            p = exp2_(__builtin_fmaf(s[bq][r], sl2, -ls[e]));
+          } else {
+            float sv;
+            score<SOFTCAP, ALIBI>(a, s[bq][r], q0 + q4 + e, key, slope, sv, dsdr);
+            p = MASK ? prob(key >= los[e] && key <= his[e], sv, ls[e]) : exp2_(sv * kLog2e - ls[e]);
+          }
           pm[r] = p;
-          dr[r] = p * (dp[bq][r] - ds[e]) * dsdr;
+          dr[r] = SOFTCAP ? p * (dp[bq][r] - ds[e]) * dsdr : p * (dp[bq][r] - ds[e]);
         }
       }
+    };
+#pragma unroll
+    for (int bq = 0; bq < NBQ; ++bq) {
+      f32x16 pm, dr;
+      if (full) elementwise(std::false_type{}, bq, pm, dr);
+      else elementwise(std::true_type{}, bq, pm, dr);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const bf16x8 pb = pack8(pm, g), rb = pack8(dr, g);
@@ -492,6 +529,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   }
   if (!kvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
+  if constexpr (!SOFTCAP) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dkacc[db] *= a.scale;
+  }
   bf16* dk = a.dk + koff;
   bf16* dv = a.dv + koff;
 #pragma unroll
