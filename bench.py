@@ -120,9 +120,18 @@ def cpu_baseline(p, budget_s: float):
     dt = time.perf_counter() - t0
     pairs_per_head = visible_pairs(p) / p.B
     flops = 4.0 * p.d * pairs_per_head * n
+    dense = 4.0 * p.d * p.N * p.N * n  # the oracle forms every score of a row, masked or not
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {len(heads_all)} (b,h) heads, all {p.N} query rows, fp64 numpy, "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall",
+            "cpu_model": cpu, "wall_s": round(dt, 3),
+            "dense_tflops": round(dense / dt / 1e12, 6)}
 
 
 def loop_ms(torch, stream, n: int, launch) -> float:
