@@ -158,6 +158,13 @@ __device__ bool map_invalid(const BwdArgs& a, int b) {
   return __syncthreads_or(st) != 0 || bad;
 }
 
+// One 16-byte chunk per lane from base + voffset (bytes; reads past `bytes` give zero)
+// into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load_lds16(const unsigned char* base, int bytes, lds_u8* lds, int voffset) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
 // ---- D = rowsum(dO * O) ------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
@@ -181,13 +188,14 @@ __global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
 
 // ---- dQ ----------------------------------------------------------------------------------
 template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
-__global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   constexpr int ROWB = 2 * D, STR = ROWB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
   constexpr int BN = 64;
-  __shared__ __attribute__((aligned(16))) unsigned char k_sh[BN * STR];
-  __shared__ __attribute__((aligned(16))) unsigned char v_sh[BN * STR];
-  const lds_u8* kt = (const lds_u8*)k_sh;
-  const lds_u8* vt = (const lds_u8*)v_sh;
+  constexpr int TILE = BN * STR, LPW = TILE / 1024 / 4, RPL = 1024 / ROWB;  // 1 KiB direct loads
+  // K and V tiles, double-buffered: step s reads buffer s % 2 while the tiles of step s+1
+  // arrive in the other one straight from HBM
+  __shared__ __attribute__((aligned(1024))) unsigned char k_sh[2][TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_sh[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int N = a.N, nqb = a.nqb;
@@ -197,6 +205,26 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
   const int qrow = qb * 128 + wave * 32 + l32;
   const bool qvalid = qrow < N;
   const size_t qoff = ((size_t)bh * N + (qvalid ? qrow : 0)) * D;
+  // direct HBM -> LDS loads: load r of this wave fills LDS bytes 1024 (wave LPW + r) +
+  // 16 lane, i.e. row ld RPL + lane / CPR at chunk position lane % CPR, which holds the
+  // row's chunk (position ^ lds_swz(row)); the buffer descriptor of a step starts at its
+  // first key and ends at N, so rows past N read as zero
+  int ldoff[LPW];
+#pragma unroll
+  for (int r = 0; r < LPW; ++r) {
+    const int row = (wave * LPW + r) * RPL + lane / CPR, pc = lane % CPR;
+    ldoff[r] = row * ROWB + ((pc ^ lds_swz<D>(row)) << 4);
+  }
+  const unsigned char* const kbase = (const unsigned char*)a.k + (size_t)bkv * N * ROWB;
+  const unsigned char* const vbase = (const unsigned char*)a.v + (size_t)bkv * N * ROWB;
+  auto issue = [&](int k0, int buf) {
+    const int bytes = max(N - k0, 0) * ROWB;
+#pragma unroll
+    for (int r = 0; r < LPW; ++r) {
+      load_lds16(kbase + (size_t)k0 * ROWB, bytes, (lds_u8*)k_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      load_lds16(vbase + (size_t)k0 * ROWB, bytes, (lds_u8*)v_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+    }
+  };
 
   bf16x8 qf[NQC], gf[NQC];
 #pragma unroll
@@ -236,10 +264,8 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dacc[db] = f32x16{};
 
-  // Steps s = 0 .. 2*nblk-1 (64 keys each).  The tiles of step s+1 are loaded into
-  // registers while step s computes, and written to LDS between two barriers.
-  constexpr int PF = BN * CPR / 256;  // 16-byte chunks per thread per tile
-  uint4 pk[PF], pv[PF];
+  // Steps s = 0 .. 2*nblk-1 (64 keys each).  The tiles of step s+1 are requested into the
+  // other LDS buffer as step s starts; one barrier per step.
   auto step_k0 = [&](int st_) -> int {
     int kb = st_ >> 1;
     if constexpr (MASKED) {
@@ -248,33 +274,17 @@ __global__ void __launch_bounds__(256) dq_kernel(const BwdArgs a) {
     }
     return kb * 128 + (st_ & 1) * BN;
   };
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
-      const int key = k0 + r;
-      pk[j] = make_uint4(0u, 0u, 0u, 0u);
-      pv[j] = pk[j];
-      if (key < N) {
-        const size_t off = ((size_t)bkv * N + key) * D + c * 8;
-        pk[j] = *(const uint4*)(a.k + off);
-        pv[j] = *(const uint4*)(a.v + off);
-      }
-    }
-  };
   const int nsteps = 2 * nblk;
-  if (nsteps > 0) fetch(step_k0(0));
+  if (nsteps > 0) issue(step_k0(0), 0);
   for (int st_ = 0; st_ < nsteps; ++st_) {
     const int k0 = step_k0(st_);
-    __syncthreads();  // the previous step's reads are done
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
-      *(uint4*)(k_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pk[j];
-      *(uint4*)(v_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pv[j];
-    }
+    // this wave's loads of step st_ have landed; after the barrier every wave's have, and
+    // every wave is done reading the buffer the next loads go to (step st_ - 1)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (st_ + 1 < nsteps) fetch(step_k0(st_ + 1));
+    if (st_ + 1 < nsteps) issue(step_k0(st_ + 1), (st_ + 1) & 1);
+    const lds_u8* kt = (const lds_u8*)k_sh[st_ & 1];
+    const lds_u8* vt = (const lds_u8*)v_sh[st_ & 1];
     {
       f32x16 st[2], dp[2];
 #pragma unroll
