@@ -11,7 +11,7 @@ import oracle
 import workload as W
 from workload import device as WD
 from exact_attention_119_amd import lib as L
-from _parity import assert_close
+from _parity import assert_close, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,10 +84,15 @@ def test_derived_lists_gqa():
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_derived_lists_full_size(cfg):
     """The benchmarked configurations (causal; causal + window 1024 + softcap 50) at full
-    size: the derived-list run is bit-identical to the map run over every output."""
+    size, in the launch the benchmark times (no map): bit-identical to the map run over every
+    output, and equal to the oracle on sampled rows of every head."""
     p = W.config_problem(cfg)
     _announce("derived full size", cfg)
-    _both(p)
+    o, lse = _both(p)
+    rows = sample_rows(p.N, 24, seed=100 + cfg)
+    heads = [(b, h) for b in range(p.B) for h in range(p.H)]
+    o_ref, lse_ref = oracle.attention_problem(p, rows=rows, heads=heads, workers=8)
+    assert_close(p, o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, f"derived cfg{cfg} sampled")
 
 
 def test_document_mask_still_needs_the_map():
