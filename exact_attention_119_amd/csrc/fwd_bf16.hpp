@@ -145,7 +145,7 @@ __host__ __device__ constexpr int key_off(int bk, int r) { return 32 * bk + 8 * 
 //           the bf16 MFMA, P.V on the fp16 MFMA with P rounded to fp16, in units of
 //           vs_kb / vs_max (the key block's V scale over the head's largest), so that
 //           P <= 2^tau stays inside fp16 whatever the scales; O is multiplied back by
-//           vs_max and normalised by the sum of P as rounded.
+//           vs_max and normalised by the fp32 row sum (fp16 P is within 2^-11 of it).
 //   MASKED  positional mask through the block map (else: all keys visible)
 //   MODE    score-modifier mode (kLinear, kSoftcap, kAlibiCausal, kGeneric)
 //   GALIBI, GSOFTCAP  modifiers of the generic mode
@@ -515,8 +515,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_used = ninf;
   float l_sum = 0.f;   // row sum of p (fp32, before rounding): LSE; for bf16 also the normaliser of O
-  float lq_sum = 0.f;  // fp8: row sum of p as rounded to fp16, the normaliser of O
-  const f16x2 ones_h = {(f16)1.0f, (f16)1.0f};
 
   // ---- score modifiers, mask and row maximum ---------------------------------------------
   // Score of one accumulator element before the maximum is taken (kq = k0 + 4hh - q):
@@ -623,31 +621,30 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     else if constexpr (MODE == kSoftcap) return exp2_(__builtin_fmaf(-2.f * cap2, sv, cap2 - moff));
     else return exp2_(sv - moff);
   };
-  auto p_pack = [&](float p0, float p1, float& ls, float& lqs) -> uint32_t {
+  auto p_pack = [&](float p0, float p1, float& ls) -> uint32_t {
     ls += p0 + p1;
     if constexpr (FP8) {
       const f32x2 v = {p0, p1};
       const f16x2 pb = __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even
-      lqs = __builtin_amdgcn_fdot2(pb, ones_h, lqs, false);
       return __builtin_bit_cast(uint32_t, pb);
     } else {
       return __builtin_bit_cast(uint32_t, to_bf16x2(p0, p1));
     }
   };
   // all three stages of one pair (RAW: softcap scores untransformed)
-  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls, float& lqs) -> uint32_t {
+  auto ppair = [&](auto raw_tag, float s0, float s1, float moff, float& ls) -> uint32_t {
     constexpr bool RAW = decltype(raw_tag)::value;
     if constexpr (MODE == kSoftcap && RAW) {
       s0 = p_pre(s0);
       s1 = p_pre(s1);
     }
-    return p_pack(p_exp(s0, moff), p_exp(s1, moff), ls, lqs);
+    return p_pack(p_exp(s0, moff), p_exp(s1, moff), ls);
   };
   // P of one 16-key slice (registers 8g..8g+7 of block bk) as the bf16 B operand
-  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls, float& lqs) -> bf16x8 {
+  auto pslice = [&](auto raw_tag, const f32x16& sacc, int g, float moff, float& ls) -> bf16x8 {
     uint32_t pk[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls, lqs);
+    for (int t = 0; t < 4; ++t) pk[t] = ppair(raw_tag, sacc[g * 8 + 2 * t], sacc[g * 8 + 2 * t + 1], moff, ls);
     const u32x4 v4 = {pk[0], pk[1], pk[2], pk[3]};
     return __builtin_bit_cast(bf16x8, v4);
   };
@@ -666,7 +663,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       const float alpha = need ? exp2_(m_used - m_new) : 1.f;
       m_used = need ? m_new : m_used;
       l_sum *= alpha;
-      lq_sum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     }
@@ -705,16 +701,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto pv_sched = [&](auto raw_tag, const lds_u8* vt, const f32x16 (&sacc)[2], float moff, float& ls, float& lqs) {
+  auto pv_sched = [&](auto raw_tag, const lds_u8* vt, const f32x16 (&sacc)[2], float moff, float& ls) {
     bf16x8 fr[PD + 1], pf[4];
     static_for<PD>([&](auto ic) { fr[ic.value] = vfrag(vt, ic.value / NDB, ic.value % NDB); });
-    pf[0] = pslice(raw_tag, sacc[0], 0, moff, ls, lqs);
+    pf[0] = pslice(raw_tag, sacc[0], 0, moff, ls);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NP>([&](auto jc) {
       constexpr int j = decltype(jc)::value, ks = j / NDB, db = j % NDB;
       if constexpr (j + PD < NP) fr[(j + PD) % (PD + 1)] = vfrag(vt, (j + PD) / NDB, (j + PD) % NDB);
       oacc[db] = pv_mma(fr[j % (PD + 1)], pf[ks], oacc[db]);
-      if constexpr (db == 0 && ks + 1 < 4) pf[ks + 1] = pslice(raw_tag, sacc[(ks + 1) >> 1], (ks + 1) & 1, moff, ls, lqs);
+      if constexpr (db == 0 && ks + 1 < 4) pf[ks + 1] = pslice(raw_tag, sacc[(ks + 1) >> 1], (ks + 1) & 1, moff, ls);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -785,10 +781,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     scales_e(k0);
     qk_sched(kc, sa);
     const float moff = rescale(prepare(YES, NO, sa, k0), k0);
-    float ls = 0.f, lqs = 0.f;
-    pv_sched(NO, vc, sa, moff, ls, lqs);
+    float ls = 0.f;
+    pv_sched(NO, vc, sa, moff, ls);
     l_sum += FP8 ? ls * ivs : ls;
-    lq_sum += lqs * ivs;
   }
 
   // ---- phase 2: FULL blocks, software-pipelined ---------------------------------------------
@@ -853,7 +848,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       moff = rescale(mcur, step_k0(s));
     };
 
-    float ls = 0.f, lqs = 0.f;
+    float ls = 0.f;
     if constexpr (NEXT) {
       const int k1 = step_k0(s + 1);
       const int kq1 = k1 + 4 * hh - qrow;
@@ -915,7 +910,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
             pin(pv1[k]);
           }
           if constexpr (a + NSTG - 1 == i) {
-            pk[k] = p_pack(pv0[k], pv1[k], ls, lqs);
+            pk[k] = p_pack(pv0[k], pv1[k], ls);
             pin(pk[k]);
             pin(ls);
           }
@@ -937,11 +932,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     } else {
       loads_and_rescale();
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls, lqs);
+      for (int sl = 0; sl < 4; ++sl) pf[sl] = pslice(YES, scur[sl >> 1], sl & 1, moff, ls);
       pv_full(vcur, pf);
     }
     l_sum += FP8 ? ls * ivs : ls;
-    lq_sum += lqs * ivs;
   };
 
   if (np_steps < nsteps) {
@@ -970,10 +964,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
   // ---- epilogue -------------------------------------------------------------------------
   l_sum = pair_sum(l_sum);
-  if constexpr (FP8) lq_sum = pair_sum(lq_sum);
   if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
-  const float onorm = FP8 ? lq_sum : l_sum;
+  const float onorm = l_sum;
   const float inv = invalid ? nanv : (onorm > 0.f ? (FP8 ? vs_max : 1.f) / onorm : 0.f);
   bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
 #pragma unroll
