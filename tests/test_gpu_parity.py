@@ -214,3 +214,29 @@ def test_fp8_block_scales_spread(d, variant):
         _announce("fp8 spread scales", variant, d, tau)
         _, o, lse = _run(p, tau=tau)
         assert_close(p, o, lse, o_ref, lse_ref, f"fp8 spread scales {variant} d={d} tau={tau}")
+
+
+def test_work_order_beyond_one_chunk():
+    """Document masks with 1152 (batch row, query block) entries: the order kernel streams
+    the work values through LDS in chunks of 1024, so the second chunk is exercised.  The
+    order equals its definition on the device's counts, the counts equal the oracle's, and
+    the forward pass that takes its row blocks in that order writes every output and
+    matches the oracle on sampled rows."""
+    p = W.make_problem(9, 2, 16384, 64, flags=C | DOC, seed=77, doc_len_range=(300, 5000))
+    _announce("work order, 1152 entries")
+    dp, o, lse = _run(p)
+    got = L.read_blockmap(dp.blockmap, p.B, p.N)
+    np.testing.assert_array_equal(got["order"], oracle.blockmap.work_order_ref(got["counts"], p.flags))
+    assert len(set(got["order"].tolist())) == p.B * 128
+    for b in (0, 8):
+        ref = oracle.blockmap_ref(1, p.N, p.flags & L.POSITIONAL, 0, p.doc_id[b:b + 1])
+        np.testing.assert_array_equal(got["counts"][b], ref["counts"][0], err_msg=f"counts of batch row {b}")
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    rows = sample_rows(p.N, 12, seed=77)
+    heads = [(b, h) for b in (0, 4, 8) for h in range(p.H)]
+    o_ref, lse_ref = oracle.attention_problem(p, rows=rows, heads=heads, workers=8)
+    sel_o = np.stack([o[b, h][rows] for b, h in heads]).reshape(3, p.H, len(rows), p.d)
+    sel_l = np.stack([lse[b, h][rows] for b, h in heads]).reshape(3, p.H, len(rows))
+    ref_o = np.stack([o_ref[b, h] for b, h in heads]).reshape(3, p.H, len(rows), p.d)
+    ref_l = np.stack([lse_ref[b, h] for b, h in heads]).reshape(3, p.H, len(rows))
+    assert_close(p, sel_o, sel_l, ref_o, ref_l, "work order beyond one chunk")
