@@ -166,16 +166,18 @@ __device__ __forceinline__ void load_lds16(const unsigned char* base, int bytes,
 }
 
 // ---- D = rowsum(dO * O) ------------------------------------------------------------------
+// D/8 lanes per row, 16 bytes of O and of dO each (coalesced rows), summed across the
+// row's lanes with shuffles (the groups are aligned, so the xor offsets stay inside them).
 template <int D>
 __global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
-  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= (size_t)a.B * a.H * a.N) return;
-  const uint4* o = (const uint4*)(a.o + row * D);
-  const uint4* g = (const uint4*)(a.dout + row * D);
+  constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per workgroup
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const uint4 x = o[c], y = g[c];
+  if (row < rows) {
+    const uint4 x = ((const uint4*)(a.o + row * D))[part];
+    const uint4 y = ((const uint4*)(a.dout + row * D))[part];
     const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -183,7 +185,9 @@ __global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
       acc = __builtin_fmaf(__uint_as_float(xs[t] & 0xFFFF0000u), __uint_as_float(ys[t] & 0xFFFF0000u), acc);
     }
   }
-  a.delta[row] = acc;
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) a.delta[row] = acc;
 }
 
 // ---- dQ ----------------------------------------------------------------------------------
@@ -577,7 +581,8 @@ void launch_m(const BwdArgs& a, hipStream_t st) {
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool masked, hipStream_t st) {
   const size_t rows = (size_t)a.B * a.H * a.N;
-  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a);
   if (masked) launch_m<D, true>(a, st);
   else launch_m<D, false>(a, st);
   return hipGetLastError();
