@@ -307,10 +307,14 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
     a.window = (flags & ATTN_WINDOW) ? mask->window : 0;
   }
   // Causal masks give the last row blocks of a head the most key blocks.  When the grid
-  // is only a few workgroups per slot (2 per CU on 256 CUs), take them heaviest-first.
+  // is only a few workgroups per slot (2 per CU on 256 CUs), take them heaviest-first; with
+  // grouped key/value heads (no window) always: that order also runs all query heads of a
+  // group on one XCD at once, sharing their K/V in its L2 (measured 4-12% faster on four
+  // grouped-query shapes; for ungrouped heads at larger grids it was not faster).
   constexpr long kSlots = 2 * 256;
   const long items = (long)B * H * a.nqb;
-  a.order = ((flags & ATTN_CAUSAL) && items < 4 * kSlots) ? kOrderHeavyFirst : kOrderHeadMajor;
+  const bool grouped = H_kv < H && !(flags & ATTN_WINDOW);
+  a.order = ((flags & ATTN_CAUSAL) && (items < 4 * kSlots || grouped)) ? kOrderHeavyFirst : kOrderHeadMajor;
   // Under a document mask a row block's work depends on its place in its document: take
   // the heaviest-first order the map builder derived from the block lists.
   if (masked && (flags & ATTN_DOCUMENT)) a.order = kOrderMapSorted;
