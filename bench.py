@@ -1,23 +1,31 @@
 """Benchmark of the fused attention forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu]
 
 A step is one pass of the whole path over one batch of synthetic input already
 resident in HBM: the block-map build (document masks and packed batches; causal and
 window masks have their block lists derived inside the forward kernel) followed by
-the forward pass, both on the current stream.  The map build is also timed on its own.  `value` is attention TFLOP/s over the
+the forward pass, both on the current stream.  `value` is attention TFLOP/s over the
 unmasked FLOPs, 4*d*H*(visible (q, k) pairs) per step, divided by the step time: the
-host clock around K steps launched back to back, synchronised on both sides.  The
-kernels' average durations (the roofline figures) come from a second pass that launches
-each kernel K times back to back between one pair of HIP events.
+host clock around K steps launched back to back, synchronised on both sides.
 
-Default workload: B=4 H=16 N=2048 d=128, causal, bf16 (configuration 2).  Other
---config values are the other synthetic workloads (1: B1 H2 N256 d64 plain;
-3: B2 H32 N8192 d128 causal+window 1024+softcap 50; 4: B1 H16 N16384 d128
-document-causal+ALiBi; 5: B1 H16 N16384 d128 fp8 plain), --plain-causal the
-configuration-3 shape with a plain causal mask, and --shape B,H,N,d [--mask causal] any
-other bf16 shape (--kv-heads H_kv for grouped-query attention), --varlen a packed batch of
-causal sequences of different lengths.
+Warm-up: at least W steps and at least --warmup-s seconds (default 3), so that the
+engine clock has settled at the board's power limit before the timed steps.  The K
+timed steps are split into up to 5 windows by HIP events recorded on the stream
+between them (one event per window, none inside a step): the median and minimum of
+the per-window step times are reported beside the host-clock mean.  When a step is
+the forward kernel alone, the kernel's time is that window's (so it can never exceed
+the step time); otherwise the forward kernel is timed the same way in a second run
+of K launches right after.  The engine clock is sampled (amdsmi) through the last
+second of warm-up and the timed steps.
+
+Default workload: B=2 H=32 N=8192 d=128 bf16, causal + sliding window of 1024 keys
++ tanh soft-cap 50 (configuration 3).  Other --config values are the other synthetic
+workloads (1: B1 H2 N256 d64 plain; 2: B4 H16 N2048 d128 causal; 4: B1 H16 N16384
+d128 document-causal+ALiBi; 5: B1 H16 N16384 d128 fp8 plain), --plain-causal the
+configuration-3 shape with a plain causal mask, and --shape B,H,N,d [--mask causal]
+any other bf16 shape (--kv-heads H_kv for grouped-query attention), --varlen a packed
+batch of causal sequences of different lengths.
 
 Printed on stdout: ONE JSON line.  Extra diagnostics go to stderr.
 """
@@ -55,6 +63,23 @@ def kernel_source_hash(files=None) -> str:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def arithmetic_dtype(dp) -> str:
+    """The types the MFMAs compute in: bf16; for e4m3 inputs the codes are widened for
+    Q.K^T (bf16) and P.V (fp16), or Q.K^T runs on the e4m3 MFMA (qk8)."""
+    if dp.fp8 is None:
+        return "bf16"
+    from exact_attention_119_amd import lib as L
+    qk = "e4m3" if dp.fp8.qk_mode == L.ATTN_QK_E4M3 else "bf16"
+    pv = "e4m3" if dp.fp8.pv_mode == L.ATTN_PV_E4M3 else "f16"
+    return f"{qk} QK^T + {pv} PV (e4m3 inputs)"
 
 
 def workload_name(p) -> str:
@@ -107,7 +132,7 @@ def cpu_baseline(p, budget_s: float):
     import numpy as np
     import oracle
     from oracle.attention import available_cores
-    cores = min(available_cores(), 16)
+    cores = min(available_cores(), 16)  # the host CPUs one GPU's share of the box holds
     heads_all = [(b, h) for b in range(p.B) for h in range(p.H)]
     t0 = time.perf_counter()
     oracle.attention_problem(p, heads=heads_all[:1], workers=1)
@@ -132,6 +157,109 @@ def cpu_baseline(p, budget_s: float):
                       f"{dt:.1f} s wall",
             "cpu_model": cpu, "wall_s": round(dt, 3),
             "dense_tflops": round(dense / dt / 1e12, 6)}
+
+
+def timed_windows(torch, stream, steps: int, launch, nwin: int = 5):
+    """Times `steps` calls of `launch` back to back: the host clock around all of them
+    (synchronised on both sides) and HIP events on `stream` at the boundaries of up to
+    `nwin` windows.  Returns (host ms per call, [event ms per call of each window])."""
+    nwin = max(1, min(nwin, steps))
+    bounds = [round(i * steps / nwin) for i in range(nwin + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for w in range(nwin):
+        for _ in range(bounds[w + 1] - bounds[w]):
+            launch()
+        ev[w + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[w].elapsed_time(ev[w + 1]) / (bounds[w + 1] - bounds[w]) for w in range(nwin)]
+    return wall * 1e3 / steps, per
+
+
+def warm_up(torch, launch, min_steps: int, min_seconds: float):
+    """At least min_steps calls and at least min_seconds of them (the queue is drained
+    every 32 calls so the host does not run far ahead of the GPU)."""
+    n, t0 = 0, time.perf_counter()
+    while n < min_steps or time.perf_counter() - t0 < min_seconds:
+        launch()
+        n += 1
+        if n % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+class ClockSampler:
+    """Samples the GPU's engine (gfx) clock through amdsmi in a background thread,
+    every `period` seconds, between start() and stop().  Reports nothing where amdsmi or
+    the metric is unavailable."""
+
+    def __init__(self, period: float = 0.05):
+        import threading
+        self.period, self.samples, self.source = period, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                return
+            h = handles[0]
+
+            def read_clock_info():
+                return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+
+            def read_metrics():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                v = m.get("current_gfxclks") or m.get("current_gfxclk")
+                if isinstance(v, (list, tuple)):
+                    v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+                    return float(sum(v) / len(v)) if v else None
+                return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
+
+            for name, fn in (("amdsmi gpu_metrics current_gfxclk", read_metrics),
+                             ("amdsmi clock_info gfx", read_clock_info)):
+                try:
+                    if fn() is not None:
+                        self._read, self.source = fn, name
+                        break
+                except Exception:  # noqa: BLE001 - any failure means: not available
+                    continue
+        except Exception:  # noqa: BLE001
+            self._read = None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append((time.perf_counter(), v))
+            except Exception:  # noqa: BLE001
+                pass
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self, since: float):
+        v = sorted(x for t, x in self.samples if t >= since)
+        if not v:
+            return None
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "source": self.source, "peak_mhz": 2400}
 
 
 def loop_ms(torch, stream, n: int, launch) -> float:
@@ -308,7 +436,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--warmup-s", type=float, default=3.0,
+                    help="minimum seconds of warm-up steps (the engine clock settles at the power limit)")
     ap.add_argument("--plain-causal", action="store_true", help="configuration-3 shape, plain causal mask")
     ap.add_argument("--shape", type=str, default=None,
                     help="supplementary bf16 workload B,H,N,d (with --mask, --kv-heads), instead of a "
@@ -382,30 +512,44 @@ def main(argv=None):
     # A step builds the block map where the forward pass needs one (document masks, packed
     # batches); causal and window masks go without, their block lists derived in the kernel.
     map_in_step = WD.needs_map(dp)
-    for _ in range(args.warmup):
-        WD.step(dp, args.tau, use_map=False)
-    torch.cuda.synchronize()
 
-    # The timed region: K whole steps back to back with nothing else on the stream.
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    def one_step():
         WD.step(dp, args.tau, use_map=False)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = wall * 1e3 / args.steps
-    # Average launch duration of each kernel: K launches of it back to back on the same
-    # stream, one event pair around them (events between launches would add their own gaps).
-    fwd_avg = loop_ms(torch, stream, args.steps, lambda: WD.forward(dp, args.tau, use_map=False))
-    if fwd_avg < 0.05:  # short kernel: the loop above measures the host's launch rate
-        eager = fwd_avg
-        fwd_avg = graph_loop_ms(torch, stream, args.steps, lambda: WD.forward(dp, args.tau, use_map=False))
-        log(f"bench: forward kernel avg {eager:.4f} ms launched from the host, {fwd_avg:.4f} ms from a graph")
+
+    def one_forward():
+        WD.forward(dp, args.tau, use_map=False)
+
+    clock = ClockSampler()
+    clock.start()
+    nwarm, twarm = warm_up(torch, one_step, args.warmup, args.warmup_s)
+    t_settled = time.perf_counter() - min(1.0, twarm)
+
+    # The timed region: K whole steps back to back with nothing else on the stream (one
+    # event between windows, none inside a step).
+    step_ms, step_win = timed_windows(torch, stream, args.steps, one_step)
+    if map_in_step:
+        # the forward kernel alone, K launches right after, timed the same way
+        _, fwd_win = timed_windows(torch, stream, args.steps, one_forward)
+    else:
+        fwd_win = step_win  # the step is the forward kernel: its own window
+    clock.stop()
+    fwd_med, fwd_min = median(fwd_win), min(fwd_win)
+    graph_note = None
+    if fwd_med < 0.05:  # short kernel: the windows above measure the host's launch rate
+        graph_note = fwd_med
+        fwd_med = fwd_min = graph_loop_ms(torch, stream, args.steps, one_forward)
+        log(f"bench: forward kernel {graph_note:.4f} ms launched from the host, {fwd_med:.4f} ms from a graph")
     map_avg = loop_ms(torch, stream, args.steps, lambda: WD.build_map(dp)) if dp.blockmap is not None else 0.0
-    log(f"bench: step {step_ms:.4f} ms (wall), forward kernel avg {fwd_avg:.4f} ms, block map build avg "
-        f"{map_avg:.4f} ms (back-to-back launches)")
+    consistent = fwd_med <= step_ms
+    log(f"bench: warm-up {nwarm} steps in {twarm:.2f} s; step {step_ms:.4f} ms (host clock, mean of {args.steps}), "
+        f"windows median {median(step_win):.4f} min {min(step_win):.4f} ms; forward kernel median {fwd_med:.4f} "
+        f"min {fwd_min:.4f} ms; block map build avg {map_avg:.4f} ms")
+    if not consistent:
+        log("bench: WARNING the forward kernel's median exceeds the step time (it was timed in its own run; "
+            "the clock differed)")
 
     dtype = p.dtype
-    achieved = flop_per_step / (fwd_avg * 1e-3) / 1e12
+    achieved = flop_per_step / (fwd_med * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
     traffic = traffic_record(name)
     from exact_attention_119_amd import lib as L
@@ -413,7 +557,7 @@ def main(argv=None):
     eb = 1 if dtype == "fp8" else 2
     alg_bytes = p.B * p.N * (p.H * (p.d * (eb + 2) + 4) + p.Hkv * 2 * p.d * eb)
     log(f"bench: algorithmic HBM bytes per launch {alg_bytes}; at the forward kernel's time that is "
-        f"{alg_bytes / (fwd_avg * 1e-3) / 1e9:.1f} GB/s of {HBM_PEAK_GBS:.0f}")
+        f"{alg_bytes / (fwd_med * 1e-3) / 1e9:.1f} GB/s of {HBM_PEAK_GBS:.0f}")
 
     out = {
         "metric": METRIC,
@@ -426,21 +570,31 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": arithmetic_dtype(dp),
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": name, "B": p.B, "H": p.H, "N": p.N, "d": p.d, "visible_pairs": pairs,
-                   "unmasked_flop_per_step": flop_per_step, "rescale_tau": args.tau,
+                   "unmasked_flop_per_step": flop_per_step, "rescale_tau": args.tau, "input_dtype": dtype,
                    "step": "block-map build + forward pass" if map_in_step else
                            ("forward pass (block lists derived from the mask in the kernel)" if dp.blockmap is not None
-                            else "forward pass"), "parallelism": "single GPU"},
+                            else "forward pass"), "parallelism": "single GPU",
+                   "warmup_run": {"steps": nwarm, "seconds": round(twarm, 3)},
+                   "step_ms_windows": {"median": round(median(step_win), 5), "min": round(min(step_win), 5),
+                                       "windows": len(step_win)},
+                   "engine_clock": clock.summary(t_settled)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel_name, "kernel_avg_ms": round(fwd_avg, 5),
-                     "map_build_avg_ms": round(map_avg, 5)},
+                     "kernel": kernel_name, "kernel_avg_ms": round(fwd_med, 5), "kernel_min_ms": round(fwd_min, 5),
+                     "kernel_timing": ("HIP events: median over the timed windows of the step, which is this "
+                                       "kernel alone" if not map_in_step else
+                                       "HIP events: median over windows of K forward launches after the timed steps"),
+                     "kernel_le_step": consistent, "map_build_avg_ms": round(map_avg, 5)},
     }
+    if dtype == "fp8":
+        out["roofline"]["note"] = ("fp8 peak; Q.K^T on the bf16 MFMA and P.V on the fp16 MFMA (both half the fp8 "
+                                   "rate) unless the kernel name says fp8-qk8")
     # Below the ridge (peak flop/s over 8 TB/s) the kernel's roofline is HBM bandwidth.
     if flop_per_step / alg_bytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9):
-        gbs = alg_bytes / (fwd_avg * 1e-3) / 1e9
+        gbs = alg_bytes / (fwd_med * 1e-3) / 1e9
         out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs / HBM_PEAK_GBS, 5), "achieved_tflops": round(achieved, 3),
                                 "algorithmic_bytes": alg_bytes})

@@ -66,13 +66,15 @@ FwdVariant select_variant(int32_t d, int32_t dtype, const attn_mask* mask, const
   return v;
 }
 
-const char* variant_name(const FwdVariant& v) {
-  static const char* const kIn[] = {"bf16", "fp8", "fp8-qk8"};
-  static const char* const kMode[] = {"linear", "softcap", "alibi-causal", "generic-alibi", "generic-alibi-softcap"};
-  static const char* const kMods[] = {"none", "softcap", "alibi", "alibi+softcap"};
-  static char names[2][3][2][5][64];
-  static bool init = false;
-  if (!init) {  // (filled once; every entry is a pure function of its indices)
+// Table of variant names, built once.  A function-local static is initialised exactly
+// once even under concurrent first calls (C++11), so every caller sees it complete.
+struct VariantNames {
+  char names[2][3][2][5][64];
+  VariantNames() {
+    static const char* const kIn[] = {"bf16", "fp8", "fp8-qk8"};
+    static const char* const kMode[] = {"linear", "softcap", "alibi-causal", "generic-alibi",
+                                        "generic-alibi-softcap"};
+    static const char* const kMods[] = {"none", "softcap", "alibi", "alibi+softcap"};
     for (int di = 0; di < 2; ++di)
       for (int in = 0; in < 3; ++in)
         for (int m = 0; m < 2; ++m)
@@ -81,8 +83,12 @@ const char* variant_name(const FwdVariant& v) {
             std::snprintf(names[di][in][m][k], 64, "%s d%d %s %s", kIn[in], di ? 128 : 64,
                           m ? "masked" : "unmasked", tail);
           }
-    init = true;
   }
+};
+
+const char* variant_name(const FwdVariant& v) {
+  static const VariantNames table;
+  const auto& names = table.names;
   int k;
   if (v.input != kInFp8Qk8) k = v.mode == bf16path::kGeneric ? (v.softcap ? 4 : 3) : v.mode;
   else k = (v.alibi ? 2 : 0) + (v.softcap ? 1 : 0);
@@ -308,12 +314,17 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   }
   // Causal masks give the last row blocks of a head the most key blocks.  When the grid
   // is only a few workgroups per slot (2 per CU on 256 CUs), take them heaviest-first; with
-  // grouped key/value heads (no window) always: that order also runs all query heads of a
-  // group on one XCD at once, sharing their K/V in its L2 (measured 4-12% faster on four
-  // grouped-query shapes; for ungrouped heads at larger grids it was not faster).
+  // grouped key/value heads (no window) also when each group stays on one XCD: that order
+  // then runs all query heads of a group there at once, sharing their K/V in its L2
+  // (measured 4-12% faster on four grouped-query shapes; for ungrouped heads at larger
+  // grids it was not faster).
   constexpr long kSlots = 2 * 256;
   const long items = (long)B * H * a.nqb;
-  const bool grouped = H_kv < H && !(flags & ATTN_WINDOW);
+  // (the heaviest-first order keeps a group's query heads on one XCD only when the 8
+  // XCDs take equal runs of B*H/8 consecutive heads and a group never straddles two runs)
+  const long bh = (long)B * H;
+  const bool group_on_xcd = bh % 8 == 0 && (bh / 8) % (H / H_kv) == 0;
+  const bool grouped = H_kv < H && !(flags & ATTN_WINDOW) && group_on_xcd;
   a.order = ((flags & ATTN_CAUSAL) && (items < 4 * kSlots || grouped)) ? kOrderHeavyFirst : kOrderHeadMajor;
   // Under a document mask a row block's work depends on its place in its document: take
   // the heaviest-first order the map builder derived from the block lists.

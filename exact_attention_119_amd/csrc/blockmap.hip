@@ -232,7 +232,9 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
     hd->nkb = nb;
     hd->flags = a.flags;
     hd->window = a.window;
-    for (int i = 0; i < 9; ++i) hd->reserved[i] = 0;
+    hd->order_full_cost = kOrderFullCost;
+    hd->order_partial_cost = kOrderPartialCost;
+    for (int i = 0; i < 7; ++i) hd->reserved[i] = 0;
   }
   if (tid == 0) {
     int32_t* counts = (int32_t*)(a.map + a.lay.counts) + ((size_t)b * nb + qb) * 2;

@@ -65,7 +65,8 @@ struct MapHeader {
   int32_t B, N, nqb, nkb;
   uint32_t flags;
   int32_t window;
-  int32_t reserved[9];
+  int32_t order_full_cost, order_partial_cost;  // weights of the work order (kOrder*Cost)
+  int32_t reserved[7];
 };
 
 }  // namespace attn119

@@ -12,12 +12,15 @@
 //   widen bf16 -> fp32, flipping the signs on the way (an XOR of the bf16 sign bits);
 //   with rotation run the fast Walsh-Hadamard transform, strides 1, 2, ..., d/2;
 //   block maximum of |y| (wave shuffles, then LDS across the four waves);
-//   s = amax / 448 and g = 448 / amax (both 1 for an all-zero block), code = e4m3(y * g)
-//   by v_cvt_pk_fp8_f32 (round to nearest even, subnormal codes kept, the sign of zero
-//   kept, nothing above 448 reachable since |y * g| <= 448 up to one rounding; the
-//   parity tests compare every code with the oracle's table-based rounding), written
-//   as 16-byte chunks; the stored scale is s (times 1/sqrt(d) with rotation, so that
-//   code * scale approximates x R).
+//   s = amax / 448 and g = 448 / amax (both 1 for an all-zero block); the code is the
+//   e4m3 value nearest to y / s, ties to even: y * g is within three fp32 ulps of y / s,
+//   and where an e4m3 tie lies that close the sign of the exact residual y - t s (one
+//   fma) moves it to the tie's correct side first (without rotation y is the input
+//   itself, so the codes are those of the exact quotient); then v_cvt_pk_fp8_f32
+//   (round to nearest even, subnormal codes kept, the sign of zero kept, nothing above
+//   448 reachable since |y * g| <= 448 up to one rounding), written as 16-byte chunks;
+//   the stored scale is s (times 1/sqrt(d) with rotation, so that code * scale
+//   approximates x R; 1 for an all-zero block).
 // HBM-bound: 2 bytes read and 1 written per element.
 #include <algorithm>
 
@@ -36,6 +39,26 @@ struct QuantArgs {
   uint32_t sign_bits[4];  // element j negated when bit j%32 of word j/32 is set (zero
                           // without rotation)
 };
+
+// y * g (g = fp32(448 / amax), s = fp32(amax / 448)) as the value to round to e4m3, placed
+// on the same side of every e4m3 tie as the exact quotient y / s: the product lies within
+// three fp32 ulps of y / s, so only the midpoint t of the e4m3 interval holding it can lie
+// between the two; when it is that close, the exact residual |y| - t s (one fma: its sign
+// is exact) decides -- t itself when the quotient is the tie, else t moved one ulp towards
+// the quotient.
+__device__ __forceinline__ float e4m3_quotient(float y, float g, float s) {
+  const float q = y * g;
+  const float aq = __builtin_fabsf(q);
+  // midpoint of the e4m3 interval of |q|: normal range (>= 2^-6): the exponent and top
+  // three mantissa bits of |q| followed by a one; subnormal range: (k + 1/2) 2^-9
+  const float t = aq >= 0x1p-6f ? __uint_as_float((__float_as_uint(aq) & 0xFFF00000u) | 0x80000u)
+                                : ((float)(int)(aq * 512.f) + 0.5f) * 0x1p-9f;
+  const int dist = (int)__float_as_uint(aq) - (int)__float_as_uint(t);
+  if (dist > 4 || dist < -4) return q;
+  const float r = __builtin_fmaf(-t, s, __builtin_fabsf(y));
+  const float at = r == 0.f ? t : __uint_as_float(__float_as_uint(t) + (r > 0.f ? 1u : 0xFFFFFFFFu));
+  return __builtin_copysignf(at, y);
+}
 
 // Lane layout: four lanes per row; lane k (0..3) of a row holds the 16-byte chunks
 // q = 4c + k, c = 0 .. D/32 - 1, i.e. elements e = 8q + i.  Element bits 0-2 and 5-6 are
@@ -164,15 +187,18 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
       unsigned char* dst = a.codes + ((size_t)bh * a.N + row) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[p][c][0] * g, v[p][c][1] * g, 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[p][c][2] * g, v[p][c][3] * g, lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[p][c][4] * g, v[p][c][5] * g, 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[p][c][6] * g, v[p][c][7] * g, hi, true);
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = e4m3_quotient(v[p][c][i], g, sc);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[0], w[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[2], w[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(w[4], w[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(w[6], w[7], hi, true);
         *(uint2*)(dst + 8 * (4 * c + k)) = make_uint2((uint32_t)lo, (uint32_t)hi);
       }
     }
   }
-  if (tid == 0) a.scales[wg] = a.rotate ? sc * a.rnorm : sc;
+  if (tid == 0) a.scales[wg] = (a.rotate && amax > 0.f) ? sc * a.rnorm : sc;  // an all-zero block: 1
 }
 
 hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N, int d, const uint32_t* signs,

@@ -298,7 +298,8 @@ def read_blockmap(blockmap, B: int, N: int) -> dict:
         return raw[lay[name]:lay[name] + n].view(dtype).reshape(shape)
 
     return dict(header=dict(magic=int(hdr.view(np.uint32)[0]), B=int(hdr[1]), N=int(hdr[2]), nqb=int(hdr[3]),
-                            nkb=int(hdr[4]), flags=int(hdr.view(np.uint32)[5]), window=int(hdr[6])),
+                            nkb=int(hdr[4]), flags=int(hdr.view(np.uint32)[5]), window=int(hdr[6]),
+                            order_full_cost=int(hdr[7]), order_partial_cost=int(hdr[8])),
                 cls=sec("cls", np.uint8, (B, nb, nb)), counts=sec("counts", np.int32, (B, nb, 2)),
                 idx=sec("idx", np.int32, (B, nb, 2, nb)), row_lo=sec("row_lo", np.int32, (B, N)),
                 row_hi=sec("row_hi", np.int32, (B, N)), pairs=sec("pairs", np.int64, (B, nb)),

@@ -137,18 +137,22 @@ typedef struct attn_fp8 {
  *                                       the next row (packed batches: or the share of the
  *                                       sequence offsets this block checks is out of order),
  *                                       else 0 (a batch row with any 1 is invalid)
- *   order    : int32  [B * nqb]         work order of the forward pass (scheduling only; it
- *                                       never changes a result): with ATTN_DOCUMENT the
- *                                       entries e = b * nqb + qb sorted by decreasing work
- *                                       2 * #FULL + 5 * #PARTIAL, equal work in increasing e;
- *                                       without it the identity 0 .. B*nqb-1
+ *   order    : int32  [B * nqb]         work order of the forward pass (this library's
+ *                                       scheduling choice; it never changes a result): with
+ *                                       ATTN_DOCUMENT the entries e = b * nqb + qb sorted by
+ *                                       decreasing work order_full_cost * #FULL +
+ *                                       order_partial_cost * #PARTIAL (weights in the
+ *                                       header), equal work in increasing e; without it the
+ *                                       identity 0 .. B*nqb-1
  */
 typedef struct attn_blockmap_header {
   uint32_t magic; /* 0x39313141 */
   int32_t B, N, nqb, nkb;
   uint32_t flags; /* mask flags restricted to CAUSAL|WINDOW|DOCUMENT */
   int32_t window;
-  int32_t reserved[9];
+  int32_t order_full_cost;    /* work of a FULL key block in the work order */
+  int32_t order_partial_cost; /* work of a PARTIAL key block in the work order */
+  int32_t reserved[7];
 } attn_blockmap_header;
 
 typedef struct attn_blockmap_layout {
@@ -272,10 +276,15 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
  *   y = x, or with rotate_signs: y = (x * signs) H, H the Sylvester Walsh-Hadamard
  *       matrix of order d, computed in fp32 by the fast transform (strides 1, 2, ...,
  *       d/2), signs[j] = -1 when bit j % 32 of rotate_signs[j / 32] is set, else +1;
- *   s = fp32(max|y| / 448) and g = fp32(448 / max|y|), both 1 for an all-zero block;
- *   codes = OCP e4m3fn of fp32(y * g), round to nearest even, saturated at +-448;
- *   scales[b][h][block] = s, or with rotation fp32(s * fp32(1/sqrt(d))), so that
- *       code * scale approximates x R with R = D H / sqrt(d) orthogonal.
+ *   s = fp32(max|y| / 448), 1 for an all-zero block;
+ *   codes = the OCP e4m3fn value nearest to y / s, ties to even, saturated at +-448
+ *       (computed as fp32(y * fp32(448 / max|y|)), with every e4m3 tie that product
+ *       comes close to resolved from the exact residual: without rotation the codes
+ *       are exactly those of x / s);
+ *   scales[b][h][block] = s, or with rotation fp32(s * fp32(1/sqrt(d))) (1 for an
+ *       all-zero block), so that code * scale approximates x R with R = D H / sqrt(d)
+ *       orthogonal; the fp32 transform rounds, so rotated codes can differ from those of
+ *       the exact x R by one step where y / s lies within that rounding of a tie.
  * Give Q and K the same signs (and V none) to keep Q.K^T and the output unchanged.
  *   x      : device bf16 [B][H][N][d];  codes: device uint8 [B][H][N][d];
  *   scales : device fp32 [B][H][ceil(N/128)];  d = 64 or 128;

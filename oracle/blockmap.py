@@ -17,10 +17,10 @@ visibility predicate, evaluated for every (query, key) position:
   qb_pairs[b][qb] = visible (q, k) pairs of the query rows of block qb
   status[b][qb] = 1 if doc_id[b][q + 1] < doc_id[b][q] for some row q of block qb
       (documents must be contiguous runs; only evaluated with the DOCUMENT flag)
-  order[B * nqb] = the forward pass's work order, a scheduling choice of this library
-      (not from the pages; it never changes a result): with the DOCUMENT flag the
-      entries e = b * nqb + qb by decreasing work 2 * #FULL + 5 * #PARTIAL, equal work
-      by increasing e; otherwise the identity
+
+(The device map also holds a work order of the query blocks; that is the library's
+scheduling choice, not part of the method, so it has no definition here: the tests
+check it as a property of the device's own stated cost.)
 
 The visible-pair count is the number of (b, q, k) with visible(q, k); the
 metric's "unmasked FLOPs" are 4 * H * d times it.
@@ -79,19 +79,8 @@ def blockmap_ref(B: int, N: int, flags: int, window: int = 0, doc_id: Optional[n
             counts[b, qb] = (len(full), len(part))
             idx[b, qb, 0, :len(full)] = full
             idx[b, qb, 1, :len(part)] = part
-    order = work_order_ref(counts, flags)
     return dict(cls=cls, counts=counts, idx=idx, row_lo=row_lo, row_hi=row_hi, pairs=pairs,
-                qb_pairs=qb_pairs, status=status, order=order, visible_pairs=int(pairs.sum()))
-
-
-def work_order_ref(counts: np.ndarray, flags: int) -> np.ndarray:
-    """Work order of the (batch row, query block) entries, see the module doc."""
-    c = np.asarray(counts, dtype=np.int64).reshape(-1, 2)
-    e = np.arange(c.shape[0])
-    if not flags & DOCUMENT:
-        return e.astype(np.int32)
-    work = 2 * c[:, 0] + 5 * c[:, 1]
-    return np.array(sorted(e, key=lambda i: (-work[i], i)), dtype=np.int32)
+                qb_pairs=qb_pairs, status=status, visible_pairs=int(pairs.sum()))
 
 
 def row_intervals_ref(N: int, flags: int, window: int = 0, doc_row=None):

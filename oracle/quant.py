@@ -10,21 +10,19 @@ unchanged and spreads a large channel over all channels.  The orthogonal matrix
 is R = D H / sqrt(d): D a diagonal of random signs (given as input), H the
 Sylvester Walsh-Hadamard matrix of order d.
 
-Steps for one (batch, head, block of 128 rows), in the precision the quantiser
-works in (fp32: the codes are integer decisions, so this side takes them in the
-same precision as the device):
-  1. x: the bf16 rows, widened exactly to fp32; with rotation x <- x * signs.
-  2. with rotation: y = x H by the fast Walsh-Hadamard transform in fp32, stages
-     of stride 1, 2, 4, ..., d/2, each mapping the pair (x[i], x[i+h]) of every
-     2h-aligned group to (x[i] + x[i+h], x[i] - x[i+h]); without: y = x.
-  3. amax = max |y| over the block; s = fp32(amax / 448) and g = fp32(448 / amax),
-     both 1 for an all-zero block.
-  4. code = the e4m3 value nearest to fp32(y * g), ties to the even code,
-     magnitudes above 448 saturated to 448 (a multiplication by the block's inverse
-     scale, the usual form of block quantisation; y * g and y / s can differ in the
-     last fp32 bit, and so, at an e4m3 tie, in the code).
-  5. stored scale: s * fp32(1/sqrt(d)) (fp32 product) with rotation, else s, so
-     that code * scale approximates x R (or x).
+The definition, for one (batch, head, block of 128 rows), in float64 (the
+plain reading of block quantisation: one scale per block, the codes the
+nearest e4m3 values of x / scale):
+  1. x: the bf16 rows, widened exactly; with rotation y = x R (a matrix product
+     in float64), without y = x.
+  2. amax = max |y| over the block; s = amax / 448 rounded to fp32 (the stored
+     scale), 1 for an all-zero block.
+  3. code = the e4m3 value nearest to y / s (float64 quotient), ties to the even
+     code, magnitudes above 448 saturated to 448; the sign is the sign of y.
+So code * s approximates x R (or x).  No evaluation order of the transform is
+part of the definition: an implementation that computes y in lower precision
+can differ from these codes only where y / s lies within its rounding error of
+an e4m3 tie (by one code), and from these scales by its rounding of amax.
 """
 
 from __future__ import annotations
@@ -35,33 +33,32 @@ import numpy as np
 
 from .decode import decode_bf16, decode_e4m3
 
-E4M3_MAX = np.float32(448.0)
+E4M3_MAX = 448.0
 BLOCK = 128
 
 
-def fwht_f32(x: np.ndarray) -> np.ndarray:
-    """Fast Walsh-Hadamard transform along the last axis (length a power of two), in
-    float32, stages of stride 1, 2, ..., d/2 (step 2 above).  Returns x H (Sylvester)."""
-    y = np.array(x, dtype=np.float32, copy=True)
-    d = y.shape[-1]
-    if d & (d - 1):
-        raise ValueError("length must be a power of two")
-    lead = y.shape[:-1]
-    h = 1
-    while h < d:
-        g = y.reshape(*lead, d // (2 * h), 2, h)
-        a, b = g[..., 0, :], g[..., 1, :]
-        y = np.stack([a + b, a - b], axis=-2).reshape(*lead, d)
-        h *= 2
-    return y
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester Walsh-Hadamard matrix of order d (a power of two), float64:
+    H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("order must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
 
 
 def signs_from_bits(bits, d: int) -> np.ndarray:
-    """+-1 float32 [d]: element j is negated when bit j % 32 of word j // 32 is set."""
+    """+-1 float64 [d]: element j is negated when bit j % 32 of word j // 32 is set."""
     words = np.asarray(bits, dtype=np.uint64)
     j = np.arange(d)
     neg = (words[j // 32] >> (j % 32).astype(np.uint64)) & np.uint64(1)
-    return np.where(neg == 1, np.float32(-1.0), np.float32(1.0)).astype(np.float32)
+    return np.where(neg == 1, -1.0, 1.0)
+
+
+def rotation(bits, d: int) -> np.ndarray:
+    """R = D H / sqrt(d), float64 [d][d] (orthogonal)."""
+    return signs_from_bits(bits, d)[:, None] * hadamard(d) / np.sqrt(d)
 
 
 def _e4m3_finite_nonneg() -> Tuple[np.ndarray, np.ndarray]:
@@ -74,39 +71,35 @@ _VALS, _CODES = _e4m3_finite_nonneg()
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
-    """Nearest e4m3 code to each float32 value, ties to the even code (mantissa LSB 0),
-    magnitudes above 448 saturated; the sign bit is the sign bit of v (step 4)."""
-    v = np.asarray(v, dtype=np.float32)
-    a = np.minimum(np.abs(v).astype(np.float64), 448.0)
+    """Nearest e4m3 code to each real value (taken in float64), ties to the even code
+    (mantissa LSB 0), magnitudes above 448 saturated; the sign bit is the sign bit of v."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
     hi = np.clip(np.searchsorted(_VALS, a, side="left"), 0, len(_VALS) - 1)
     lo = np.maximum(hi - 1, 0)
     dlo, dhi = a - _VALS[lo], _VALS[hi] - a
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (_CODES[hi] % 2 == 0))
     code = np.where(pick_hi, _CODES[hi], _CODES[lo]).astype(np.uint8)
-    neg = np.signbit(v)
-    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 def quantize_blocks_ref(x_bits: np.ndarray, sign_bits: Optional[np.ndarray] = None,
                         block: int = BLOCK) -> Tuple[np.ndarray, np.ndarray]:
-    """Codes uint8 [B][H][N][d] and stored scales float32 [B][H][ceil(N/block)] of bf16
-    rows x_bits [B][H][N][d] (bit patterns), with incoherent processing when sign_bits
-    (d/32 words) is given."""
-    x = decode_bf16(x_bits).astype(np.float32)
-    B, H, N, d = x.shape
+    """Codes uint8 [B][H][N][d] and scales float32 [B][H][ceil(N/block)] of bf16 rows
+    x_bits [B][H][N][d] (bit patterns), with incoherent processing when sign_bits (d/32
+    words) is given (steps 1-3 of the module doc)."""
+    y = decode_bf16(x_bits)
+    B, H, N, d = y.shape
     if sign_bits is not None:
-        x = fwht_f32(x * signs_from_bits(sign_bits, d))
+        y = y @ rotation(sign_bits, d)
     nblk = (N + block - 1) // block
-    codes = np.empty(x.shape, dtype=np.uint8)
+    codes = np.empty(y.shape, dtype=np.uint8)
     scales = np.empty((B, H, nblk), dtype=np.float32)
-    rnorm = np.float32(1.0 / np.sqrt(np.float64(d)))
     for j in range(nblk):
         r0, r1 = j * block, min(N, (j + 1) * block)
-        y = x[:, :, r0:r1, :]
-        amax = np.abs(y).max(axis=(2, 3))
-        s = np.where(amax > 0, amax / E4M3_MAX, np.float32(1.0)).astype(np.float32)
-        with np.errstate(divide="ignore"):
-            g = np.where(amax > 0, E4M3_MAX / amax, np.float32(1.0)).astype(np.float32)
-        codes[:, :, r0:r1, :] = e4m3_encode(y * g[:, :, None, None])
-        scales[:, :, j] = (s * rnorm).astype(np.float32) if sign_bits is not None else s
+        blk = y[:, :, r0:r1, :]
+        amax = np.abs(blk).max(axis=(2, 3))
+        s = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+        codes[:, :, r0:r1, :] = e4m3_encode(blk / s.astype(np.float64)[:, :, None, None])
+        scales[:, :, j] = s
     return codes, scales

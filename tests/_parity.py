@@ -54,3 +54,24 @@ def sample_rows(N: int, n: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     extra = rng.choice(N, size=min(N, n), replace=False)
     return np.array(sorted(fixed.union(extra.tolist()).intersection(range(N))), dtype=np.int64)
+
+
+def check_work_order(order, counts, header, document: bool, what: str = "order"):
+    """The block map's work order (the library's scheduling choice, not part of the
+    method) as a property of the device's own stated cost: a permutation of the (batch
+    row, query block) entries; under a document mask the work order_full_cost * #FULL +
+    order_partial_cost * #PARTIAL (weights read from the map header, counts from the
+    map) never increases along it and equal work keeps index order; otherwise the
+    identity."""
+    order = np.asarray(order, dtype=np.int64)
+    M = order.size
+    assert np.array_equal(np.sort(order), np.arange(M)), f"{what}: not a permutation"
+    if not document:
+        assert np.array_equal(order, np.arange(M)), f"{what}: not the identity"
+        return
+    wf, wp = int(header["order_full_cost"]), int(header["order_partial_cost"])
+    assert wf > 0 and wp > 0, f"{what}: no stated cost"
+    c = np.asarray(counts, dtype=np.int64).reshape(-1, 2)
+    w = (wf * c[:, 0] + wp * c[:, 1])[order]
+    ok = (w[:-1] > w[1:]) | ((w[:-1] == w[1:]) & (order[:-1] < order[1:]))
+    assert np.all(ok), f"{what}: work increases along the order at {np.nonzero(~ok)[0][:5]}"

@@ -105,12 +105,31 @@ def test_grouped_heads_bit_identical_to_repeated_heads(variant, dtype):
     np.testing.assert_array_equal(lse, lse_r)
 
 
-def test_grouped_heads_full_size_sampled():
-    """B1 H32 N8192 d128, eight key/value heads, causal: sampled rows of every head."""
-    p = W.make_problem(1, 32, 8192, 128, flags=C, seed=32, H_kv=8)
-    _announce("gqa full size", p.name)
-    _, o, lse = _run_gqa(p)
-    rows = sample_rows(p.N, 24, seed=32)
-    heads = [(0, h) for h in range(p.H)]
+def _run_gqa_derived(p, tau=8.0):
+    """attn_fwd_gqa without a block map: the kernel derives the causal block lists (the
+    route the benchmark and map-less callers take)."""
+    dp = WD.to_device(p)
+    dp.o.fill_(float("nan"))
+    dp.lse.fill_(float("nan"))
+    L.attn_fwd_gqa(dp.q, dp.k, dp.v, dp.o, dp.lse, scale=p.scale, dtype=dp.dtype, mask=dp.mask,
+                   blockmap=None, fp8=dp.fp8, rescale_tau=tau)
+    o, lse = WD.outputs(dp)
+    return dp, o, lse
+
+
+@pytest.mark.parametrize("route", ["map", "derived"])
+@pytest.mark.parametrize("shape", [(1, 32, 8), (1, 16, 2), (3, 12, 4)], ids=lambda t: f"B{t[0]}H{t[1]}kv{t[2]}")
+def test_grouped_heads_full_size_sampled(shape, route):
+    """Causal N8192 d128 with grouped key/value heads: every output written, sampled rows
+    of every head against the oracle.  B1 H32/8 takes the heaviest-first order (a group's
+    heads on one XCD); B1 H16/2 and B3 H12/4 do not meet that order's condition (a group
+    would straddle XCDs) and keep the head-major order."""
+    B, H, Hkv = shape
+    p = W.make_problem(B, H, 8192, 128, flags=C, seed=(32, B, H, Hkv), H_kv=Hkv)
+    _announce("gqa full size", p.name, route)
+    _, o, lse = _run_gqa(p) if route == "map" else _run_gqa_derived(p)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    rows = sample_rows(p.N, 12, seed=32)
+    heads = [(b, h) for b in range(B) for h in range(p.H)]
     o_ref, lse_ref = oracle.attention_problem(p, rows=rows, heads=heads, workers=8)
-    assert_close(p, o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, "gqa full size sampled")
+    assert_close(p, o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, f"gqa full size sampled {p.name} {route}")

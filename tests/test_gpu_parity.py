@@ -9,7 +9,7 @@ import oracle
 import workload as W
 from workload import device as WD
 from exact_attention_119_amd import lib as L
-from _parity import assert_close, errors, sample_rows
+from _parity import assert_close, check_work_order, errors, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -53,12 +53,9 @@ def _check_map(dp, rows=None):
     assert (hd["magic"], hd["B"], hd["N"], hd["flags"], hd["window"]) == \
         (0x39313141, p.B, p.N, p.flags & L.POSITIONAL, p.window if p.flags & L.ATTN_WINDOW else 0)
     np.testing.assert_array_equal(got["status"], ref["status"], err_msg="status")
-    # the work order ranks the counts of every batch row (an invalid row's counts are
-    # unspecified), so it is checked against its definition on the device's counts
-    np.testing.assert_array_equal(got["order"], oracle.blockmap.work_order_ref(got["counts"], p.flags),
-                                  err_msg="order")
-    if rows is None:
-        np.testing.assert_array_equal(got["order"], ref["order"], err_msg="order")
+    # the work order ranks the device's counts of every batch row (an invalid row's
+    # counts are unspecified) by the cost the map states
+    check_work_order(got["order"], got["counts"], hd, bool(p.flags & L.ATTN_DOCUMENT))
     sel = slice(None) if rows is None else rows
     for key in ("cls", "counts", "idx", "row_lo", "row_hi"):
         np.testing.assert_array_equal(got[key][sel], ref[key][sel], err_msg=key)
@@ -219,15 +216,14 @@ def test_fp8_block_scales_spread(d, variant):
 def test_work_order_beyond_one_chunk():
     """Document masks with 1152 (batch row, query block) entries: the order kernel streams
     the work values through LDS in chunks of 1024, so the second chunk is exercised.  The
-    order equals its definition on the device's counts, the counts equal the oracle's, and
+    order sorts the device's counts by the map's stated cost, the counts equal the oracle's, and
     the forward pass that takes its row blocks in that order writes every output and
     matches the oracle on sampled rows."""
     p = W.make_problem(9, 2, 16384, 64, flags=C | DOC, seed=77, doc_len_range=(300, 5000))
     _announce("work order, 1152 entries")
     dp, o, lse = _run(p)
     got = L.read_blockmap(dp.blockmap, p.B, p.N)
-    np.testing.assert_array_equal(got["order"], oracle.blockmap.work_order_ref(got["counts"], p.flags))
-    assert len(set(got["order"].tolist())) == p.B * 128
+    check_work_order(got["order"], got["counts"], got["header"], True)
     for b in (0, 8):
         ref = oracle.blockmap_ref(1, p.N, p.flags & L.POSITIONAL, 0, p.doc_id[b:b + 1])
         np.testing.assert_array_equal(got["counts"][b], ref["counts"][0], err_msg=f"counts of batch row {b}")

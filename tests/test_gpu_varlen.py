@@ -10,7 +10,7 @@ import oracle
 import workload as W
 from workload import device as WD
 from exact_attention_119_amd import lib as L
-from _parity import assert_close, sample_rows
+from _parity import assert_close, check_work_order, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -73,8 +73,9 @@ def _check_prepared(dp):
     ref = oracle.blockmap_ref(1, p.N, flags, p.window, ids_ref[None])
     assert (got["header"]["B"], got["header"]["N"], got["header"]["flags"]) == (1, p.N, flags)
     np.testing.assert_array_equal(got["status"], ref["status"])
-    for key in ("cls", "counts", "idx", "row_lo", "row_hi", "order"):
+    for key in ("cls", "counts", "idx", "row_lo", "row_hi"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    check_work_order(got["order"], got["counts"], got["header"], True)
     np.testing.assert_array_equal(got["pairs"], ref["qb_pairs"])
     assert L.attn_blockmap_status(dp.blockmap[:mb]) == L.ATTN_OK
 

@@ -126,20 +126,29 @@ def test_qb_pairs_and_doc_status():
     assert O.blockmap_ref(2, 320, CAUSAL, 0, doc)["status"].sum() == 0
 
 
-def test_work_order_properties():
-    """The work order is a permutation of the (b, qb) entries; under a document mask the
-    work 2 * #FULL + 5 * #PARTIAL never increases along it and equal work keeps index
-    order; other masks keep the identity."""
+def test_work_order_checker_accepts_the_order_and_rejects_mistakes():
+    """The GPU tests check the device's work order (a scheduling choice, not part of the
+    method) with tests/_parity.check_work_order.  The checker itself: it accepts an
+    order sorted by the stated cost and rejects a swapped pair, a repeated entry and a
+    non-identity order without documents."""
+    from _parity import check_work_order
     rng = np.random.default_rng(7)
     lengths = rng.integers(40, 700, size=12)
     doc = np.repeat(np.arange(len(lengths)), lengths)[:1500].astype(np.int32)
     doc = np.stack([doc, np.sort(rng.integers(0, 5, size=1500)).astype(np.int32)])
     m = O.blockmap_ref(2, 1500, CAUSAL | DOCUMENT, 0, doc)
-    order = m["order"]
-    nb = m["counts"].shape[1]
-    assert sorted(order.tolist()) == list(range(2 * nb))
-    work = [2 * int(m["counts"][e // nb, e % nb, 0]) + 5 * int(m["counts"][e // nb, e % nb, 1]) for e in order]
-    assert len(set(work)) > 3  # the workload does spread the work
-    for i in range(len(order) - 1):
-        assert work[i] > work[i + 1] or (work[i] == work[i + 1] and order[i] < order[i + 1])
-    assert O.blockmap_ref(2, 1500, CAUSAL, 0, doc)["order"].tolist() == list(range(2 * nb))
+    hd = dict(order_full_cost=2, order_partial_cost=5)
+    c = m["counts"].reshape(-1, 2).astype(np.int64)
+    work = 2 * c[:, 0] + 5 * c[:, 1]
+    assert len(set(work.tolist())) > 3  # the workload does spread the work
+    order = np.array(sorted(range(len(work)), key=lambda e: (-work[e], e)))
+    check_work_order(order, m["counts"], hd, True)
+    i = int(np.nonzero(work[order][:-1] > work[order][1:])[0][0])
+    bad = order.copy()
+    bad[[i, i + 1]] = bad[[i + 1, i]]
+    for wrong in (bad, np.concatenate([order[:-1], order[:1]])):
+        with pytest.raises(AssertionError):
+            check_work_order(wrong, m["counts"], hd, True)
+    check_work_order(np.arange(len(work)), m["counts"], hd, False)
+    with pytest.raises(AssertionError):
+        check_work_order(order, m["counts"], hd, False)

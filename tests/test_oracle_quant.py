@@ -1,7 +1,7 @@
 """Pins of the oracle's fp8 quantiser with incoherent processing (oracle/quant.py):
-the transform against the Hadamard matrix, the e4m3 rounding against torch's cast,
-and the block quantisation against its defining properties and the input generator's
-own (independent) quantiser."""
+the Hadamard matrix against scipy's and its closed form, the e4m3 rounding against
+torch's cast, and the block quantisation against its defining properties and the
+input generator's own (independently written) quantiser."""
 
 import numpy as np
 import pytest
@@ -13,33 +13,26 @@ from oracle.decode import decode_bf16, decode_e4m3, dequant_blocks
 from workload import gen
 
 
-@pytest.mark.parametrize("d", [2, 8, 64, 128])
-def test_fwht_is_the_sylvester_hadamard_product(d):
-    rng = np.random.default_rng(d)
-    x = rng.standard_normal((5, d)).astype(np.float32)
-    H = scipy.linalg.hadamard(d).astype(np.float64)
-    y64 = x.astype(np.float64) @ H
-    y = Qz.fwht_f32(x)
-    assert y.dtype == np.float32
-    bound = np.log2(d) * 2.0 ** -23 * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True)
-    assert np.all(np.abs(y - y64) <= bound)
-    # unit vectors give the rows of H exactly
-    np.testing.assert_array_equal(Qz.fwht_f32(np.eye(d, dtype=np.float32)), H)
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 128])
+def test_hadamard_is_sylvesters(d):
+    H = Qz.hadamard(d)
+    np.testing.assert_array_equal(H, scipy.linalg.hadamard(d))
+    # closed form: H[i, j] = (-1)^popcount(i & j)
+    i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
+    pc = np.vectorize(lambda x: bin(x).count("1"))(i & j) if d > 1 else np.zeros((1, 1), int)
+    np.testing.assert_array_equal(H, (-1.0) ** pc)
+    np.testing.assert_array_equal(H @ H.T, d * np.eye(d))
 
 
-def test_fwht_twice_is_d_times_identity_and_keeps_the_norm():
-    rng = np.random.default_rng(1)
-    x = rng.integers(-8, 9, (7, 128)).astype(np.float32)
-    np.testing.assert_array_equal(Qz.fwht_f32(Qz.fwht_f32(x)), 128 * x)
-    y = Qz.fwht_f32(x)
-    np.testing.assert_allclose((y.astype(np.float64) ** 2).sum(1), 128 * (x.astype(np.float64) ** 2).sum(1))
-
-
-def test_signs_from_bits():
+def test_signs_and_rotation():
     s = Qz.signs_from_bits([0b101, 1 << 31], 64)
-    neg = np.nonzero(s < 0)[0]
-    np.testing.assert_array_equal(neg, [0, 2, 63])
+    np.testing.assert_array_equal(np.nonzero(s < 0)[0], [0, 2, 63])
     assert set(np.unique(s)) == {-1.0, 1.0}
+    R = Qz.rotation([0x12345678, 0x9ABCDEF0, 0x0F1E2D3C, 0x4B5A6978], 128)
+    np.testing.assert_allclose(R @ R.T, np.eye(128), atol=1e-14)
+    # row j of R is sign_j times row j of H over sqrt(d)
+    sg = Qz.signs_from_bits([0x12345678, 0x9ABCDEF0, 0x0F1E2D3C, 0x4B5A6978], 128)
+    np.testing.assert_allclose(R[5], sg[5] * scipy.linalg.hadamard(128)[5] / np.sqrt(128), rtol=0, atol=0)
 
 
 def test_e4m3_encode_matches_torch_cast():
@@ -55,34 +48,58 @@ def test_e4m3_encode_matches_torch_cast():
     np.testing.assert_array_equal(Qz.e4m3_encode(v), ref)
 
 
+def test_e4m3_encode_in_float64_resolves_what_fp32_cannot():
+    """The definition rounds the float64 quotient: a value 2^-40 above a tie goes up,
+    2^-40 below goes down, whatever fp32 would make of it."""
+    srt = np.unique(np.abs(decode_e4m3(np.arange(0x7F, dtype=np.uint8))))
+    mids = (srt[1:] + srt[:-1]) / 2
+    up = Qz.e4m3_encode(mids * (1 + 2.0 ** -40))
+    down = Qz.e4m3_encode(mids * (1 - 2.0 ** -40))
+    np.testing.assert_array_equal(up.astype(int), np.arange(1, 0x7F))
+    np.testing.assert_array_equal(down.astype(int), np.arange(0, 0x7E))
+
+
 def test_e4m3_encode_round_trips_and_saturates():
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
-    np.testing.assert_array_equal(Qz.e4m3_encode(decode_e4m3(codes).astype(np.float32)), codes)
-    np.testing.assert_array_equal(Qz.e4m3_encode(np.float32([450.0, 463.9, -455.0])), [0x7E, 0x7E, 0xFE])
+    np.testing.assert_array_equal(Qz.e4m3_encode(decode_e4m3(codes)), codes)
+    np.testing.assert_array_equal(Qz.e4m3_encode(np.array([450.0, 463.9, -455.0])), [0x7E, 0x7E, 0xFE])
 
 
 def _bf16(x):
     return gen.bf16_bits_from_f32(np.asarray(x, dtype=np.float32))
 
 
-def test_quantize_unrotated_agrees_with_the_generators_quantiser():
-    """The input generator quantises with an fp64 division; this side multiplies by the
-    fp32 inverse scale.  With bf16 inputs and 448 = 7 * 2^6 the exact quotient often
-    lies at or next to an e4m3 tie: only there may the two differ, by one code."""
+def test_quantize_unrotated_equals_the_generators_quantiser():
+    """Both sides take round-to-nearest-even of x / s with s = fp32(amax / 448): equal
+    scales and equal codes everywhere, exact ties included (bf16 inputs and
+    448 = 7 * 2^6 put many quotients exactly on an e4m3 tie)."""
     rng = np.random.default_rng(3)
     x = rng.standard_normal((2, 3, 300, 64)).astype(np.float32)
     bits = _bf16(x)
     codes, scales = Qz.quantize_blocks_ref(bits)
     gcodes, gscales = gen.quantize_e4m3_blocks(decode_bf16(bits).astype(np.float32))
     np.testing.assert_array_equal(scales, gscales)
-    diff = decode_e4m3(codes) != decode_e4m3(gcodes)
-    assert diff.mean() < 1e-3
-    s = np.repeat(scales, 128, axis=2)[:, :, :300, None]
-    v64 = (decode_bf16(bits) / s.astype(np.float64))[diff]
-    a, b = decode_e4m3(codes)[diff], decode_e4m3(gcodes)[diff]
-    tie = (a + b) / 2
-    assert np.all(np.abs(v64 - tie) <= np.abs(tie) * 2.0 ** -21)  # within fp32 rounding of a tie
-    assert np.all(np.abs(codes.astype(int)[diff] - gcodes.astype(int)[diff]) == 1)
+    # (the generator writes +0 for a negative value that rounds to zero, the oracle -0)
+    np.testing.assert_array_equal(decode_e4m3(codes), decode_e4m3(gcodes))
+    s = np.repeat(scales, 128, axis=2)[:, :, :300, None].astype(np.float64)
+    q = decode_bf16(bits) / s
+    srt = np.unique(np.abs(decode_e4m3(np.arange(0x7F, dtype=np.uint8))))
+    ties = np.isin(np.abs(q), (srt[1:] + srt[:-1]) / 2)
+    assert ties.sum() > 50  # the exact-tie case is exercised, and both sides agree on it
+
+
+def test_quantize_rotated_equals_the_generators_rotation():
+    """The generator rotates with its own Hadamard construction (Kronecker products) and
+    its own sign decoding; the oracle's rotated codes and scales are the same."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((1, 2, 260, 128)).astype(np.float32)
+    x[..., [3, 50, 51, 90]] *= 20
+    bits = _bf16(x)
+    words = np.array([0x9E3779B9, 0x7F4A7C15, 0x2545F491, 0x4F6CDD1D], dtype=np.uint32)
+    codes, scales = Qz.quantize_blocks_ref(bits, words)
+    gcodes, gscales = gen.quantize_e4m3_blocks(decode_bf16(bits) @ gen.rotation_matrix(words, 128))
+    np.testing.assert_array_equal(scales, gscales)
+    np.testing.assert_array_equal(decode_e4m3(codes), decode_e4m3(gcodes))
 
 
 @pytest.mark.parametrize("rotate", [False, True])
@@ -94,27 +111,30 @@ def test_quantize_block_properties(rotate):
     bits = _bf16(x)
     sb = np.array([0x9E3779B9, 0x7F4A7C15, 0x2545F491, 0x4F6CDD1D], dtype=np.uint32) if rotate else None
     codes, scales = Qz.quantize_blocks_ref(bits, sb)
-    rnorm = np.float32(1 / np.sqrt(d))
     y = decode_bf16(bits)
     if rotate:
-        y = (y * Qz.signs_from_bits(sb, d)) @ scipy.linalg.hadamard(d)
+        y = (y * Qz.signs_from_bits(sb, d)) @ scipy.linalg.hadamard(d) / np.sqrt(d)
     for b in range(2):
         for j in range(3):
             blk = y[0, b, 128 * j:128 * (j + 1)]
             c = codes[0, b, 128 * j:128 * (j + 1)]
-            s = scales[0, b, j] / (rnorm if rotate else 1)
             if not np.any(blk):
                 # (+0 or -0: a sign flip of +0 gives -0)
-                assert np.all(c & 0x7F == 0) and scales[0, b, j] == (rnorm if rotate else 1.0)
+                assert np.all(c & 0x7F == 0) and scales[0, b, j] == 1.0
                 continue
+            amax = np.abs(blk).max()
+            assert abs(scales[0, b, j] - amax / 448) <= 2.0 ** -24 * amax / 448
             # the largest magnitude lands on +-448 (code 0x7E / 0xFE)
             i = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
             assert c[i] & 0x7F == 0x7E
             # every code is within half an e4m3 step (relative 2^-4, or 2^-10 absolute
-            # in the subnormal range) of y * 448 / amax
-            v = blk * 448.0 / np.abs(blk).max()
+            # in the subnormal range) of y / s, and none is nearer
+            v = blk / np.float64(scales[0, b, j])
             err = np.abs(decode_e4m3(c) - v)
-            assert np.all(err <= np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10) * 1.0001)
+            assert np.all(err <= np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-12))
+            allv = decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+            near = np.abs(np.abs(v)[..., None] - allv).min(axis=-1)
+            np.testing.assert_allclose(err, near, rtol=0, atol=1e-12)
 
 
 def test_rotation_keeps_scores_and_reduces_the_outlier_error():
@@ -138,6 +158,6 @@ def test_rotation_keeps_scores_and_reduces_the_outlier_error():
         err[rot is not None] = np.abs(s - s_exact).mean()
     assert err[True] < 0.5 * err[False]
     # without quantisation the rotation is exact: (x R)(y R)^T = x y^T
-    R = np.diag(Qz.signs_from_bits(sb, d).astype(np.float64)) @ scipy.linalg.hadamard(d) / np.sqrt(d)
+    R = np.diag(Qz.signs_from_bits(sb, d)) @ scipy.linalg.hadamard(d) / np.sqrt(d)
     xq, xk = decode_bf16(qb)[0, 0], decode_bf16(kb)[0, 0]
     np.testing.assert_allclose((xq @ R) @ (xk @ R).T, s_exact, rtol=1e-9, atol=1e-9)

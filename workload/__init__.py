@@ -23,4 +23,6 @@ from .gen import (  # noqa: F401
     make_varlen_problem,
     make_dout,
     quantize_e4m3_blocks,
+    rotation_matrix,
+    sylvester_hadamard,
 )

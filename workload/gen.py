@@ -15,6 +15,16 @@ Recipe, fixed so that both sides of the parity check see identical bytes:
   * fp8 inputs: per (b, h, 128-row block) scale = amax / 448 in fp32 (1.0 for
     an all-zero block), code = OCP E4M3FN round-to-nearest-even of
     x / scale, saturated to +-448.  Dequantised value = code value * scale.
+  * fp8 inputs with incoherent processing (``rotate=True``; the FlashAttention-3
+    news, section "Analyse", names a processing step against outlier features,
+    read as incoherent processing): after V, d/32 sign words are drawn with
+    ``rng.integers(0, 2**32)``; Q and K (their fp32 values, in float64) are
+    multiplied by R = D H / sqrt(d) (D the signs, bit j % 32 of word j // 32 set
+    = -1; H the Sylvester Hadamard matrix) before the block quantisation above,
+    whose maximum is then taken in float64 and rounded to fp32 after the
+    division by 448.  V is not rotated.  Q.K^T is unchanged by R up to the
+    quantisation, so the attention of the rotated codes approximates that of the
+    source values.
   * Documents: lengths drawn uniformly from [lo, hi] (inclusive) until they
     cover N; the last one is truncated.  Ids 0, 1, 2, ... in token order.
 """
@@ -80,6 +90,7 @@ class Problem:
     alibi_slopes: Optional[np.ndarray] = None
     H_kv: Optional[int] = None
     cu_seqlens: Optional[np.ndarray] = None  # packed variable-length batch (B = 1): int32 [nseq + 1]
+    rotate_signs: Optional[np.ndarray] = None  # uint32 [d/32]: Q and K codes are of x R (incoherent processing)
 
     @property
     def Hkv(self) -> int:
@@ -89,7 +100,7 @@ class Problem:
     def digests(self) -> dict:
         """sha256 of every generated buffer (hex)."""
         out = {}
-        for key in ("q", "k", "v", "q_scale", "k_scale", "v_scale", "doc_id", "cu_seqlens"):
+        for key in ("q", "k", "v", "q_scale", "k_scale", "v_scale", "doc_id", "cu_seqlens", "rotate_signs"):
             arr = getattr(self, key)
             if arr is not None:
                 out[key] = hashlib.sha256(np.ascontiguousarray(arr).tobytes()).hexdigest()
@@ -146,11 +157,13 @@ def e4m3_codes_from_f64(x: np.ndarray) -> np.ndarray:
 
 
 def quantize_e4m3_blocks(x: np.ndarray, block: int = QUANT_BLOCK) -> Tuple[np.ndarray, np.ndarray]:
-    """Per (b, h, row block) E4M3 quantisation of fp32 x[B][H][N][d].
+    """Per (b, h, row block) E4M3 quantisation of x[B][H][N][d] (fp32, or float64 values
+    such as rotated rows: then the maximum is taken in float64 and amax / 448 rounded to fp32).
 
     Returns (codes uint8 [B][H][N][d], scales float32 [B][H][ceil(N/block)]).
     """
-    x = np.asarray(x, dtype=np.float32)
+    wide = np.asarray(x).dtype == np.float64
+    x = np.asarray(x, dtype=np.float64 if wide else np.float32)
     B, H, N, d = x.shape
     nblk = (N + block - 1) // block
     scales = np.empty((B, H, nblk), dtype=np.float32)
@@ -158,12 +171,36 @@ def quantize_e4m3_blocks(x: np.ndarray, block: int = QUANT_BLOCK) -> Tuple[np.nd
     for j in range(nblk):
         r0, r1 = j * block, min(N, (j + 1) * block)
         blk = x[:, :, r0:r1, :]
-        amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)
-        s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        if wide:
+            amax = np.abs(blk).max(axis=(2, 3))
+            s = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+        else:
+            amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)
+            s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
         scales[:, :, j] = s
         codes[:, :, r0:r1, :] = e4m3_codes_from_f64(
             blk.astype(np.float64) / s.astype(np.float64)[:, :, None, None])
     return codes, scales
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order d (a power of two) as float64, by Kronecker
+    products of [[1, 1], [1, -1]]."""
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    if h.shape[0] != d:
+        raise ValueError("order must be a power of two")
+    return h
+
+
+def rotation_matrix(sign_words: np.ndarray, d: int) -> np.ndarray:
+    """R = D H / sqrt(d) for sign words (bit j % 32 of word j // 32 set: D[j] = -1)."""
+    w = np.asarray(sign_words, dtype=np.uint64)
+    j = np.arange(d)
+    neg = ((w[j // 32] >> (j % 32).astype(np.uint64)) & np.uint64(1)).astype(bool)
+    signs = np.where(neg, -1.0, 1.0)
+    return (signs[:, None] * sylvester_hadamard(d)) / math.sqrt(d)
 
 
 # --------------------------------------------------------------------------
@@ -195,7 +232,7 @@ def _f32(x: float) -> float:
 
 
 def _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale, doc_lengths, n_outliers,
-           outlier_gain, alibi_slopes=None, H_kv=None) -> Problem:
+           outlier_gain, alibi_slopes=None, H_kv=None, rotate=False) -> Problem:
     doc_id = None
     if doc_lengths is not None:
         doc_id = np.stack([doc_ids_from_lengths(doc_lengths[b]) for b in range(B)]).astype(np.int32)
@@ -219,13 +256,25 @@ def _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale, doc_leng
         return Problem(q=bf16_bits_from_f32(xs[0]), k=bf16_bits_from_f32(xs[1]),
                        v=bf16_bits_from_f32(xs[2]), **kw)
     if dtype == "fp8":
+        signs = None
+        if rotate:
+            signs = rng.integers(0, 2 ** 32, size=(d + 31) // 32, dtype=np.uint64).astype(np.uint32)
+            R = rotation_matrix(signs, d)
+            xs[0] = xs[0].astype(np.float64) @ R
+            xs[1] = xs[1].astype(np.float64) @ R
         (qc, qs), (kc, ks), (vc, vs) = (quantize_e4m3_blocks(x) for x in xs)
-        return Problem(q=qc, k=kc, v=vc, q_scale=qs, k_scale=ks, v_scale=vs, **kw)
+        return Problem(q=qc, k=kc, v=vc, q_scale=qs, k_scale=ks, v_scale=vs, rotate_signs=signs, **kw)
+    if rotate:
+        raise ValueError("incoherent processing applies to fp8 inputs")
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def config_problem(cfg: int) -> Problem:
-    """The five synthetic workloads, drawn with ``default_rng([119, cfg])``."""
+def config_problem(cfg: int, rotate: bool = False) -> Problem:
+    """The five synthetic workloads, drawn with ``default_rng([119, cfg])``; ``rotate``
+    (configuration 5 only) quantises Q and K after the rotation R (incoherent processing),
+    the same draws otherwise."""
+    if rotate and cfg != 5:
+        raise ValueError("only the fp8 configuration has a rotated form")
     rng = np.random.default_rng([119, cfg])
     if cfg == 1:
         return _build("cfg1", rng, 1, 2, 256, 64, "bf16", 0, 0, 0.0, 1.0 / 8.0, None, 0, 1.0)
@@ -240,8 +289,8 @@ def config_problem(cfg: int) -> Problem:
         return _build("cfg4", rng, 1, 16, 16384, 128, "bf16", ATTN_CAUSAL | ATTN_DOCUMENT | ATTN_ALIBI,
                       0, 0.0, 1.0 / math.sqrt(128), [lengths], 0, 1.0)
     if cfg == 5:
-        return _build("cfg5", rng, 1, 16, 16384, 128, "fp8", 0, 0, 0.0, 1.0 / math.sqrt(128), None, 4,
-                      20.0)
+        return _build("cfg5-rot" if rotate else "cfg5", rng, 1, 16, 16384, 128, "fp8", 0, 0, 0.0,
+                      1.0 / math.sqrt(128), None, 4, 20.0, rotate=rotate)
     raise ValueError(f"no config {cfg}")
 
 
@@ -250,9 +299,10 @@ def make_problem(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", flags: 
                  seed: Union[int, Tuple[int, ...]] = 0,
                  doc_len_range: Optional[Tuple[int, int]] = None, n_outliers: int = 0,
                  outlier_gain: float = 20.0, alibi_slopes: Optional[np.ndarray] = None,
-                 H_kv: Optional[int] = None) -> Problem:
+                 H_kv: Optional[int] = None, rotate: bool = False) -> Problem:
     """An ad-hoc problem of any shape, drawn with ``default_rng([119, 1000, *seed])``;
-    H_kv key/value heads shared by groups of H / H_kv query heads (default H_kv = H)."""
+    H_kv key/value heads shared by groups of H / H_kv query heads (default H_kv = H);
+    ``rotate`` (fp8): Q and K quantised after the rotation R (incoherent processing)."""
     seed_t = (seed,) if isinstance(seed, int) else tuple(seed)
     rng = np.random.default_rng([119, 1000, *seed_t])
     if scale is None:
@@ -264,8 +314,8 @@ def make_problem(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", flags: 
     if alibi_slopes is not None:
         alibi_slopes = np.asarray(alibi_slopes, dtype=np.float32)
     name = f"B{B}H{H}N{N}d{d}" + ("" if H_kv is None else f"Hkv{H_kv}")
-    return _build(name, rng, B, H, N, d, dtype, flags, window, softcap, scale,
-                  doc_lengths, n_outliers, outlier_gain, alibi_slopes, H_kv)
+    return _build(name + ("-rot" if rotate else ""), rng, B, H, N, d, dtype, flags, window, softcap, scale,
+                  doc_lengths, n_outliers, outlier_gain, alibi_slopes, H_kv, rotate)
 
 
 def make_varlen_problem(lengths: Sequence[int], H: int, d: int, *, dtype: str = "bf16", flags: int = 0,
