@@ -20,6 +20,11 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
                       uint32_t flags, int window, float softcap, const float* slopes, const void* map,
                       hipStream_t stream);
+hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                              float scale, uint32_t flags, int window, float softcap, const float* slopes,
+                              const void* map, hipStream_t stream);
+size_t bwd_scratch_rows();
 hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N, int d, const uint32_t* signs,
                         hipStream_t stream);
 template <int D, int IN>
@@ -426,6 +431,27 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
   const float* slopes = (mask && (flags & ATTN_ALIBI)) ? mask->alibi_slopes : nullptr;
   if (launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, scale, flags, window, cap, slopes,
                  positional(mask) ? blockmap : nullptr, (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_gqa_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t H_kv,
+                                 int32_t N, int32_t d, float scale, const attn_mask* mask, const void* blockmap,
+                                 size_t blockmap_bytes, void* stream) {
+  attn_status st = attn_check_args_gqa(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, H_kv, N, d,
+                                       scale, ATTN_BF16, mask, blockmap, blockmap_bytes, nullptr, 8.f);
+  if (st != ATTN_OK) return st;
+  if (positional(mask) && !blockmap) return ATTN_ERR_BAD_BLOCKMAP;
+  if (!dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_INVALID_ARG;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N > (uint64_t)bwd_scratch_rows()) return ATTN_ERR_INVALID_ARG;
+  const uint32_t flags = mask ? mask->flags : 0u;
+  const int window = (flags & ATTN_WINDOW) ? mask->window : 0;
+  const float cap = (flags & ATTN_SOFTCAP) ? mask->softcap : 0.f;
+  const float* slopes = (mask && (flags & ATTN_ALIBI)) ? mask->alibi_slopes : nullptr;
+  if (launch_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, scale, flags, window, cap, slopes,
+                         positional(mask) ? blockmap : nullptr, (hipStream_t)stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

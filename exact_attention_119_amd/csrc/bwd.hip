@@ -21,9 +21,11 @@
 // row fragments of a row-major LDS tile as A operands, transposed fragments
 // (ds_read_b64_tr_b16) as A operands of the T^T products, and accumulators packed to
 // bf16 as B operands in the contraction order those transposed reads produce.
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/attn119.h"
+
 #include "common.hpp"
 
 namespace attn119 {
@@ -622,6 +624,56 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   const bool masked = (flags & kPositional) != 0;
   if (masked && !map) return hipErrorInvalidValue;
   return d == 128 ? bwd::launch_d<128>(a, masked, stream) : bwd::launch_d<64>(a, masked, stream);
+}
+
+// ---- the backward pass without a caller workspace ------------------------------------
+// For callers that cannot allocate (HIP graph capture, tight serving loops, harnesses that
+// forbid hipMalloc): the row sums D live in this file-scope device array instead of a
+// caller-owned buffer.  Each GPU holds its own copy at its own address until the process
+// ends; host code never passes the array's name (a host-side stand-in) to a kernel, only
+// the device address hipGetSymbolAddress returns for the current device, looked up once
+// per device.  Every call on a GPU shares that GPU's array, so calls that overlap on one
+// GPU race; D is fully written by the row-sum kernel before anything reads it, so nothing
+// needs clearing.
+constexpr size_t kScratchRows = size_t(1) << 22;  // 4,194,304 rows of D = 16 MiB per GPU
+static __device__ __align__(256) float scratch[kScratchRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t bwd_scratch_rows() { return kScratchRows; }
+
+// Device address of this GPU's scratch array (resolved on the first call on the device).
+hipError_t bwd_scratch_ptr(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                              float scale, uint32_t flags, int window, float softcap, const float* slopes,
+                              const void* map, hipStream_t stream) {
+  if ((size_t)B * H * N > kScratchRows) return hipErrorInvalidValue;
+  float* delta = nullptr;
+  const hipError_t e = bwd_scratch_ptr(&delta);
+  if (e != hipSuccess) return e;
+  return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, flags, window, softcap,
+                    slopes, map, stream);
 }
 
 }  // namespace attn119

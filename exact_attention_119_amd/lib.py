@@ -42,7 +42,7 @@ ATTN_QK_E4M3 = 1
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
-           "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa")
+           "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa", "attn_bwd_gqa_noalloc")
 
 
 class AttnError(RuntimeError):
@@ -112,6 +112,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                  ctypes.POINTER(attn_mask), vp, sz, vp]
     lib.attn_bwd_gqa.restype = i32
+    lib.attn_bwd_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                         ctypes.POINTER(attn_mask), vp, sz, vp]
+    lib.attn_bwd_gqa_noalloc.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, ctypes.POINTER(attn_mask),
                              vp, sz, vp]
     lib.attn_bwd.restype = i32
@@ -283,6 +286,20 @@ def attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, *, scale: float, mask
                                _ptr(dv), _ptr(delta), B, H, H_kv, N, d, float(scale),
                                ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes, _stream(stream)),
            "attn_bwd_gqa")
+
+
+def attn_bwd_gqa_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, scale: float, mask: Optional[attn_mask] = None,
+                         blockmap=None, stream=None) -> None:
+    """attn_bwd_gqa without the delta workspace: the row sums live in the library's per-GPU
+    scratch array (no allocation; calls overlapping on one GPU race)."""
+    B, H, N, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[1])
+    mbytes = 0 if blockmap is None else blockmap.numel() * blockmap.element_size()
+    _check(load().attn_bwd_gqa_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, H, H_kv, N, d, float(scale),
+                                       ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes,
+                                       _stream(stream)),
+           "attn_bwd_gqa_noalloc")
 
 
 def read_blockmap(blockmap, B: int, N: int) -> dict:

@@ -321,6 +321,22 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* stream);
 
 /*
+ * The backward pass of attn_bwd_gqa without the delta workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the row sums D go to a scratch array inside the library, one per GPU,
+ * of at most 4,194,304 rows (16 MiB, held by each GPU the library runs on until the process
+ * ends).  This call allocates nothing.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (on different streams, or from different threads) race;
+ * serialise them.  Arguments, results and errors as attn_bwd_gqa without delta, plus
+ * ATTN_ERR_INVALID_ARG when B * H * N exceeds 4,194,304.  dq, dk, dv are bit-identical to
+ * attn_bwd_gqa's for the same inputs.
+ */
+attn_status attn_bwd_gqa_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H, int32_t H_kv,
+                                 int32_t N, int32_t d, float scale, const attn_mask* mask, const void* blockmap,
+                                 size_t blockmap_bytes, void* stream);
+
+/*
  * Name of the compiled kernel variant attn_fwd selects for these arguments, e.g.
  * "bf16 d128 masked softcap" (host logic only, no HIP call, usable without a GPU);
  * NULL when the combination is unsupported.  The string is static.  A "masked"

@@ -207,3 +207,13 @@ def test_kernel_variant_selection(L):
     assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8q) == "fp8-qk8 d64 masked alibi"
     assert L.attn_fwd_kernel_name(96, 0, None, None) is None
     assert L.attn_fwd_kernel_name(128, 1, None, None) is None
+
+
+def test_noalloc_backward_rejects_more_rows_than_its_scratch(L):
+    """attn_bwd_gqa_noalloc keeps the row sums in a 4,194,304-row scratch array: a call with
+    more rows (B * H * N) is refused before anything is launched."""
+    lib = L.load()
+    st = lib.attn_bwd_gqa_noalloc(P, P, P, P, P, P, P, P, P, 1, 64, 64, 65537, 128, 0.1, None, None, 0, None)
+    assert st == L.ATTN_ERR_INVALID_ARG
+    st = lib.attn_bwd_gqa_noalloc(P, P, P, P, P, None, P, P, P, 1, 4, 4, 300, 128, 0.1, None, None, 0, None)
+    assert st == L.ATTN_ERR_INVALID_ARG
