@@ -162,7 +162,8 @@ def cpu_baseline(p, budget_s: float):
 def timed_windows(torch, stream, steps: int, launch, nwin: int = 5):
     """Times `steps` calls of `launch` back to back: the host clock around all of them
     (synchronised on both sides) and HIP events on `stream` at the boundaries of up to
-    `nwin` windows.  Returns (host ms per call, [event ms per call of each window])."""
+    `nwin` windows.  Returns (host ms per call, [event ms per call of each window],
+    event ms per call over all windows)."""
     nwin = max(1, min(nwin, steps))
     bounds = [round(i * steps / nwin) for i in range(nwin + 1)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
@@ -176,7 +177,7 @@ def timed_windows(torch, stream, steps: int, launch, nwin: int = 5):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [ev[w].elapsed_time(ev[w + 1]) / (bounds[w + 1] - bounds[w]) for w in range(nwin)]
-    return wall * 1e3 / steps, per
+    return wall * 1e3 / steps, per, ev[0].elapsed_time(ev[nwin]) / steps
 
 
 def warm_up(torch, launch, min_steps: int, min_seconds: float):
@@ -526,14 +527,14 @@ def main(argv=None):
 
     # The timed region: K whole steps back to back with nothing else on the stream (one
     # event between windows, none inside a step).
-    step_ms, step_win = timed_windows(torch, stream, args.steps, one_step)
+    step_ms, step_win, step_ev = timed_windows(torch, stream, args.steps, one_step)
     if map_in_step:
         # the forward kernel alone, K launches right after, timed the same way
-        _, fwd_win = timed_windows(torch, stream, args.steps, one_forward)
+        _, fwd_win, fwd_mean = timed_windows(torch, stream, args.steps, one_forward)
     else:
-        fwd_win = step_win  # the step is the forward kernel: its own window
+        fwd_win, fwd_mean = step_win, step_ev  # the step is the forward kernel: its own window
     clock.stop()
-    fwd_med, fwd_min = median(fwd_win), min(fwd_win)
+    fwd_med, fwd_min = fwd_mean, min(fwd_win)
     graph_note = None
     if fwd_med < 0.05:  # short kernel: the windows above measure the host's launch rate
         graph_note = fwd_med
@@ -542,10 +543,10 @@ def main(argv=None):
     map_avg = loop_ms(torch, stream, args.steps, lambda: WD.build_map(dp)) if dp.blockmap is not None else 0.0
     consistent = fwd_med <= step_ms
     log(f"bench: warm-up {nwarm} steps in {twarm:.2f} s; step {step_ms:.4f} ms (host clock, mean of {args.steps}), "
-        f"windows median {median(step_win):.4f} min {min(step_win):.4f} ms; forward kernel median {fwd_med:.4f} "
-        f"min {fwd_min:.4f} ms; block map build avg {map_avg:.4f} ms")
+        f"windows median {median(step_win):.4f} min {min(step_win):.4f} ms; forward kernel mean {fwd_med:.4f} "
+        f"(window median {median(fwd_win):.4f}) min {fwd_min:.4f} ms; block map build avg {map_avg:.4f} ms")
     if not consistent:
-        log("bench: WARNING the forward kernel's median exceeds the step time (it was timed in its own run; "
+        log("bench: WARNING the forward kernel's mean exceeds the step time (it was timed in its own run; "
             "the clock differed)")
 
     dtype = p.dtype
@@ -583,10 +584,13 @@ def main(argv=None):
                    "engine_clock": clock.summary(t_settled)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel_name, "kernel_avg_ms": round(fwd_med, 5), "kernel_min_ms": round(fwd_min, 5),
-                     "kernel_timing": ("HIP events: median over the timed windows of the step, which is this "
-                                       "kernel alone" if not map_in_step else
-                                       "HIP events: median over windows of K forward launches after the timed steps"),
+                     "kernel": kernel_name, "kernel_avg_ms": round(fwd_med, 5),
+                     "kernel_window_median_ms": round(median(fwd_win), 5), "kernel_min_ms": round(fwd_min, 5),
+                     "kernel_timing": ("HIP events around the timed steps, each step being this kernel alone: "
+                                       "mean per launch, and the median and minimum of the windows"
+                                       if not map_in_step else
+                                       "HIP events around K forward launches right after the timed steps: mean per "
+                                       "launch, and the median and minimum of the windows"),
                      "kernel_le_step": consistent, "map_build_avg_ms": round(map_avg, 5)},
     }
     if dtype == "fp8":
