@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["exact_attention_119_amd/csrc/fwd_bf16.hpp", "exact_attention_119_amd/csrc/fwd_kernel.hpp",
+KERNEL_SOURCES = ["exact_attention_119_amd/csrc/fwd_bf16.hpp",
                   "exact_attention_119_amd/csrc/fwd_args.hpp", "exact_attention_119_amd/csrc/common.hpp",
                   "exact_attention_119_amd/build.py"]
 QUANT_SOURCES = ["exact_attention_119_amd/csrc/quant.hip", "exact_attention_119_amd/csrc/common.hpp",
@@ -97,7 +97,8 @@ def workload_name(p) -> str:
     if p.flags & 8:
         mods.append("alibi")
     kv = "" if p.Hkv == p.H else f" Hkv{p.Hkv}"
-    return f"B{p.B} H{p.H}{kv} N{p.N} d{p.d} {'+'.join(mods) or 'no-mask'} {p.dtype}"
+    rot = " rotated" if p.rotate_signs is not None else ""
+    return f"B{p.B} H{p.H}{kv} N{p.N} d{p.d} {'+'.join(mods) or 'no-mask'} {p.dtype}{rot}"
 
 
 def visible_pairs(p) -> int:
@@ -451,6 +452,10 @@ def main(argv=None):
     ap.add_argument("--kv-heads", type=int, default=None,
                     help="key/value heads of a --shape workload (grouped-query attention)")
     ap.add_argument("--tau", type=float, default=8.0)
+    ap.add_argument("--qk8", action="store_true",
+                    help="fp8 workloads: Q.K^T on the e4m3 MFMA (a measured mode, see the design notes)")
+    ap.add_argument("--rotate", action="store_true",
+                    help="configuration 5 with incoherent processing: Q and K quantised after the rotation")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
     ap.add_argument("--bwd", action="store_true",
@@ -502,10 +507,11 @@ def main(argv=None):
     elif args.plain_causal:
         p = W.make_problem(2, 32, 8192, 128, flags=W.ATTN_CAUSAL, seed=3)
     else:
-        p = W.config_problem(args.config)
+        p = W.config_problem(args.config, rotate=args.rotate)
     name = workload_name(p)
     log(f"bench: {name}; generating done, staging to HBM")
-    dp = WD.to_device(p)
+    from exact_attention_119_amd import lib as L
+    dp = WD.to_device(p, qk_mode=L.ATTN_QK_E4M3 if args.qk8 else L.ATTN_QK_BF16)
     pairs = visible_pairs(p)
     flop_per_step = 4.0 * p.d * p.H * pairs
     stream = torch.cuda.current_stream()

@@ -27,12 +27,10 @@ hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const
 size_t bwd_scratch_rows();
 hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N, int d, const uint32_t* signs,
                         hipStream_t stream);
-template <int D, int IN>
-hipError_t launch_fwd_family(const FwdArgs& a, bool masked, bool alibi, bool softcap, hipStream_t st);
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
 namespace bf16path {
 constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
-template <int D, bool FP8>
+template <int D, bool FP8, bool QK8>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st);
 }  // namespace bf16path
 }  // namespace attn119
@@ -79,24 +77,19 @@ struct VariantNames {
     static const char* const kIn[] = {"bf16", "fp8", "fp8-qk8"};
     static const char* const kMode[] = {"linear", "softcap", "alibi-causal", "generic-alibi",
                                         "generic-alibi-softcap"};
-    static const char* const kMods[] = {"none", "softcap", "alibi", "alibi+softcap"};
     for (int di = 0; di < 2; ++di)
       for (int in = 0; in < 3; ++in)
         for (int m = 0; m < 2; ++m)
-          for (int k = 0; k < 5; ++k) {
-            const char* tail = in != 2 ? kMode[k] : kMods[k < 4 ? k : 3];
+          for (int k = 0; k < 5; ++k)
             std::snprintf(names[di][in][m][k], 64, "%s d%d %s %s", kIn[in], di ? 128 : 64,
-                          m ? "masked" : "unmasked", tail);
-          }
+                          m ? "masked" : "unmasked", kMode[k]);
   }
 };
 
 const char* variant_name(const FwdVariant& v) {
   static const VariantNames table;
   const auto& names = table.names;
-  int k;
-  if (v.input != kInFp8Qk8) k = v.mode == bf16path::kGeneric ? (v.softcap ? 4 : 3) : v.mode;
-  else k = (v.alibi ? 2 : 0) + (v.softcap ? 1 : 0);
+  const int k = v.mode == bf16path::kGeneric ? (v.softcap ? 4 : 3) : v.mode;
   return names[v.d == 128][v.input][v.masked][k];
 }
 
@@ -247,9 +240,9 @@ attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, voi
     if (fp8->qk_mode != ATTN_QK_BF16 && fp8->qk_mode != ATTN_QK_E4M3) return ATTN_ERR_UNSUPPORTED;
   }
   if (positional(mask)) {
-    // Causal and window masks may come without a map (the bf16-path kernel derives the
-    // block lists from the flags); a document mask, and Q.K^T on the e4m3 MFMA, need one.
-    const bool need = (mask->flags & ATTN_DOCUMENT) || (dtype == ATTN_FP8_E4M3 && fp8->qk_mode == ATTN_QK_E4M3);
+    // Causal and window masks may come without a map (the kernel derives the block lists
+    // from the flags); a document mask needs one.
+    const bool need = (mask->flags & ATTN_DOCUMENT) != 0;
     if (blockmap || need) {
       if (!blockmap || !aligned16(blockmap)) return ATTN_ERR_BAD_BLOCKMAP;
       if (blockmap_bytes != map_layout(B, N).total) return ATTN_ERR_BAD_BLOCKMAP;
@@ -338,14 +331,14 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   const hipStream_t s = (hipStream_t)stream;
   const FwdVariant var = select_variant(d, dtype, mask, fp8);
   if (dtype == ATTN_BF16)
-    e = d == 128 ? bf16path::launch<128, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else if (fp8->qk_mode == ATTN_QK_BF16)
-    e = d == 128 ? bf16path::launch<128, true>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, true>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else
-    e = d == 128 ? launch_fwd_family<128, kInFp8Qk8>(a, masked, alibi, softcap, s)
-                 : launch_fwd_family<64, kInFp8Qk8>(a, masked, alibi, softcap, s);
+    e = d == 128 ? bf16path::launch<128, true, true>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true, true>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

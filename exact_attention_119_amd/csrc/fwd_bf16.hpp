@@ -146,11 +146,19 @@ __host__ __device__ constexpr int key_off(int bk, int r) { return 32 * bk + 8 * 
 //           vs_kb / vs_max (the key block's V scale over the head's largest), so that
 //           P <= 2^tau stays inside fp16 whatever the scales; O is multiplied back by
 //           vs_max and normalised by the fp32 row sum (fp16 P is within 2^-11 of it).
+//   QK8     (with FP8) Q.K^T on the e4m3 MFMA instead: K codes go to LDS as they are (direct
+//           loads), Q codes stay in VGPRs, S = K.Q^T on v_mfma_scale_f32_32x32x64_f8f6f4
+//           (unit block scales; the fp32 scales are applied to S as above).  The MFMA
+//           sums a 64-term dot product with about 14 bits below its largest product
+//           (measured; truncating), so a score dominated by a few large products carries
+//           an error of that size.
 //   MASKED  positional mask through the block map (else: all keys visible)
 //   MODE    score-modifier mode (kLinear, kSoftcap, kAlibiCausal, kGeneric)
 //   GALIBI, GSOFTCAP  modifiers of the generic mode
-template <int D, bool FP8, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
+template <int D, bool FP8, bool QK8, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
 __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) {
+  static_assert(FP8 || !QK8, "the e4m3 Q.K^T takes e4m3 inputs");
+  static_assert(!(QK8 && MODE == kSoftcap), "softcap with e4m3 Q.K^T runs in the generic mode");
   constexpr int BN = 64;                 // keys per step
   constexpr int ROWB = D * 2;            // bytes per 16-bit row of Q/K/V (LDS; HBM for bf16)
   constexpr int HROWB = FP8 ? D : D * 2;  // bytes per row in HBM
@@ -160,8 +168,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   constexpr int LOADS = TILE / 1024;     // 1 KiB direct loads per tile
   constexpr int LPW = LOADS / 4;         // ... per wave
   constexpr int RPL = 1024 / ROWB;       // rows per direct load
-  constexpr int NQC = D / 16;            // 16-wide d chunks of Q (MFMA k steps)
+  // K in LDS: 16-bit rows, or e4m3 codes with QK8
+  constexpr int KROWB = QK8 ? D : ROWB;  // bytes per K row in LDS
+  constexpr int KCPR = KROWB / 16;
+  constexpr int KRP256 = 256 / KROWB;
+  constexpr int KLPW = BN * KROWB / 1024 / 4;  // 1 KiB direct K loads per wave
+  constexpr int KRPL = 1024 / KROWB;
+  constexpr bool DIRECT_K = !FP8 || QK8;  // K tiles by direct HBM -> LDS loads
+  constexpr bool DIRECT_V = !FP8;         // V tiles likewise (else staged and widened)
+  constexpr int NQC = QK8 ? D / 64 : D / 16;  // MFMA k steps of S (64- or 16-wide d chunks)
   constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
+  typedef typename std::conditional<QK8, i32x8, bf16x8>::type KF;  // K fragment / Q operand
 
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[TILE];
@@ -309,8 +326,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   };
 
   // ---- Q tile -> VGPRs (B operand of S^T = K Q^T) ----------------------------------------
-  bf16x8 qf[NQC];
-  if constexpr (FP8) {
+  KF qf[NQC];
+  if constexpr (QK8) {
+    // 32 codes per lane: d = 64c + 32hh .. +31 of the lane's row (the f8f6f4 operand layout)
+    const unsigned char* qp = (const unsigned char*)a.q + (head_row0 + (qvalid ? qrow : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      const u32x4 lo = *(const u32x4*)(qp + c * 64 + hh * 32);
+      const u32x4 hi = *(const u32x4*)(qp + c * 64 + hh * 32 + 16);
+      const i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      qf[c] = qvalid ? v : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  } else if constexpr (FP8) {
     const unsigned char* qp = (const unsigned char*)a.q + (head_row0 + (qvalid ? qrow : 0)) * D;
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
@@ -330,7 +357,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // ---- direct HBM -> LDS loads ---------------------------------------------------------
   // K rows: 16-byte chunk ch of row r sits at chunk position ch ^ kswz(r).
   // V rows: chunk ch of row r sits at ch ^ vswz(r).
-  auto kswz = [](int r) { return (r / RP256) % CPR; };
+  auto kswz = [](int r) { return (r / KRP256) % KCPR; };
   auto vswz = [](int r) { return 4 * ((r / RP256) % (CPR / 4)); };
   // The buffer descriptor of a step starts at its first key row and covers the rows
   // left in the head, so every row past N reads as zero (range-checked on the lane
@@ -341,19 +368,23 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * HROWB), (short)0,
                                              max(N - k0, 0) * HROWB, 0x00020000);
   };
-  int koff[LPW], voff[LPW];  // byte offsets within a tile, per direct load of this wave
+  int koff[KLPW], voff[LPW];  // byte offsets within a tile, per direct load of this wave
+#pragma unroll
+  for (int r = 0; r < KLPW; ++r) {
+    const int ld = wave * KLPW + r;
+    const int row = ld * KRPL + lane / KCPR;
+    koff[r] = row * KROWB + ((lane % KCPR) ^ kswz(row)) * 16;
+  }
 #pragma unroll
   for (int r = 0; r < LPW; ++r) {
     const int ld = wave * LPW + r;
     const int row = ld * RPL + lane / CPR;
-    const int pos = lane % CPR;
-    koff[r] = row * ROWB + (pos ^ kswz(row)) * 16;
-    voff[r] = row * ROWB + (pos ^ vswz(row)) * 16;
+    voff[r] = row * ROWB + ((lane % CPR) ^ vswz(row)) * 16;
   }
   auto issue_k = [&](int k0, lds_u8* dst) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
 #pragma unroll
-    for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, koff[r]);
+    for (int r = 0; r < KLPW; ++r) load_lds16(rs, dst + (wave * KLPW + r) * 1024, koff[r]);
   };
   auto issue_v = [&](int k0, lds_u8* dst) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
@@ -389,7 +420,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     }
   }
   auto stage_k = [&](int k0) {
-    if constexpr (FP8) {
+    if constexpr (!DIRECT_K) {
       const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
 #pragma unroll
       for (int j = 0; j < SCH; ++j)
@@ -405,7 +436,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     }
   };
   auto commit_k_chunk = [&](lds_u8* dst, int j) {
-    if constexpr (FP8)
+    if constexpr (!DIRECT_K)
       *(__attribute__((address_space(3))) u32x4*)(dst + stpos[j]) = e4m3x8_to_bf16x8(kst[j].x, kst[j].y);
   };
   auto commit_v_chunk = [&](lds_u8* dst, int j) {
@@ -423,17 +454,26 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // the tiles of step s (bf16: requested straight into LDS; fp8: committed from the
   // staging registers, then the tiles of the step after are staged)
   auto wait_tiles = [&]() {
-    if constexpr (FP8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's chunk writes
-    else wait_vmem();                                                        // this wave's direct loads
+    if constexpr (DIRECT_K && DIRECT_V) wait_vmem();  // this wave's direct loads
+    else if constexpr (DIRECT_K) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // both kinds
+    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's chunk writes
   };
 
   // ---- LDS read addressing -------------------------------------------------------------
-  // K (A operand of S^T): lane reads row 32*bk + l32, chunk 2c + hh.
-  int kread[NQC];
+  // K (A operand of S^T): lane reads row 32*bk + l32, chunk 2c + hh (16-bit rows), or the
+  // two chunks 4c + 2hh and 4c + 2hh + 1 (e4m3 rows: 32 codes per lane).
+  int kread[NQC][QK8 ? 2 : 1];
   {
     const int sw = kswz(l32);  // the same for rows l32 and 32 + l32
 #pragma unroll
-    for (int c = 0; c < NQC; ++c) kread[c] = l32 * ROWB + ((2 * c + hh) ^ sw) * 16;
+    for (int c = 0; c < NQC; ++c) {
+      if constexpr (QK8) {
+        kread[c][0] = l32 * KROWB + ((4 * c + 2 * hh) ^ sw) * 16;
+        kread[c][1] = l32 * KROWB + ((4 * c + 2 * hh + 1) ^ sw) * 16;
+      } else {
+        kread[c][0] = l32 * ROWB + ((2 * c + hh) ^ sw) * 16;
+      }
+    }
   }
   // V^T (A operand of O^T): two 16-lane transposing reads per MFMA.  Within a 16-lane
   // group, source lane 4e + a addresses key row key_e and the 4 d values
@@ -449,8 +489,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       vread[db] = row * ROWB + (chunk ^ vswz(row)) * 16 + (aa & 1) * 8;
     }
   }
-  auto kfrag = [&](const lds_u8* kt, int bk, int c) {
-    return *(const __attribute__((address_space(3))) bf16x8*)(kt + bk * 32 * ROWB + kread[c]);
+  auto kfrag = [&](const lds_u8* kt, int bk, int c) -> KF {
+    if constexpr (QK8) {
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+      const u32x4 lo = *(const lds_u32x4*)(kt + bk * 32 * KROWB + kread[c][0]);
+      const u32x4 hi = *(const lds_u32x4*)(kt + bk * 32 * KROWB + kread[c][1]);
+      return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      return *(const __attribute__((address_space(3))) bf16x8*)(kt + bk * 32 * ROWB + kread[c][0]);
+    }
+  };
+  // S^T += K Q^T for one MFMA k step
+  auto qk_mma = [&](const KF& ka, const KF& qb, const f32x16& acc) -> f32x16 {
+    if constexpr (QK8)  // A and B as OCP e4m3 (format 0), unit E8M0 block scales (127 = 2^0)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qb, acc, 0, 0, 0, 127, 0, 127);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, acc, 0, 0, 0);
   };
   auto vfrag = [&](const lds_u8* vt, int ks, int db) {
     const lds_u8* base = vt + ks * 16 * ROWB + vread[db];
@@ -689,7 +743,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // slices formed under the MFMAs of the slice before; both read their LDS fragments
   // PD MFMAs ahead, with scheduling fences between the MFMAs.
   auto qk_sched = [&](const lds_u8* kt, f32x16 (&sacc)[2]) {
-    bf16x8 fr[PD + 1];
+    KF fr[PD + 1];
     static_for<PD>([&](auto ic) { fr[ic.value] = kfrag(kt, ic.value & 1, ic.value >> 1); });
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -697,7 +751,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     static_for<NQ>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + PD < NQ) fr[(i + PD) % (PD + 1)] = kfrag(kt, (i + PD) & 1, (i + PD) >> 1);
-      sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], sacc[i & 1], 0, 0, 0);
+      sacc[i & 1] = qk_mma(fr[i % (PD + 1)], qf[i >> 1], sacc[i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -720,7 +774,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       sacc[bk] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NQC; ++c)
-        sacc[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kt, bk, c), qf[c], sacc[bk], 0, 0, 0);
+        sacc[bk] = qk_mma(kfrag(kt, bk, c), qf[c], sacc[bk]);
     }
   };
   auto pv_full = [&](const lds_u8* vt, const bf16x8 (&pf)[4]) {
@@ -741,18 +795,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // staged)
   const int np_steps = 2 * npart;
   if (nsteps > 0) {
-    if constexpr (FP8) {
-      stage_k(step_k0_first(0));
-      stage_v(step_k0_first(0));
-      commit_k(kl0);
-      commit_v(vl0);
-      if (1 < nsteps) {
-        stage_k(step_k0_first(1));
-        stage_v(step_k0_first(1));
-      }
-    } else {
+    if constexpr (DIRECT_K) {
       issue_k(step_k0_first(0), kl0);
+    } else {
+      stage_k(step_k0_first(0));
+      commit_k(kl0);
+      if (1 < nsteps) stage_k(step_k0_first(1));
+    }
+    if constexpr (DIRECT_V) {
       issue_v(step_k0_first(0), vl0);
+    } else {
+      stage_v(step_k0_first(0));
+      commit_v(vl0);
+      if (1 < nsteps) stage_v(step_k0_first(1));
     }
   }
   for (int s = 0; s < np_steps; ++s) {
@@ -761,16 +816,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     wait_tiles();
     __syncthreads();  // K(s), V(s) in; every read of step s-1 done
     if (s + 1 < nsteps) {
-      if constexpr (FP8) {
-        commit_k((s & 1) ? kl0 : kl1);
-        commit_v((s & 1) ? vl0 : vl1);
-        if (s + 2 < nsteps) {
-          stage_k(step_k0(s + 2));
-          stage_v(step_k0(s + 2));
-        }
-      } else {
+      if constexpr (DIRECT_K) {
         issue_k(step_k0_first(s + 1), (s & 1) ? kl0 : kl1);
+      } else {
+        commit_k((s & 1) ? kl0 : kl1);
+        if (s + 2 < nsteps) stage_k(step_k0(s + 2));
+      }
+      if constexpr (DIRECT_V) {
         issue_v(step_k0_first(s + 1), (s & 1) ? vl0 : vl1);
+      } else {
+        commit_v((s & 1) ? vl0 : vl1);
+        if (s + 2 < nsteps) stage_v(step_k0(s + 2));
       }
     }
     const int k0 = step_k0(s);
@@ -797,15 +853,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   //   exponential pairs of P(s) start in slots [E, WP), pair k in slot E + k(WP-E)/16,
   //   its later stages one and two slots on, each packed before the P.V MFMA that
   //   consumes it; the transform and maximum of
-  //   S(s+1) take slots [WP, NS), after its MFMAs have completed.  Scheduling fences
+  //   S(s+1) take slots [PS, NS), after its MFMAs have completed.  Scheduling fences
   //   between the slots keep this interleaving, so the VALU work of a slot runs under
-  //   that slot's MFMA.
-  constexpr int E = 2;                 // slots issued before the loads and the rescale
-  constexpr int WP = NQ + NP / 2;
-  constexpr int EPS = 32 / (NS - WP);  // S(s+1) elements per maximum slot
+  //   that slot's MFMA.  (With the e4m3 Q.K^T a step has only NQ = 2*D/64 Q.K^T MFMAs, each
+  //   of twice the work: the loads and rescale follow the first slot or none, and the
+  //   exponentials are packed closer so that slice 0 is ready for the first P.V MFMA.)
+  constexpr int E = QK8 ? (D == 128 ? 1 : 0) : 2;  // slots issued before the loads and the rescale
+  constexpr int WP = QK8 ? (D == 128 ? 11 : 5) : NQ + NP / 2;
+  constexpr int PS = QK8 ? (D == 128 ? 8 : 4) : WP;  // first slot of the maximum of S(s+1)
   constexpr bool PRE = MODE == kSoftcap;  // softcap scores reach the loop raw
   constexpr int NSTG = PRE ? 3 : 2;       // slots a pair's stages span
-  static_assert(EPS * (NS - WP) == 32, "maximum slots");
+  static_assert(PS >= NQ && PS < NS, "maximum slots");
   // pair k starts in slot E + k(WP - E)/16
   static_assert(E + ((4 * 0 + 3) * (WP - E)) / 16 + NSTG - 1 < NQ + NDB * 0 &&
                     E + ((4 * 1 + 3) * (WP - E)) / 16 + NSTG - 1 < NQ + NDB * 1 &&
@@ -823,27 +881,25 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     // from the staging registers one 16-byte chunk per slot from slot E on, each tile
     // restaged -- K(s+3), V(s+2) -- after its last chunk; the last step commits nothing)
     float moff = 0.f;
+    constexpr int VC0 = E + (DIRECT_K ? 0 : SCH);  // first slot of the V chunk commits
     auto fp8_tiles = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (FP8 && ISSUE_K && i >= E && i < E + SCH) {
+      if constexpr (!DIRECT_K && ISSUE_K && i >= E && i < E + SCH) {
         commit_k_chunk(kcur, i - E);
         if constexpr (i == E + SCH - 1) {
           if (s + 3 < nsteps) stage_k(step_k0(s + 3));
         }
       }
-      if constexpr (FP8 && NEXT && i >= E + SCH && i < E + 2 * SCH) {
-        commit_v_chunk(vnext, i - E - SCH);
-        if constexpr (i == E + 2 * SCH - 1) {
+      if constexpr (!DIRECT_V && NEXT && i >= VC0 && i < VC0 + SCH) {
+        commit_v_chunk(vnext, i - VC0);
+        if constexpr (i == VC0 + SCH - 1) {
           if (s + 2 < nsteps) stage_v(step_k0(s + 2));
         }
       }
     };
     auto loads_and_rescale = [&]() {
-      if constexpr (FP8) {
-      } else {
-        if constexpr (ISSUE_K) issue_k(step_k0(s + 2), kcur);
-        if constexpr (NEXT) issue_v(step_k0(s + 1), vnext);
-      }
+      if constexpr (DIRECT_K && ISSUE_K) issue_k(step_k0(s + 2), kcur);
+      if constexpr (DIRECT_V && NEXT) issue_v(step_k0(s + 1), vnext);
       scales_e(step_k0(s));
       moff = rescale(mcur, step_k0(s));
     };
@@ -853,13 +909,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       const int k1 = step_k0(s + 1);
       const int kq1 = k1 + 4 * hh - qrow;
       scales_p(k1);
-      auto frag = [&](int i) -> bf16x8 {
-        if (i < NQ) return kfrag(knext, i & 1, i >> 1);
-        const int j = i - NQ;
-        return vfrag(vcur, j / NDB, j % NDB);
+      // fragment of slot i, read PD slots ahead: K fragments (slots below NQ) and V
+      // fragments in rings of their own, both indexed by the slot
+      KF kr[PD + 1];
+      bf16x8 vr[PD + 1];
+      auto frag = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < NQ) kr[i % (PD + 1)] = kfrag(knext, i & 1, i >> 1);
+        else vr[i % (PD + 1)] = vfrag(vcur, (i - NQ) / NDB, (i - NQ) % NDB);
       };
-      bf16x8 fr[PD + 1];
-      static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic.value); });
+      static_for<PD>([&](auto ic) { frag(ic); });
       snext[0] = f32x16{};
       snext[1] = f32x16{};
       uint32_t pk[16];
@@ -873,13 +932,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
           __builtin_amdgcn_sched_barrier(0);
         }
         fp8_tiles(ic);
-        if constexpr (i + PD < NS) fr[(i + PD) % (PD + 1)] = frag(i + PD);
+        if constexpr (i + PD < NS) frag(std::integral_constant<int, i + PD>{});
         if constexpr (i < NQ) {
-          snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (PD + 1)], qf[i >> 1], snext[i & 1], 0, 0, 0);
+          snext[i & 1] = qk_mma(kr[i % (PD + 1)], qf[i >> 1], snext[i & 1]);
         } else {
           constexpr int j = i - NQ, ks = j / NDB, db = j % NDB;
           const u32x4 v4 = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
-          oacc[db] = pv_mma(fr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4), oacc[db]);
+          oacc[db] = pv_mma(vr[i % (PD + 1)], __builtin_bit_cast(bf16x8, v4), oacc[db]);
         }
         // pair k: stages in slots a(k) (+1, +2), a(k) = E + k(WP - E)/16; the
         // instructions of one slot come from different pairs and do not wait on each other
@@ -915,9 +974,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
             pin(ls);
           }
         });
-        if constexpr (i >= WP) {
-          static_for<EPS>([&](auto ec) {
-            constexpr int idx = (i - WP) * EPS + decltype(ec)::value, bk = idx >> 4, r = idx & 15;
+        if constexpr (i >= PS) {
+          // S(s+1) elements [32(i - PS)/(NS - PS), 32(i - PS + 1)/(NS - PS)) in this slot
+          constexpr int e0 = 32 * (i - PS) / (NS - PS), e1 = 32 * (i - PS + 1) / (NS - PS);
+          static_for<e1 - e0>([&](auto ec) {
+            constexpr int idx = e0 + decltype(ec)::value, bk = idx >> 4, r = idx & 15;
             float sv = snext[bk][r];
             pin(sv);
             const float x = xform(sv, bk, r, kq1);
@@ -943,11 +1004,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     wait_tiles();
     __syncthreads();  // K(t) in; every read of step t-1 done
     if (t + 1 < nsteps) {
-      if constexpr (FP8) {
+      if constexpr (DIRECT_K) {
+        issue_k(step_k0_first(t + 1), kl1);
+      } else {
         commit_k(kl1);
         if (t + 2 < nsteps) stage_k(step_k0(t + 2));
-      } else {
-        issue_k(step_k0_first(t + 1), kl1);
       }
     }
     qk_full(kl0, sa);
@@ -989,24 +1050,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 
 // Launches the variant (masked, mode, generic modifiers) chosen on the host; a
 // document mask is never launched without a block map (causal and window masks may
-// come without one: the kernel derives their lists).
-template <int D, bool FP8>
+// come without one: the kernel derives their lists).  With the e4m3 Q.K^T (QK8) a
+// softcap without ALiBi runs in the generic mode (its transform before the maximum).
+template <int D, bool FP8, bool QK8>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st) {
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
   if (masked && a.map == nullptr && (a.mflags & kDocument)) return hipErrorInvalidValue;
   if (FP8 && (!a.q_scale || !a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
+  if (QK8 && mode == kSoftcap) {
+    mode = kGeneric;
+    galibi = false;
+    gsoftcap = true;
+  }
+  constexpr int kSC = QK8 ? kGeneric : kSoftcap;   // the softcap-only mode
+  constexpr bool kSCA = false, kSCS = QK8;         // its generic modifiers
+  const bool softcap_only = QK8 ? (mode == kGeneric && !galibi && gsoftcap) : mode == kSoftcap;
   if (masked) {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kLinear, false, false>), grid, block, 0, st, a);
-    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kSoftcap, false, false>), grid, block, 0, st, a);
-    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, true, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kLinear, false, false>), grid, block, 0, st, a);
+    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kSC, kSCA, kSCS>), grid, block, 0, st, a);
+    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;
   } else {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kLinear, false, false>), grid, block, 0, st, a);
-    else if (mode == kSoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kSoftcap, false, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, false, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kLinear, false, false>), grid, block, 0, st, a);
+    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kSC, kSCA, kSCS>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;  // (ALiBi on a causal mask always has a block map)
   }
   return hipGetLastError();

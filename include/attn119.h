@@ -87,10 +87,14 @@ enum {
 enum {
   ATTN_QK_BF16 = 0, /* Q and K codes widened exactly to bf16, bf16 MFMA with fp32 accumulation:
                        scores exact to fp32 rounding (the accurate mode) */
-  ATTN_QK_E4M3 = 1  /* Q.K^T on the e4m3 MFMA (twice the bf16 rate).  gfx950 sums the products
-                       of one fp8 MFMA to about 2^-13 of the largest product, so a score
-                       dominated by a few large channels (outlier features) carries an error
-                       of that size */
+  ATTN_QK_E4M3 = 1  /* Q.K^T on the e4m3 MFMA (twice the bf16 rate), P.V as ATTN_PV_F16.
+                       gfx950's f8f6f4 MFMA truncates its 64-term sums at about 2^-14 of the
+                       largest product (measured), so a score dominated by a few large
+                       products (outlier features) carries an error of that size relative
+                       to them: on four x20 channels the LSE error at |LSE| ~ 600 is ~0.07
+                       without and ~3e-3 with incoherent processing (attn_fp8_quantize's
+                       rotation of Q and K), O within 6e-2 beyond bf16 rounding with it.
+                       A measured mode: the accurate one is ATTN_QK_BF16 */
 };
 
 /*
@@ -194,8 +198,7 @@ attn_status attn_check_args(const void* q, const void* k, const void* v, void* o
  *   dtype        : ATTN_BF16 or ATTN_FP8_E4M3 (then `fp8` is required).
  *   mask         : NULL for plain attention.
  *   blockmap     : built by attn_blockmap_build for the same (B, N, mask).  Required
- *                  with DOCUMENT (and with fp8 qk_mode ATTN_QK_E4M3 under any
- *                  CAUSAL/WINDOW mask).  With CAUSAL and/or WINDOW alone it may be
+ *                  with DOCUMENT.  With CAUSAL and/or WINDOW alone it may be
  *                  NULL: every row then sees one interval of keys whose ends grow with
  *                  the row, and the kernel derives the same block lists and row
  *                  intervals from the flags (bit-identical results, no map launch).

@@ -94,7 +94,7 @@ def test_check_args_ok_and_errors(L):
     assert ck(mask=L.make_mask(L.ATTN_CAUSAL | L.ATTN_WINDOW, window=5)) == L.ATTN_OK
     assert ck(mask=L.make_mask(L.ATTN_DOCUMENT | L.ATTN_CAUSAL, doc_id=P)) == L.ATTN_ERR_BAD_BLOCKMAP
     f8 = L.make_fp8(P, P, P, qk_mode=L.ATTN_QK_E4M3)
-    assert ck(mask=m, dtype=1, fp8=f8) == L.ATTN_ERR_BAD_BLOCKMAP
+    assert ck(mask=m, dtype=1, fp8=f8) == L.ATTN_OK
     assert ck(mask=m, dtype=1, fp8=f8, blockmap=P, blockmap_bytes=nbytes) == L.ATTN_OK
     assert ck(mask=m, dtype=1, fp8=L.make_fp8(P, P, P)) == L.ATTN_OK
     assert ck(mask=m, blockmap=P, blockmap_bytes=nbytes - 1) == L.ATTN_ERR_BAD_BLOCKMAP
@@ -203,8 +203,8 @@ def test_kernel_variant_selection(L):
     assert L.attn_fwd_kernel_name(128, 1, L.make_mask(C | WI | SC, window=9, softcap=50.0), fp8) == \
         "fp8 d128 masked softcap"
     fp8q = L.make_fp8(P, P, P, qk_mode=L.ATTN_QK_E4M3)
-    assert L.attn_fwd_kernel_name(128, 1, None, fp8q) == "fp8-qk8 d128 unmasked none"
-    assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8q) == "fp8-qk8 d64 masked alibi"
+    assert L.attn_fwd_kernel_name(128, 1, None, fp8q) == "fp8-qk8 d128 unmasked linear"
+    assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8q) == "fp8-qk8 d64 masked alibi-causal"
     assert L.attn_fwd_kernel_name(96, 0, None, None) is None
     assert L.attn_fwd_kernel_name(128, 1, None, None) is None
 

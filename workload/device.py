@@ -76,8 +76,7 @@ def build_map(dp: DeviceProblem, stream=None) -> None:
 def needs_map(dp: DeviceProblem) -> bool:
     """Whether the forward pass needs a block map: document masks and packed batches do;
     causal and window masks on the bf16 path derive their block lists in the kernel."""
-    qk8 = dp.fp8 is not None and dp.fp8.qk_mode == L.ATTN_QK_E4M3
-    return dp.blockmap is not None and (dp.cu_seqlens is not None or bool(dp.p.flags & L.ATTN_DOCUMENT) or qk8)
+    return dp.blockmap is not None and (dp.cu_seqlens is not None or bool(dp.p.flags & L.ATTN_DOCUMENT))
 
 
 def forward(dp: DeviceProblem, rescale_tau: float = 8.0, stream=None, use_map: bool = True) -> None:
