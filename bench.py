@@ -264,6 +264,26 @@ class ClockSampler:
                 "source": self.source, "peak_mhz": 2400}
 
 
+def rescale_events(torch, dp) -> dict:
+    """Mean rescale events per query row of the online softmax at tau = 0 and tau = 8
+    (attn_fwd_rescale_counts; one untimed pass each), the first visible step excluded."""
+    from exact_attention_119_amd import lib as L
+    from workload import device as WD
+    p = dp.p
+    out = {}
+    counts = torch.empty((p.B, p.H, p.N), dtype=torch.int32, device="cuda")
+    for tau in (0.0, 8.0):
+        if WD.needs_map(dp):
+            WD.build_map(dp)
+        L.attn_fwd_rescale_counts(dp.q, dp.k, dp.v, dp.o, dp.lse, counts, scale=p.scale, dtype=dp.dtype,
+                                  mask=dp.mask, blockmap=dp.blockmap if WD.needs_map(dp) else None, rescale_tau=tau)
+        torch.cuda.synchronize()
+        out[f"tau{tau:g}_per_row_after_first"] = round(float((counts.double() - 1).mean().item()), 5)
+    r0, r8 = out["tau0_per_row_after_first"], out["tau8_per_row_after_first"]
+    out["ratio_tau0_over_tau8"] = round(r0 / r8, 2) if r8 > 0 else None
+    return out
+
+
 def loop_ms(torch, stream, n: int, launch) -> float:
     """Average duration of `launch` over n back-to-back calls on `stream` (HIP events)."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -608,6 +628,8 @@ def main(argv=None):
         out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs / HBM_PEAK_GBS, 5), "achieved_tflops": round(achieved, 3),
                                 "algorithmic_bytes": alg_bytes})
+    if p.dtype == "bf16" and p.cu_seqlens is None:
+        out["config"]["rescale_events"] = rescale_events(torch, dp)
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)

@@ -30,7 +30,7 @@ hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N
 constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
 namespace bf16path {
 constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
-template <int D, bool FP8, bool QK8>
+template <int D, bool FP8, bool QK8, bool COUNT>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st);
 }  // namespace bf16path
 }  // namespace attn119
@@ -267,10 +267,16 @@ const char* attn_fwd_kernel_name(int32_t d, int32_t dtype, const attn_mask* mask
   return variant_name(select_variant(d, dtype, mask, fp8));
 }
 
-attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                         int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
-                         const attn_mask* mask, const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8,
-                         float rescale_tau, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass behind attn_fwd_gqa and attn_fwd_rescale_counts (counts: null, or
+// device int32 [B][H][N] for the rescale events of every query row).
+attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
+                     int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
+                     const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
+                     int32_t* counts, void* stream) {
   const attn_status st = attn_check_args_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap,
                                              blockmap_bytes, fp8, rescale_tau);
   if (st != ATTN_OK) return st;
@@ -297,6 +303,7 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
     a.cap2 = (float)((double)mask->softcap * kLog2e);
   }
   a.tau = rescale_tau;
+  a.rescale_counts = counts;
   a.alibi_exp = (float)(-8.0 / (double)H);
   a.alibi_slopes = (alibi && mask) ? mask->alibi_slopes : nullptr;
   if (dtype == ATTN_FP8_E4M3) {
@@ -330,16 +337,41 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   hipError_t e;
   const hipStream_t s = (hipStream_t)stream;
   const FwdVariant var = select_variant(d, dtype, mask, fp8);
-  if (dtype == ATTN_BF16)
-    e = d == 128 ? bf16path::launch<128, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+  if (counts)  // (bf16 only: checked by the entry point)
+    e = d == 128 ? bf16path::launch<128, false, false, true>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, false, false, true>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+  else if (dtype == ATTN_BF16)
+    e = d == 128 ? bf16path::launch<128, false, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, false, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else if (fp8->qk_mode == ATTN_QK_BF16)
-    e = d == 128 ? bf16path::launch<128, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, true, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else
-    e = d == 128 ? bf16path::launch<128, true, true>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, true, true>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, true, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                         int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
+                         const attn_mask* mask, const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8,
+                         float rescale_tau, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap, blockmap_bytes, fp8,
+                  rescale_tau, nullptr, stream);
+}
+
+attn_status attn_fwd_rescale_counts(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int32_t* counts, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                    float scale, int32_t dtype, const attn_mask* mask, const void* blockmap,
+                                    size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau, void* stream) {
+  if (!counts || (reinterpret_cast<uintptr_t>(counts) & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;  // the counting kernels are built for bf16 inputs
+  return fwd_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap, blockmap_bytes, fp8,
+                  rescale_tau, counts, stream);
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,

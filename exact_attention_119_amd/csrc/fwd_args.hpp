@@ -28,6 +28,7 @@ struct FwdArgs {
   uint32_t mflags;            // positional mask flags the map was built for
   int window;
   int order;                  // work order: kOrderHeadMajor or kOrderHeavyFirst
+  int* rescale_counts;        // [B][H][N] rescale events per query row, or null (not counted)
 };
 
 // Order in which workgroups take (b*H + h, row block) work items.  Workgroup L runs on

@@ -152,10 +152,12 @@ __host__ __device__ constexpr int key_off(int bk, int r) { return 32 * bk + 8 * 
 //           sums a 64-term dot product with about 14 bits below its largest product
 //           (measured; truncating), so a score dominated by a few large products carries
 //           an error of that size.
+//   COUNT   also count each row's rescale events into a.rescale_counts (a separate
+//           instantiation, so that the counter costs the other kernels no register)
 //   MASKED  positional mask through the block map (else: all keys visible)
 //   MODE    score-modifier mode (kLinear, kSoftcap, kAlibiCausal, kGeneric)
 //   GALIBI, GSOFTCAP  modifiers of the generic mode
-template <int D, bool FP8, bool QK8, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
+template <int D, bool FP8, bool QK8, bool COUNT, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
 __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) {
   static_assert(FP8 || !QK8, "the e4m3 Q.K^T takes e4m3 inputs");
   static_assert(!(QK8 && MODE == kSoftcap), "softcap with e4m3 Q.K^T runs in the generic mode");
@@ -569,6 +571,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_used = ninf;
   float l_sum = 0.f;   // row sum of p (fp32, before rounding): LSE; for bf16 also the normaliser of O
+  int nres = 0;        // steps in which this row's offset was replaced (rescale events)
 
   // ---- score modifiers, mask and row maximum ---------------------------------------------
   // Score of one accumulator element before the maximum is taken (kq = k0 + 4hh - q):
@@ -716,6 +719,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float alpha = need ? exp2_(m_used - m_new) : 1.f;
       m_used = need ? m_new : m_used;
+      if constexpr (COUNT) nres += need ? 1 : 0;
       l_sum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
@@ -1045,6 +1049,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     else if (l_sum > 0.f) lse = (m_used + __builtin_amdgcn_logf(l_sum)) * 0.6931471805599453f;
     else lse = ninf;
     a.lse[head_row0 + qrow] = lse;
+    if constexpr (COUNT) a.rescale_counts[head_row0 + qrow] = nres;
   }
 }
 
@@ -1052,8 +1057,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 // document mask is never launched without a block map (causal and window masks may
 // come without one: the kernel derives their lists).  With the e4m3 Q.K^T (QK8) a
 // softcap without ALiBi runs in the generic mode (its transform before the maximum).
-template <int D, bool FP8, bool QK8>
+template <int D, bool FP8, bool QK8, bool COUNT>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st) {
+  if (COUNT != (a.rescale_counts != nullptr)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
   if (masked && a.map == nullptr && (a.mflags & kDocument)) return hipErrorInvalidValue;
   if (FP8 && (!a.q_scale || !a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
@@ -1066,17 +1072,17 @@ hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gso
   constexpr bool kSCA = false, kSCS = QK8;         // its generic modifiers
   const bool softcap_only = QK8 ? (mode == kGeneric && !galibi && gsoftcap) : mode == kSoftcap;
   if (masked) {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kLinear, false, false>), grid, block, 0, st, a);
-    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kSC, kSCA, kSCS>), grid, block, 0, st, a);
-    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, true, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kLinear, false, false>), grid, block, 0, st, a);
+    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kSC, kSCA, kSCS>), grid, block, 0, st, a);
+    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;
   } else {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kLinear, false, false>), grid, block, 0, st, a);
-    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kSC, kSCA, kSCS>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, false, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kLinear, false, false>), grid, block, 0, st, a);
+    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kSC, kSCA, kSCS>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;  // (ALiBi on a causal mask always has a block map)
   }
   return hipGetLastError();

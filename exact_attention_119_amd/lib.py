@@ -42,7 +42,8 @@ ATTN_QK_E4M3 = 1
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
-           "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa", "attn_bwd_gqa_noalloc")
+           "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa", "attn_bwd_gqa_noalloc",
+           "attn_fwd_rescale_counts")
 
 
 class AttnError(RuntimeError):
@@ -100,6 +101,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
                                  vp, sz, ctypes.POINTER(attn_fp8), f32, vp]
     lib.attn_fwd_gqa.restype = i32
+    lib.attn_fwd_rescale_counts.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                            ctypes.POINTER(attn_mask), vp, sz, ctypes.POINTER(attn_fp8), f32, vp]
+    lib.attn_fwd_rescale_counts.restype = i32
     lib.attn_varlen_workspace_bytes.argtypes = [i32, ctypes.POINTER(attn_mask), ctypes.POINTER(sz)]
     lib.attn_varlen_workspace_bytes.restype = i32
     lib.attn_varlen_prepare.argtypes = [vp, i32, i32, ctypes.POINTER(attn_mask), vp, sz, vp]
@@ -229,6 +233,21 @@ def attn_fwd_gqa(q, k, v, o, lse, *, scale: float, dtype: int = ATTN_BF16, mask:
                                int(dtype), ctypes.byref(mask) if mask else None, _ptr(blockmap), mbytes,
                                ctypes.byref(fp8) if fp8 else None, float(rescale_tau), _stream(stream)),
            "attn_fwd_gqa")
+
+
+def attn_fwd_rescale_counts(q, k, v, o, lse, counts, *, scale: float, dtype: int = ATTN_BF16,
+                            mask: Optional[attn_mask] = None, blockmap=None, fp8: Optional[attn_fp8] = None,
+                            rescale_tau: float = 8.0, stream=None) -> None:
+    """attn_fwd_gqa that also writes the rescale events of every query row into counts
+    (int32 [B][H][N])."""
+    B, H, N, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[1])
+    mbytes = 0 if blockmap is None else blockmap.numel() * blockmap.element_size()
+    _check(load().attn_fwd_rescale_counts(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(counts), B, H, H_kv,
+                                          N, d, float(scale), int(dtype), ctypes.byref(mask) if mask else None,
+                                          _ptr(blockmap), mbytes, ctypes.byref(fp8) if fp8 else None,
+                                          float(rescale_tau), _stream(stream)),
+           "attn_fwd_rescale_counts")
 
 
 def attn_varlen_workspace_bytes(total: int, mask: Optional[attn_mask] = None) -> int:

@@ -237,6 +237,27 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
                          const attn_fp8* fp8, float rescale_tau, void* stream);
 
 /*
+ * The forward pass of attn_fwd_gqa that also counts, for every query row, its rescale
+ * events: the steps (64 keys each) in which the row's running maximum exceeded the offset
+ * in use by more than rescale_tau, so that the offset was replaced and the accumulator
+ * rescaled (the first step with a visible key always counts).  The measurement behind the
+ * page "FlashAttention 4: ... για LLMs" (el.linux-konsole.com), section "Έξυπνος
+ * επανακανονισμός Softmax ...": rescaling only on a significant growth of the maximum
+ * makes rescales rare.  The count depends on the kernel's step order (for a query block:
+ * its PARTIAL key blocks ascending, then its FULL ones ascending; without a positional
+ * mask and N a multiple of 128, all key blocks ascending).
+ *   counts: device int32 [B][H][N], 4-byte aligned; every row is written.
+ * bf16 inputs only (a separate instantiation of the kernels, so the counter costs the
+ * other kernels nothing).  O and LSE are those of attn_fwd_gqa.  Errors as attn_fwd_gqa,
+ * plus ATTN_ERR_INVALID_ARG for a null or misaligned counts and ATTN_ERR_UNSUPPORTED for
+ * fp8 inputs.
+ */
+attn_status attn_fwd_rescale_counts(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int32_t* counts, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                    float scale, int32_t dtype, const attn_mask* mask, const void* blockmap,
+                                    size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau, void* stream);
+
+/*
  * Variable-length batches (varlen): sequences of different lengths packed one after
  * another without padding, the other gap the page "FlashAttention 4: ... για LLMs"
  * (el.linux-konsole.com) names in its section "Συμβατότητα και τρέχουσα κατάσταση".
