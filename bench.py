@@ -78,7 +78,7 @@ def arithmetic_dtype(dp) -> str:
         return "bf16"
     from exact_attention_119_amd import lib as L
     qk = "e4m3" if dp.fp8.qk_mode == L.ATTN_QK_E4M3 else "bf16"
-    pv = "e4m3" if dp.fp8.pv_mode == L.ATTN_PV_E4M3 else "f16"
+    pv = {L.ATTN_PV_E4M3: "e4m3", L.ATTN_PV_FP4: "e2m1 (E8M0 block scales)"}.get(dp.fp8.pv_mode, "f16")
     return f"{qk} QK^T + {pv} PV (e4m3 inputs)"
 
 
@@ -474,6 +474,8 @@ def main(argv=None):
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--qk8", action="store_true",
                     help="fp8 workloads: Q.K^T on the e4m3 MFMA (a measured mode, see the design notes)")
+    ap.add_argument("--pv", choices=["f16", "e4m3", "fp4"], default="f16",
+                    help="fp8 workloads with --qk8: P.V precision (e4m3 or fp4 P are measured modes)")
     ap.add_argument("--rotate", action="store_true",
                     help="configuration 5 with incoherent processing: Q and K quantised after the rotation")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -531,7 +533,8 @@ def main(argv=None):
     name = workload_name(p)
     log(f"bench: {name}; generating done, staging to HBM")
     from exact_attention_119_amd import lib as L
-    dp = WD.to_device(p, qk_mode=L.ATTN_QK_E4M3 if args.qk8 else L.ATTN_QK_BF16)
+    pv_mode = {"f16": L.ATTN_PV_F16, "e4m3": L.ATTN_PV_E4M3, "fp4": L.ATTN_PV_FP4}[args.pv]
+    dp = WD.to_device(p, qk_mode=L.ATTN_QK_E4M3 if args.qk8 else L.ATTN_QK_BF16, pv_mode=pv_mode)
     pairs = visible_pairs(p)
     flop_per_step = 4.0 * p.d * p.H * pairs
     stream = torch.cuda.current_stream()

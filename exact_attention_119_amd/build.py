@@ -32,6 +32,7 @@ SOURCES = [
     "fwd_fp8p_d64.hip",
     "fwd_fp8qk8_d128.hip",
     "fwd_fp8qk8_d64.hip",
+    "fwd_fp8pv_d128.hip",
     "fwd_count_d128.hip",
     "fwd_count_d64.hip",
     "quant.hip",

@@ -27,10 +27,11 @@ hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const
 size_t bwd_scratch_rows();
 hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N, int d, const uint32_t* signs,
                         hipStream_t stream);
-constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2;
+constexpr int kInBf16 = 0, kInFp8 = 1, kInFp8Qk8 = 2, kInFp8Pv8 = 3, kInFp8Pv4 = 4;
 namespace bf16path {
 constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
-template <int D, bool FP8, bool QK8, bool COUNT>
+constexpr int kPvE4m3 = 1, kPvFp4 = 2;
+template <int D, bool FP8, bool QK8, bool COUNT, int PV>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st);
 }  // namespace bf16path
 }  // namespace attn119
@@ -49,7 +50,7 @@ bool positional(const attn_mask* m) { return m && (m->flags & (ATTN_CAUSAL | ATT
 // The compiled kernel variant a call selects (host logic only, testable on a CPU).
 struct FwdVariant {
   int d;
-  int input;     // kInBf16, kInFp8, kInFp8Qk8
+  int input;     // kInBf16, kInFp8, kInFp8Qk8, kInFp8Pv8, kInFp8Pv4
   bool masked;   // positional mask through the block map
   int mode;      // bf16 kernel: score-modifier mode
   bool alibi, softcap;
@@ -60,6 +61,8 @@ FwdVariant select_variant(int32_t d, int32_t dtype, const attn_mask* mask, const
   const uint32_t flags = mask ? mask->flags : 0u;
   v.d = d;
   v.input = dtype == ATTN_BF16 ? kInBf16 : (fp8 && fp8->qk_mode == ATTN_QK_E4M3 ? kInFp8Qk8 : kInFp8);
+  if (v.input == kInFp8Qk8 && fp8->pv_mode == ATTN_PV_E4M3) v.input = kInFp8Pv8;
+  if (v.input == kInFp8Qk8 && fp8->pv_mode == ATTN_PV_FP4) v.input = kInFp8Pv4;
   v.masked = positional(mask);
   v.alibi = flags & ATTN_ALIBI;
   v.softcap = flags & ATTN_SOFTCAP;
@@ -72,13 +75,13 @@ FwdVariant select_variant(int32_t d, int32_t dtype, const attn_mask* mask, const
 // Table of variant names, built once.  A function-local static is initialised exactly
 // once even under concurrent first calls (C++11), so every caller sees it complete.
 struct VariantNames {
-  char names[2][3][2][5][64];
+  char names[2][5][2][5][64];
   VariantNames() {
-    static const char* const kIn[] = {"bf16", "fp8", "fp8-qk8"};
+    static const char* const kIn[] = {"bf16", "fp8", "fp8-qk8", "fp8-qk8-pv8", "fp8-qk8-pv4"};
     static const char* const kMode[] = {"linear", "softcap", "alibi-causal", "generic-alibi",
                                         "generic-alibi-softcap"};
     for (int di = 0; di < 2; ++di)
-      for (int in = 0; in < 3; ++in)
+      for (int in = 0; in < 5; ++in)
         for (int m = 0; m < 2; ++m)
           for (int k = 0; k < 5; ++k)
             std::snprintf(names[di][in][m][k], 64, "%s d%d %s %s", kIn[in], di ? 128 : 64,
@@ -236,8 +239,13 @@ attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, voi
     return ATTN_ERR_INVALID_ARG;
   if (dtype == ATTN_FP8_E4M3) {
     if (!fp8 || !fp8->q_scale || !fp8->k_scale || !fp8->v_scale) return ATTN_ERR_INVALID_ARG;
-    if (fp8->pv_mode != ATTN_PV_F16) return ATTN_ERR_UNSUPPORTED;
     if (fp8->qk_mode != ATTN_QK_BF16 && fp8->qk_mode != ATTN_QK_E4M3) return ATTN_ERR_UNSUPPORTED;
+    if (fp8->pv_mode != ATTN_PV_F16 && fp8->pv_mode != ATTN_PV_E4M3 && fp8->pv_mode != ATTN_PV_FP4)
+      return ATTN_ERR_UNSUPPORTED;
+    // the fp8/fp4 P.V: with the e4m3 Q.K^T, d = 128, no mask and no score modifier
+    if (fp8->pv_mode != ATTN_PV_F16 &&
+        (fp8->qk_mode != ATTN_QK_E4M3 || d != 128 || (mask && mask->flags != 0u)))
+      return ATTN_ERR_UNSUPPORTED;
   }
   if (positional(mask)) {
     // Causal and window masks may come without a map (the kernel derives the block lists
@@ -338,17 +346,21 @@ attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float
   const hipStream_t s = (hipStream_t)stream;
   const FwdVariant var = select_variant(d, dtype, mask, fp8);
   if (counts)  // (bf16 only: checked by the entry point)
-    e = d == 128 ? bf16path::launch<128, false, false, true>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, false, false, true>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, false, false, true, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, false, false, true, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else if (dtype == ATTN_BF16)
-    e = d == 128 ? bf16path::launch<128, false, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, false, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, false, false, false, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, false, false, false, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else if (fp8->qk_mode == ATTN_QK_BF16)
-    e = d == 128 ? bf16path::launch<128, true, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, true, false, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, true, false, false, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true, false, false, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+  else if (fp8->pv_mode == ATTN_PV_E4M3)  // (d = 128: checked)
+    e = bf16path::launch<128, true, true, false, bf16path::kPvE4m3>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+  else if (fp8->pv_mode == ATTN_PV_FP4)
+    e = bf16path::launch<128, true, true, false, bf16path::kPvFp4>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   else
-    e = d == 128 ? bf16path::launch<128, true, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s)
-                 : bf16path::launch<64, true, true, false>(a, var.masked, var.mode, var.alibi, var.softcap, s);
+    e = d == 128 ? bf16path::launch<128, true, true, false, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s)
+                 : bf16path::launch<64, true, true, false, 0>(a, var.masked, var.mode, var.alibi, var.softcap, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -60,6 +60,8 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // score-modifier modes
 constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
+// P.V precision (PV): the 16-bit MFMA; e4m3 P; E2M1 P with E8M0 block scales
+constexpr int kPv16 = 0, kPvE4m3 = 1, kPvFp4 = 2;
 
 // f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction
 template <typename F, int... I>
@@ -154,11 +156,18 @@ __host__ __device__ constexpr int key_off(int bk, int r) { return 32 * bk + 8 * 
 //           an error of that size.
 //   COUNT   also count each row's rescale events into a.rescale_counts (a separate
 //           instantiation, so that the counter costs the other kernels no register)
+//   PV      P.V precision: 0 the 16-bit MFMA above; with QK8 (no positional mask, linear
+//           scores, D = 128) also P on the f8f6f4 MFMA with the V codes as they are:
+//           kPvE4m3, P rounded to e4m3; kPvFp4, P rounded to E2M1 with one E8M0 scale
+//           per lane's 32 keys (the smallest power of two that holds their largest value,
+//           "Direct-P" from the exponentials); O is normalised by the sum of the rounded P
 //   MASKED  positional mask through the block map (else: all keys visible)
 //   MODE    score-modifier mode (kLinear, kSoftcap, kAlibiCausal, kGeneric)
 //   GALIBI, GSOFTCAP  modifiers of the generic mode
-template <int D, bool FP8, bool QK8, bool COUNT, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
+template <int D, bool FP8, bool QK8, bool COUNT, int PV, bool MASKED, int MODE, bool GALIBI, bool GSOFTCAP>
 __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) {
+  static_assert(PV == 0 || (QK8 && !MASKED && MODE == kLinear && D == 128 && !COUNT),
+                "the fp8/fp4 P.V runs with the e4m3 Q.K^T, no positional mask, linear scores, d = 128");
   static_assert(FP8 || !QK8, "the e4m3 Q.K^T takes e4m3 inputs");
   static_assert(!(QK8 && MODE == kSoftcap), "softcap with e4m3 Q.K^T runs in the generic mode");
   constexpr int BN = 64;                 // keys per step
@@ -177,7 +186,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   constexpr int KLPW = BN * KROWB / 1024 / 4;  // 1 KiB direct K loads per wave
   constexpr int KRPL = 1024 / KROWB;
   constexpr bool DIRECT_K = !FP8 || QK8;  // K tiles by direct HBM -> LDS loads
-  constexpr bool DIRECT_V = !FP8;         // V tiles likewise (else staged and widened)
+  constexpr bool DIRECT_V = !FP8 || PV != 0;  // V tiles likewise (else staged and widened)
+  // V in LDS: 16-bit rows, or e4m3 codes for the fp8/fp4 P.V
+  constexpr int VROWB = PV ? D : ROWB;
+  constexpr int VCPR = VROWB / 16;
+  constexpr int VLPW = BN * VROWB / 1024 / 4;
+  constexpr int VRPL = 1024 / VROWB;
   constexpr int NQC = QK8 ? D / 64 : D / 16;  // MFMA k steps of S (64- or 16-wide d chunks)
   constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
   typedef typename std::conditional<QK8, i32x8, bf16x8>::type KF;  // K fragment / Q operand
@@ -360,7 +374,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // K rows: 16-byte chunk ch of row r sits at chunk position ch ^ kswz(r).
   // V rows: chunk ch of row r sits at ch ^ vswz(r).
   auto kswz = [](int r) { return (r / KRP256) % KCPR; };
-  auto vswz = [](int r) { return 4 * ((r / RP256) % (CPR / 4)); };
+  // (e4m3 V rows for the fp8/fp4 P.V: chunk ch of row r at ch ^ 2(bit1(r) | bit3(r) << 1),
+  // which spreads the 8 rows one transposing read touches over distinct banks)
+  auto vswz = [](int r) {
+    if constexpr (PV != 0) return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+    else return 4 * ((r / RP256) % (CPR / 4));
+  };
   // The buffer descriptor of a step starts at its first key row and covers the rows
   // left in the head, so every row past N reads as zero (range-checked on the lane
   // offset; no address ever leaves the head).
@@ -370,7 +389,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * HROWB), (short)0,
                                              max(N - k0, 0) * HROWB, 0x00020000);
   };
-  int koff[KLPW], voff[LPW];  // byte offsets within a tile, per direct load of this wave
+  int koff[KLPW], voff[VLPW];  // byte offsets within a tile, per direct load of this wave
 #pragma unroll
   for (int r = 0; r < KLPW; ++r) {
     const int ld = wave * KLPW + r;
@@ -378,10 +397,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     koff[r] = row * KROWB + ((lane % KCPR) ^ kswz(row)) * 16;
   }
 #pragma unroll
-  for (int r = 0; r < LPW; ++r) {
-    const int ld = wave * LPW + r;
-    const int row = ld * RPL + lane / CPR;
-    voff[r] = row * ROWB + ((lane % CPR) ^ vswz(row)) * 16;
+  for (int r = 0; r < VLPW; ++r) {
+    const int ld = wave * VLPW + r;
+    const int row = ld * VRPL + lane / VCPR;
+    voff[r] = row * VROWB + ((lane % VCPR) ^ vswz(row)) * 16;
   }
   auto issue_k = [&](int k0, lds_u8* dst) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
@@ -391,7 +410,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   auto issue_v = [&](int k0, lds_u8* dst) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
 #pragma unroll
-    for (int r = 0; r < LPW; ++r) load_lds16(rs, dst + (wave * LPW + r) * 1024, voff[r]);
+    for (int r = 0; r < VLPW; ++r) load_lds16(rs, dst + (wave * VLPW + r) * 1024, voff[r]);
   };
 
   // ---- fp8: staging through VGPRs ------------------------------------------------------
@@ -491,6 +510,35 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       vread[db] = row * ROWB + (chunk ^ vswz(row)) * 16 + (aa & 1) * 8;
     }
   }
+  // V^T (A operand of the f8f6f4 P.V, e4m3 codes): 32 keys of one d per lane from four
+  // 8-bit transposing reads.  Within a 16-lane group, result lane i, byte e comes from
+  // source lane 2e + i/8, byte i % 8 (measured on gfx950): source lane 2e + c addresses
+  // key row row_e(r) and the 8 d values 32 db + 16 mh + 8c .. +7, and result lane i holds
+  // d = 32 db + 16 mh + i for the 8 keys.  The keys follow the P operand: e4m3 P lane
+  // (n, hh) byte j is the score of key 32(j/16) + 8(j%16/4) + j%4 + 4 hh (the S accumulator
+  // order), and an e2m1 B lane of half hh pairs its nibble p with A half p/16, byte
+  // 16 hh + p%16 (measured), so the A bytes of half hh' are, per read r (bytes 8r..8r+7):
+  //   e4m3 P: rows 16 r + 8(e/4) + e%4 + 4 hh'
+  //   e2m1 P: rows 32 hh' + 16(r%2) + 8(e/4) + e%4 + 4(r/2)
+  int vread8[PV ? NDB : 1];
+  if constexpr (PV != 0) {
+    const int src = lane & 15, e = src >> 1, c = src & 1, G = lane >> 4, hp = G >> 1, mh = G & 1;
+    const int hsw = ((e >> 1) & 1) | (((e >> 2) & 1) << 1);  // the rows' swizzle (bits 1, 3 of the row)
+    const int L = PV == kPvE4m3 ? 8 * (e >> 2) + (e & 3) + 4 * hp : 32 * hp + 8 * (e >> 2) + (e & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vread8[db] = L * VROWB + 32 * (db ^ hsw) + 16 * mh + 8 * c;
+  }
+  auto vfrag8 = [&](const lds_u8* vt, int db) -> i32x8 {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i lds_v2i;
+    v2i w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int roff = PV == kPvE4m3 ? 16 * r : 16 * (r & 1) + 4 * (r >> 1);
+      w[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vt + vread8[PV ? db : 0] + roff * VROWB));
+    }
+    return i32x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+  };
   auto kfrag = [&](const lds_u8* kt, int bk, int c) -> KF {
     if constexpr (QK8) {
       typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -572,6 +620,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   float m_used = ninf;
   float l_sum = 0.f;   // row sum of p (fp32, before rounding): LSE; for bf16 also the normaliser of O
   int nres = 0;        // steps in which this row's offset was replaced (rescale events)
+  float lq_sum = 0.f;  // fp8/fp4 P.V: row sum of P as rounded for the MFMA, the normaliser of O
 
   // ---- score modifiers, mask and row maximum ---------------------------------------------
   // Score of one accumulator element before the maximum is taken (kq = k0 + 4hh - q):
@@ -721,6 +770,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       m_used = need ? m_new : m_used;
       if constexpr (COUNT) nres += need ? 1 : 0;
       l_sum *= alpha;
+      if constexpr (PV != 0) lq_sum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
     }
@@ -740,6 +790,77 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     else
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc, 0, 0, 0);
   };
+  // ---- the fp8/fp4 P.V (PV != 0) ---------------------------------------------------------------
+  // P of a whole step as the B operand of the f8f6f4 MFMA: the lane's 32 exponentials in
+  // accumulator order (j = 16 bk + r), offset moff (linear scores), V-scale units as above.
+  auto p8_exp = [&](const f32x16 (&sacc)[2], int j, float moff) -> float {
+    return exp2_(__builtin_fmaf(sacc[j >> 4][j & 15], ct, -moff));
+  };
+  // Rounds the 32 values of p to the operand's format and adds the rounded values to lq;
+  // sc is the lane's E8M0 block scale byte (127 = 1 for e4m3).
+  auto p8_pack = [&](const float (&p)[32], float& lq, int& sc) -> i32x8 {
+    i32x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (PV == kPvE4m3) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);  // round to nearest even
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], x, true);
+        b[w] = x;
+        const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.f, false);
+        const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.f, true);
+        lq += (d0[0] + d0[1]) + (d1[0] + d1[1]);
+      }
+      sc = 127;
+    } else {
+      // block scale 2^e: the smallest power of two with max p <= 6 * 2^e (6 = E2M1's
+      // largest value), e in [-126, 127]; the codes are those of p / 2^e, nearest even
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, p[j]);
+      const uint32_t tb = __builtin_bit_cast(uint32_t, amax * (1.f / 6.f));
+      int e = (int)((tb >> 23) & 255u) - 127 + ((tb & 0x7FFFFFu) != 0u ? 1 : 0);
+      e = min(max(e, -126), 127);
+      float sv = __builtin_ldexpf(1.f, e);
+      if (amax > 6.f * sv && e < 127) {  // (amax / 6 rounded down onto a power of two)
+        ++e;
+        sv *= 2.f;
+      } else if (e > -126 && amax <= 3.f * sv) {
+        --e;
+        sv *= 0.5f;
+      }
+      static_for<16>([&](auto tc) {  // (the byte select is an immediate)
+        constexpr int t = decltype(tc)::value;
+        b[t >> 2] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32((unsigned)b[t >> 2], p[2 * t], p[2 * t + 1], sv, t & 3);
+      });
+      static_for<16>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        const f32x2 dv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((unsigned)b[t >> 2], sv, t & 3);
+        lq += dv[0] + dv[1];
+      });
+      sc = e + 127;
+    }
+    return b;
+  };
+  auto pv8_mma = [&](const i32x8& va, const i32x8& pb, int sc, const f32x16& acc) -> f32x16 {
+    if constexpr (PV == kPvFp4)  // A e4m3 (format 0), B E2M1 (format 4) with the lane's block scale
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc, 0, 4, 0, 127, 0, sc);
+    else
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc, 0, 0, 0, 127, 0, 127);
+  };
+  // a whole step's P.V, not pipelined (the PARTIAL tail block and the last step)
+  auto pv8_step = [&](const lds_u8* vt, const f32x16 (&sacc)[2], float moff, float& ls, float& lq) {
+    float p[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      p[j] = p8_exp(sacc, j, moff);
+      ls += p[j];
+    }
+    int sc = 127;
+    const i32x8 pb = p8_pack(p, lq, sc);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = pv8_mma(vfrag8(vt, db), pb, sc, oacc[db]);
+  };
+
   constexpr int NQ = 2 * NQC, NP = 4 * NDB, NS = NQ + NP;  // MFMAs of S = K Q^T, of O += V P, of a step
   constexpr int PD = 3;                                     // LDS fragments are read PD MFMAs ahead
 
@@ -842,7 +963,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     qk_sched(kc, sa);
     const float moff = rescale(prepare(YES, NO, sa, k0), k0);
     float ls = 0.f;
-    pv_sched(NO, vc, sa, moff, ls);
+    if constexpr (PV != 0) {
+      float lq = 0.f;
+      pv8_step(vc, sa, moff, ls, lq);
+      lq_sum += lq * ivs;
+    } else {
+      pv_sched(NO, vc, sa, moff, ls);
+    }
     l_sum += FP8 ? ls * ivs : ls;
   }
 
@@ -1003,6 +1130,79 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     l_sum += FP8 ? ls * ivs : ls;
   };
 
+  // The fp8/fp4 P.V step: 4 Q.K^T MFMAs of S(s+1) with the 32 exponentials of P(s) under
+  // them (8 per slot) and P(s) rounded to the operand after the last, then the 4 P.V MFMAs
+  // (one per 32-wide d block, each taking the whole step's P) with the maximum of S(s+1).
+  auto step8 = [&](auto next_tag, auto issue_k_tag, int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur,
+                   lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr bool ISSUE_K = decltype(issue_k_tag)::value;
+    wait_tiles();
+    __syncthreads();
+    float moff = 0.f, ls = 0.f, lq = 0.f;
+    auto loads_and_rescale = [&]() {
+      if constexpr (ISSUE_K) issue_k(step_k0(s + 2), kcur);
+      if constexpr (NEXT) issue_v(step_k0(s + 1), vnext);
+      scales_e(step_k0(s));
+      moff = rescale(mcur, step_k0(s));
+    };
+    if constexpr (NEXT) {
+      const int k1 = step_k0(s + 1);
+      scales_p(k1);
+      KF kr[2];
+      kr[0] = kfrag(knext, 0, 0);
+      kr[1] = kfrag(knext, 1, 0);
+      snext[0] = f32x16{};
+      snext[1] = f32x16{};
+      float p[32];
+      i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0}, vf[2];
+      int sc = 127;
+      float mx = ninf;
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<NQ + NDB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i == 0) {
+          loads_and_rescale();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (i < NQ) {
+          snext[i & 1] = qk_mma(kr[i & 1], qf[i >> 1], snext[i & 1]);
+          if constexpr (i + 2 < NQ) kr[i & 1] = kfrag(knext, (i + 2) & 1, (i + 2) >> 1);
+          static_for<32 / NQ>([&](auto jc) {
+            constexpr int j = i * (32 / NQ) + decltype(jc)::value;
+            p[j] = p8_exp(scur, j, moff);
+            ls += p[j];
+          });
+          if constexpr (i == NQ - 2) vf[0] = vfrag8(vcur, 0);
+          if constexpr (i == NQ - 1) {
+            pb = p8_pack(p, lq, sc);
+            vf[1] = vfrag8(vcur, 1);
+          }
+        } else {
+          constexpr int db = i - NQ;
+          oacc[db] = pv8_mma(vf[db & 1], pb, sc, oacc[db]);
+          if constexpr (db + 2 < NDB) vf[db & 1] = vfrag8(vcur, db + 2);
+          static_for<32 / NDB>([&](auto ec) {
+            constexpr int idx = db * (32 / NDB) + decltype(ec)::value;
+            mx = __builtin_fmaxf(mx, snext[idx >> 4][idx & 15]);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mcur = finalize(mx, k1);
+    } else {
+      loads_and_rescale();
+      pv8_step(vcur, scur, moff, ls, lq);
+    }
+    l_sum += ls * ivs;
+    lq_sum += lq * ivs;
+  };
+  auto run_step = [&](auto next_tag, auto issue_k_tag, int s, lds_u8* kcur, lds_u8* knext, lds_u8* vcur,
+                      lds_u8* vnext, f32x16 (&scur)[2], f32x16 (&snext)[2], float& mcur) {
+    if constexpr (PV != 0) step8(next_tag, issue_k_tag, s, kcur, knext, vcur, vnext, scur, snext, mcur);
+    else step(next_tag, issue_k_tag, s, kcur, knext, vcur, vnext, scur, snext, mcur);
+  };
+
   if (np_steps < nsteps) {
     const int t = np_steps;  // first FULL step (even); K(t), V(t) requested
     wait_tiles();
@@ -1020,18 +1220,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     float mcand = prepare(NO, YES, sa, step_k0(t));
     int s = t;
     for (; s + 2 < nsteps; s += 2) {
-      step(YES, YES, s, kl0, kl1, vl0, vl1, sa, sb, mcand);
-      step(YES, YES, s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
+      run_step(YES, YES, s, kl0, kl1, vl0, vl1, sa, sb, mcand);
+      run_step(YES, YES, s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
     }
-    step(YES, NO, s, kl0, kl1, vl0, vl1, sa, sb, mcand);
-    step(NO, NO, s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
+    run_step(YES, NO, s, kl0, kl1, vl0, vl1, sa, sb, mcand);
+    run_step(NO, NO, s + 1, kl1, kl0, vl1, vl0, sb, sa, mcand);
   }
 
   // ---- epilogue -------------------------------------------------------------------------
   l_sum = pair_sum(l_sum);
+  if constexpr (PV != 0) lq_sum = pair_sum(lq_sum);
   if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
-  const float onorm = l_sum;
+  const float onorm = PV != 0 ? lq_sum : l_sum;
   const float inv = invalid ? nanv : (onorm > 0.f ? (FP8 ? vs_max : 1.f) / onorm : 0.f);
   bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
 #pragma unroll
@@ -1057,9 +1258,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
 // document mask is never launched without a block map (causal and window masks may
 // come without one: the kernel derives their lists).  With the e4m3 Q.K^T (QK8) a
 // softcap without ALiBi runs in the generic mode (its transform before the maximum).
-template <int D, bool FP8, bool QK8, bool COUNT>
+template <int D, bool FP8, bool QK8, bool COUNT, int PV>
 hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gsoftcap, hipStream_t st) {
   if (COUNT != (a.rescale_counts != nullptr)) return hipErrorInvalidValue;
+  if constexpr (PV != 0) {
+    // the fp8/fp4 P.V: e4m3 inputs and Q.K^T, no positional mask, linear scores
+    const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
+    if (masked || mode != kLinear || !a.q_scale || !a.k_scale || !a.v_scale) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false, PV, false, kLinear, false, false>), grid, block, 0,
+                       st, a);
+    return hipGetLastError();
+  } else {
   const dim3 grid((unsigned)(a.B * a.H * a.nqb)), block(256);
   if (masked && a.map == nullptr && (a.mflags & kDocument)) return hipErrorInvalidValue;
   if (FP8 && (!a.q_scale || !a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
@@ -1072,20 +1281,21 @@ hipError_t launch(const FwdArgs& a, bool masked, int mode, bool galibi, bool gso
   constexpr bool kSCA = false, kSCS = QK8;         // its generic modifiers
   const bool softcap_only = QK8 ? (mode == kGeneric && !galibi && gsoftcap) : mode == kSoftcap;
   if (masked) {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kLinear, false, false>), grid, block, 0, st, a);
-    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kSC, kSCA, kSCS>), grid, block, 0, st, a);
-    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, true, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, true, kLinear, false, false>), grid, block, 0, st, a);
+    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, true, kSC, kSCA, kSCS>), grid, block, 0, st, a);
+    else if (mode == kAlibiCausal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, true, kAlibiCausal, false, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, true, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, true, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;
   } else {
-    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kLinear, false, false>), grid, block, 0, st, a);
-    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kSC, kSCA, kSCS>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kGeneric, true, false>), grid, block, 0, st, a);
-    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, false, kGeneric, true, true>), grid, block, 0, st, a);
+    if (mode == kLinear) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, false, kLinear, false, false>), grid, block, 0, st, a);
+    else if (softcap_only) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, false, kSC, kSCA, kSCS>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && !gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, false, kGeneric, true, false>), grid, block, 0, st, a);
+    else if (mode == kGeneric && galibi && gsoftcap) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FP8, QK8, COUNT, 0, false, kGeneric, true, true>), grid, block, 0, st, a);
     else return hipErrorInvalidValue;  // (ALiBi on a causal mask always has a block map)
   }
   return hipGetLastError();
+  }
 }
 
 }  // namespace bf16path

@@ -3,6 +3,6 @@
 
 namespace attn119 {
 namespace bf16path {
-template hipError_t launch<128, false, false, false>(const FwdArgs&, bool, int, bool, bool, hipStream_t);
+template hipError_t launch<128, false, false, false, 0>(const FwdArgs&, bool, int, bool, bool, hipStream_t);
 }  // namespace bf16path
 }  // namespace attn119

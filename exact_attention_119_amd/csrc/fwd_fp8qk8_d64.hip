@@ -4,6 +4,6 @@
 
 namespace attn119 {
 namespace bf16path {
-template hipError_t launch<64, true, true, false>(const FwdArgs&, bool, int, bool, bool, hipStream_t);
+template hipError_t launch<64, true, true, false, 0>(const FwdArgs&, bool, int, bool, bool, hipStream_t);
 }  // namespace bf16path
 }  // namespace attn119

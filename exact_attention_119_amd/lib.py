@@ -38,6 +38,7 @@ ATTN_PV_E4M3 = 1
 
 ATTN_QK_BF16 = 0
 ATTN_QK_E4M3 = 1
+ATTN_PV_FP4 = 2
 
 EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_build",
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",

@@ -79,8 +79,17 @@ enum {
   ATTN_PV_F16 = 0,  /* V codes widened exactly to fp16, P (in units of the V block scale over
                        the head's largest V block scale, <= 2^tau) rounded to fp16, fp16 MFMA
                        with fp32 accumulation */
-  ATTN_PV_E4M3 = 1  /* P rounded to e4m3 (saturating), fp8 MFMA on the V codes (not built yet:
-                       ATTN_ERR_UNSUPPORTED) */
+  ATTN_PV_E4M3 = 1, /* P rounded to e4m3 and multiplied with the V codes on the f8f6f4 MFMA
+                       (FlashAttention-3's all-FP8 product, "FlashAttention-3: ..." (ctol-
+                       digital.de), "Analyse"): a measured mode, its error reported, not
+                       gated.  Needs qk_mode ATTN_QK_E4M3, d = 128 and no mask or modifier
+                       (else ATTN_ERR_UNSUPPORTED).  O is normalised by the sum of the rounded P */
+  ATTN_PV_FP4 = 2   /* P rounded to FP4 (E2M1) with one E8M0 scale per 32 keys of a row (the
+                       smallest power of two that holds their largest value without clipping),
+                       straight from the exponentials, on the scaled f8f6f4 MFMA with the V
+                       codes: the "Direct-P" of "Hardware-Aware FP4 FlashAttention-4"
+                       (gist.science) for non-causal inference, a measured mode with the same
+                       conditions as ATTN_PV_E4M3 */
 };
 
 /* attn_fp8.qk_mode */

@@ -40,3 +40,4 @@ from .attention import (  # noqa: F401
 from .blockmap import blockmap_ref, row_intervals_ref, visible_pairs_ref  # noqa: F401
 from .quant import e4m3_encode, hadamard, quantize_blocks_ref, rotation, signs_from_bits  # noqa: F401
 from .attention_bwd import attention_bwd_ref, attention_bwd_problem  # noqa: F401
+from . import fp4  # noqa: F401

@@ -108,6 +108,14 @@ def test_check_args_ok_and_errors(L):
     assert ck(dtype=1, fp8=L.make_fp8(P, P, None)) == L.ATTN_ERR_INVALID_ARG
     assert ck(dtype=1, fp8=L.make_fp8(P, P, P)) == L.ATTN_OK
     assert ck(dtype=1, fp8=L.make_fp8(P, P, P, pv_mode=5)) == L.ATTN_ERR_UNSUPPORTED
+    # the fp8/fp4 P.V: with the e4m3 Q.K^T, d = 128, no mask or modifier
+    for pv in (L.ATTN_PV_E4M3, L.ATTN_PV_FP4):
+        f = L.make_fp8(P, P, P, pv_mode=pv, qk_mode=L.ATTN_QK_E4M3)
+        assert ck(dtype=1, fp8=f) == L.ATTN_OK
+        assert ck(dtype=1, fp8=L.make_fp8(P, P, P, pv_mode=pv)) == L.ATTN_ERR_UNSUPPORTED
+        assert ck(dtype=1, fp8=f, d=64) == L.ATTN_ERR_UNSUPPORTED
+        assert ck(dtype=1, fp8=f, mask=L.make_mask(L.ATTN_CAUSAL)) == L.ATTN_ERR_UNSUPPORTED
+        assert ck(dtype=1, fp8=f, mask=L.make_mask(L.ATTN_SOFTCAP, softcap=5.0)) == L.ATTN_ERR_UNSUPPORTED
 
 
 def test_check_args_grouped_heads(L):
@@ -205,6 +213,8 @@ def test_kernel_variant_selection(L):
     fp8q = L.make_fp8(P, P, P, qk_mode=L.ATTN_QK_E4M3)
     assert L.attn_fwd_kernel_name(128, 1, None, fp8q) == "fp8-qk8 d128 unmasked linear"
     assert L.attn_fwd_kernel_name(64, 1, L.make_mask(C | AL), fp8q) == "fp8-qk8 d64 masked alibi-causal"
+    assert L.attn_fwd_kernel_name(128, 1, None, L.make_fp8(P, P, P, pv_mode=L.ATTN_PV_FP4, qk_mode=L.ATTN_QK_E4M3)) \
+        == "fp8-qk8-pv4 d128 unmasked linear"
     assert L.attn_fwd_kernel_name(96, 0, None, None) is None
     assert L.attn_fwd_kernel_name(128, 1, None, None) is None
 
