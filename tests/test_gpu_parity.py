@@ -25,6 +25,10 @@ VARIANTS = {
     "alibi_causal": dict(flags=C | AL),
     "alibi": dict(flags=AL),
     "softcap": dict(flags=SC, softcap=2.0),
+    # (cap 50: every step on the polynomial; cap 8: scores past 4 send some steps to the
+    # exact formula; causal so that masked steps and both paths meet)
+    "softcap50": dict(flags=C | SC, softcap=50.0),
+    "softcap8": dict(flags=C | SC, softcap=8.0),
     "cfg3like": dict(flags=C | WI | SC, window=100, softcap=3.0),
     "cfg4like": dict(flags=C | DOC | AL),
     "everything": dict(flags=C | WI | DOC | AL | SC, window=70, softcap=2.5),
