@@ -59,7 +59,27 @@ struct BwdArgs {
   int window;
   const unsigned char* map;  // block map (positional masks)
   MapLayout lay;
+  int heavy;  // causal mask without documents: workgroups take the heaviest blocks first
 };
+
+// Order in which workgroups take their blocks (workgroup L runs on XCD L % 8).  Under a
+// causal mask the work of a row block grows with its index and the work of a key block
+// falls with it; in block order the long blocks would start last and leave most CUs idle
+// at the end.  With `heavy` the blocks go out block-major, heaviest first (last row
+// block first for dQ, first key block first for dK/dV), which is longest-first list
+// scheduling; when the item's heads are a multiple of 8, XCD x takes the contiguous
+// heads x*n/8 .. (x+1)*n/8-1, so the workgroups of one head share an L2.
+__device__ __forceinline__ void bwd_item(int L, int nheads, int nblk, bool heavy, bool rising, int& head,
+                                         int& blk) {
+  if (heavy) {
+    const int r = L / nheads, i = L - r * nheads;
+    head = (nheads & 7) ? i : (i & 7) * (nheads >> 3) + (i >> 3);
+    blk = rising ? r : nblk - 1 - r;
+  } else {
+    head = L / nblk;
+    blk = L - head * nblk;
+  }
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 // LDS tiles: rows of 2D bytes, 16-byte chunk ch of row r stored at chunk position
@@ -205,7 +225,8 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int N = a.N, nqb = a.nqb;
-  const int bh = blockIdx.x / nqb, qb = blockIdx.x - bh * nqb;
+  int bh, qb;
+  bwd_item(blockIdx.x, a.B * a.H, nqb, a.heavy, false, bh, qb);
   const int b = bh / a.H, h = bh - b * a.H;
   const int bkv = b * a.Hkv + h / (a.H / a.Hkv);
   const int qrow = qb * 128 + wave * 32 + l32;
@@ -359,18 +380,20 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   constexpr int ROWB = 2 * D, STR = ROWB, CPR = ROWB / 16, NQC = D / 16, NDB = D / 32;
   constexpr int BM = 64;  // query rows per step
   constexpr int NBQ = BM / 32;
-  __shared__ __attribute__((aligned(16))) unsigned char q_sh[BM * STR];
-  __shared__ __attribute__((aligned(16))) unsigned char g_sh[BM * STR];
-  __shared__ __attribute__((aligned(16))) float lse_s[BM];
-  __shared__ __attribute__((aligned(16))) float dl_s[BM];
-  __shared__ __attribute__((aligned(16))) int lo_s[BM];
-  __shared__ __attribute__((aligned(16))) int hi_s[BM];
-  const lds_u8* qt = (const lds_u8*)q_sh;
-  const lds_u8* gt = (const lds_u8*)g_sh;
+  constexpr int TILE = BM * STR, LPW = TILE / 1024 / 4, RPL = 1024 / ROWB;  // 1 KiB direct loads
+  // Q and dO tiles of a step, double-buffered: step s reads buffer s % 2 while the rows of
+  // step s+1 arrive in the other one straight from HBM; the per-row values likewise
+  __shared__ __attribute__((aligned(1024))) unsigned char q_sh[2][TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char g_sh[2][TILE];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][BM];
+  __shared__ __attribute__((aligned(16))) int lo_s[2][BM];
+  __shared__ __attribute__((aligned(16))) int hi_s[2][BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int N = a.N, nqb = a.nqb;
-  const int bkv = blockIdx.x / nqb, kb = blockIdx.x - bkv * nqb;
+  int bkv, kb;
+  bwd_item(blockIdx.x, a.B * a.Hkv, nqb, a.heavy, true, bkv, kb);
   const int b = bkv / a.Hkv, kvh = bkv - b * a.Hkv;
   const int grp = a.H / a.Hkv;
   const int key = kb * 128 + wave * 32 + l32;
@@ -418,24 +441,29 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     }
     return true;
   };
-  constexpr int PF = BM * CPR / 256;
-  uint4 pq[PF], pg[PF];
+  // direct HBM -> LDS loads (the layout of the dQ kernel's): load r of this wave fills LDS
+  // bytes 1024 (wave LPW + r) + 16 lane, row ld RPL + lane / CPR at chunk position lane %
+  // CPR, which holds the row's chunk (position ^ lds_swz(row)); the buffer descriptor of a
+  // step starts at its first row and ends at N, so rows past N read as zero
+  int ldoff[LPW];
+#pragma unroll
+  for (int r = 0; r < LPW; ++r) {
+    const int row = (wave * LPW + r) * RPL + lane / CPR, pc = lane % CPR;
+    ldoff[r] = row * ROWB + ((pc ^ lds_swz<D>(row)) << 4);
+  }
   float p_lse = 0.f, p_dl = 0.f;
   int p_lo = 0, p_hi = -1;
-  auto fetch = [&](int hq, int qb, int sub) {
+  // requests the Q and dO rows of a step into buffer buf, and loads its per-row values
+  auto fetch = [&](int hq, int qb, int sub, int buf) {
     const int bh = b * a.H + kvh * grp + hq;
     const int q0 = qb * 128 + sub * BM;
+    const int bytes = max(N - q0, 0) * ROWB;
+    const unsigned char* qbase = (const unsigned char*)a.q + ((size_t)bh * N + q0) * ROWB;
+    const unsigned char* gbase = (const unsigned char*)a.dout + ((size_t)bh * N + q0) * ROWB;
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
-      const int q = q0 + r;
-      pq[j] = make_uint4(0u, 0u, 0u, 0u);
-      pg[j] = pq[j];
-      if (q < N) {
-        const size_t off = ((size_t)bh * N + q) * D + c * 8;
-        pq[j] = *(const uint4*)(a.q + off);
-        pg[j] = *(const uint4*)(a.dout + off);
-      }
+    for (int r = 0; r < LPW; ++r) {
+      load_lds16(qbase, bytes, (lds_u8*)q_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      load_lds16(gbase, bytes, (lds_u8*)g_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
     }
     if (tid < BM) {
       const int q = q0 + tid;
@@ -452,92 +480,133 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
       }
     }
   };
+  auto put_rows = [&](int buf) {
+    if (tid < BM) {
+      lse_s[buf][tid] = p_lse;
+      dl_s[buf][tid] = p_dl;
+      lo_s[buf][tid] = p_lo;
+      hi_s[buf][tid] = p_hi;
+    }
+  };
   int hq = 0, qb = -1, sub = 128 / BM - 1;
   bool have = !invalid && next(hq, qb, sub);
-  if (have) fetch(hq, qb, sub);
+  if (have) {
+    fetch(hq, qb, sub, 0);
+    put_rows(0);
+  }
+  int buf = 0;
   while (have) {
     const int h = kvh * grp + hq;
     const int q0 = qb * 128 + sub * BM;
     const float slope = ALIBI ? head_slope(a, h) : 0.f;
-    __syncthreads();  // the previous step's reads are done
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int t = tid + 256 * j, r = t / CPR, c = t - r * CPR;
-      *(uint4*)(q_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pq[j];
-      *(uint4*)(g_sh + r * STR + ((c ^ lds_swz<D>(r)) << 4)) = pg[j];
-    }
-    if (tid < BM) {
-      lse_s[tid] = p_lse;
-      dl_s[tid] = p_dl;
-      lo_s[tid] = p_lo;
-      hi_s[tid] = p_hi;
-    }
+    // this wave's loads of the step have landed (and its per-row writes); after the
+    // barrier every wave's have, and every wave is done reading the other buffer
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
     int nh = hq, nq = qb, ns = sub;
     const bool more = next(nh, nq, ns);
-    if (more) fetch(nh, nq, ns);
-    f32x16 s[NBQ], dp[NBQ];
-#pragma unroll
-    for (int bq = 0; bq < NBQ; ++bq) {
-      s[bq] = f32x16{};
-      dp[bq] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NQC; ++c) {
-        s[bq] = mfma(row_frag<STR>(qt, 32 * bq, l32, hh, c, rsw), kf[c], s[bq]);
-        dp[bq] = mfma(row_frag<STR>(gt, 32 * bq, l32, hh, c, rsw), vf[c], dp[bq]);
-      }
-    }
-    // P and dR = P (dP - D) ds/dr of 32 query rows (without softcap ds/dr is the scale,
-    // applied to dK at the end).  A FULL block (and every step without a positional mask:
-    // rows past N are zero rows of Q and dO, so they add nothing) needs no mask.
-    const bool full = !MASKED || cls[(size_t)qb * nqb] == 2;
-    auto elementwise = [&](auto mask_tag, int bq, f32x16& pm, f32x16& dr) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // rows 32bq + 4hh + 8j .. +3 of the step: one 16-byte LDS read per per-row array
-        const int q4 = 32 * bq + 4 * hh + 8 * j;
-        const float4 l4 = *(const float4*)&lse_s[q4];
-        const float4 d4 = *(const float4*)&dl_s[q4];
-        const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
-        int los[4] = {0, 0, 0, 0}, his[4] = {0, 0, 0, 0};
-        if constexpr (MASK) {
-          const int4 lo4 = *(const int4*)&lo_s[q4];
-          const int4 hi4 = *(const int4*)&hi_s[q4];
-          los[0] = lo4.x; los[1] = lo4.y; los[2] = lo4.z; los[3] = lo4.w;
-          his[0] = hi4.x; his[1] = hi4.y; his[2] = hi4.z; his[3] = hi4.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          float p, dsdr = 1.f;
-          if constexpr (!SOFTCAP && !ALIBI && !MASK) {
-            p = exp2_(__builtin_fmaf(s[bq][r], sl2, -ls[e]));
-          } else {
-            float sv;
-            score<SOFTCAP, ALIBI>(a, s[bq][r], q0 + q4 + e, key, slope, sv, dsdr);
-            p = MASK ? prob(key >= los[e] && key <= his[e], sv, ls[e]) : exp2_(sv * kLog2e - ls[e]);
-          }
-          pm[r] = p;
-          dr[r] = SOFTCAP ? p * (dp[bq][r] - ds[e]) * dsdr : p * (dp[bq][r] - ds[e]);
-        }
+    if (more) fetch(nh, nq, ns, buf ^ 1);
+    const lds_u8* qt = (const lds_u8*)q_sh[buf];
+    const lds_u8* gt = (const lds_u8*)g_sh[buf];
+    const float* lse_b = lse_s[buf];
+    const float* dl_b = dl_s[buf];
+    const int* lo_b = lo_s[buf];
+    const int* hi_b = hi_s[buf];
+    // The step as one stream of MFMA slots, in this order: S and dP of rows 0-31 (SP0),
+    // of rows 32-63 (SP1), then dV and dK from rows 0-31 (TR0) and from rows 32-63 (TR1).
+    // Every slot reads its LDS fragment PD slots ahead, and the elementwise work of a
+    // 32-row slice runs on the vector ALU under the MFMAs of the next phase: P and dR of
+    // rows 0-31 under SP1, of rows 32-63 under TR0.  The per-row values of a slice are
+    // read under its own SP phase.  Scheduling fences keep the slots in this order.
+    static_assert(NBQ == 2, "two 32-row slices per step");
+    constexpr int NSP = 2 * NQC, NTR = 4 * NDB, NM = 2 * (NSP + NTR), PD = 4;
+    auto frag = [&](auto ic) -> bf16x8 {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < 2 * NSP) {
+        constexpr int bq = i / NSP, c = (i % NSP) / 2;
+        return row_frag<STR>((i & 1) ? gt : qt, 32 * bq, l32, hh, c, rsw);
+      } else {
+        constexpr int t = i - 2 * NSP, bq = t / NTR, g = (t % NTR) / (2 * NDB), db = (t % (2 * NDB)) / 2;
+        return tr_frag<STR>((t & 1) ? qt : gt, 2 * bq + g, troff[db]);
       }
     };
-#pragma unroll
-    for (int bq = 0; bq < NBQ; ++bq) {
-      f32x16 pm, dr;
-      if (full) elementwise(std::false_type{}, bq, pm, dr);
-      else elementwise(std::true_type{}, bq, pm, dr);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const bf16x8 pb = pack8(pm, g), rb = pack8(dr, g);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = mfma(tr_frag<STR>(gt, 2 * bq + g, troff[db]), pb, dvacc[db]);
-          dkacc[db] = mfma(tr_frag<STR>(qt, 2 * bq + g, troff[db]), rb, dkacc[db]);
-        }
+    // per-row values of slice bq, rows 32bq + 8j + 4hh .. +3 (one 16-byte LDS read each)
+    float4 rl[2][4], rd[2][4];
+    int4 rlo[2][4], rhi[2][4];
+    auto read_rows = [&](int bq, int j) {
+      const int q4 = 32 * bq + 4 * hh + 8 * j;
+      rl[bq][j] = *(const float4*)&lse_b[q4];
+      rd[bq][j] = *(const float4*)&dl_b[q4];
+      if constexpr (MASKED) {
+        rlo[bq][j] = *(const int4*)&lo_b[q4];
+        rhi[bq][j] = *(const int4*)&hi_b[q4];
       }
-    }
+    };
+    f32x16 s[2], dp[2], pm[2], dr[2];
+    bf16x8 pb[2][2], rb[2][2];
+    // P and dR of accumulator register r of slice bq (row 32bq + 8(r/4) + 4hh + r%4).
+    // Without a positional mask every element is visible (rows and keys past N are
+    // zero rows of Q, dO, K and V: they add nothing to any gradient); with one, the row's
+    // key interval decides (a FULL block's intervals hold every key of it).
+    auto elem = [&](int bq, int r) {
+      const int j = r >> 2, e = r & 3;
+      const float ls = rl[bq][j][e], dd = rd[bq][j][e];
+      float p, dsdr = 1.f;
+      if constexpr (!SOFTCAP && !ALIBI && !MASKED) {
+        p = exp2_(__builtin_fmaf(s[bq][r], sl2, -ls));
+      } else {
+        float sv;
+        score<SOFTCAP, ALIBI>(a, s[bq][r], q0 + 32 * bq + 8 * j + 4 * hh + e, key, slope, sv, dsdr);
+        if constexpr (MASKED)
+          p = prob(key >= rlo[bq][j][e] && key <= rhi[bq][j][e], sv, ls);
+        else
+          p = exp2_(sv * kLog2e - ls);
+      }
+      pm[bq][r] = p;
+      dr[bq][r] = SOFTCAP ? p * (dp[bq][r] - dd) * dsdr : p * (dp[bq][r] - dd);
+    };
+    // elementwise work of slot k of a phase of n slots: registers 16k/n .. 16(k+1)/n - 1,
+    // and the bf16 operands of a half once its 8 registers are done
+    auto elems = [&](int bq, int k, int n) {
+      const int r0 = 16 * k / n, r1 = 16 * (k + 1) / n;
+      for (int r = r0; r < r1; ++r) elem(bq, r);
+      if (r0 < 8 && r1 >= 8) {
+        pb[bq][0] = pack8(pm[bq], 0);
+        rb[bq][0] = pack8(dr[bq], 0);
+      }
+      if (r1 == 16) {
+        pb[bq][1] = pack8(pm[bq], 1);
+        rb[bq][1] = pack8(dr[bq], 1);
+      }
+    };
+    bf16x8 fr[PD + 1];
+    static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic); });
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + PD < NM) fr[(i + PD) % (PD + 1)] = frag(std::integral_constant<int, i + PD>{});
+      const bf16x8 f = fr[i % (PD + 1)];
+      if constexpr (i < 2 * NSP) {
+        constexpr int bq = i / NSP, c = (i % NSP) / 2, k = i % NSP;
+        if constexpr (i & 1)
+          dp[bq] = mfma(f, vf[c], dp[bq]);
+        else
+          s[bq] = mfma(f, kf[c], s[bq]);
+        if constexpr (k < 4) read_rows(bq, k);
+        if constexpr (bq == 1) elems(0, k, NSP);
+      } else {
+        constexpr int t = i - 2 * NSP, bq = t / NTR, g = (t % NTR) / (2 * NDB), db = (t % (2 * NDB)) / 2;
+        if constexpr (t & 1)
+          dkacc[db] = mfma(f, rb[bq][g], dkacc[db]);
+        else
+          dvacc[db] = mfma(f, pb[bq][g], dvacc[db]);
+        if constexpr (bq == 0) elems(1, t, NTR);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (more) put_rows(buf ^ 1);  // (its loads were issued at the step's start)
+    buf ^= 1;
     hq = nh;
     qb = nq;
     sub = ns;
@@ -621,6 +690,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.window = window;
   a.map = (const unsigned char*)map;
   a.lay = map_layout(B, N);
+  a.heavy = (flags & kCausal) && !(flags & kDocument);
   const bool masked = (flags & kPositional) != 0;
   if (masked && !map) return hipErrorInvalidValue;
   return d == 128 ? bwd::launch_d<128>(a, masked, stream) : bwd::launch_d<64>(a, masked, stream);

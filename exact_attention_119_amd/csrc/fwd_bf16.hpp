@@ -63,16 +63,6 @@ constexpr int kLinear = 0, kSoftcap = 1, kAlibiCausal = 2, kGeneric = 3;
 // P.V precision (PV): the 16-bit MFMA; e4m3 P; E2M1 P with E8M0 block scales
 constexpr int kPv16 = 0, kPvE4m3 = 1, kPvFp4 = 2;
 
-// f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
 
