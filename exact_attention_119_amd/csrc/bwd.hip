@@ -111,6 +111,29 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int g) {
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// The same product with the register files chosen here, for the dK/dV kernel, whose
+// accumulators, resident K and V and S/dP tiles need more than either file alone:
+// acc += a b with acc in AGPRs, and d = a b / acc += a b with d, acc in VGPRs and b in
+// AGPRs.  The compiler does not see these as MFMAs, so the code that uses them covers
+// the hazards itself: a VALU read of an MFMA result waits kMfmaToValu wait states after
+// the last MFMA that wrote it (an s_nop), and so does the epilogue's read of the AGPR
+// accumulators; chained MFMAs on one accumulator (same opcode, same registers) and LDS
+// loads into an operand (s_waitcnt, which the compiler inserts for asm operands too) need
+// nothing more.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v0(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// wait states between an 8-pass XDL op writing a register and a VALU op reading it, with
+// margin (three s_nop 7: 24)
+__device__ __forceinline__ void mfma_result_wait() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
 // row offset (minus 4*hh) of accumulator register r: 8*(r>>2) + (r&3)
 __device__ __forceinline__ constexpr int acc_row(int r) { return 8 * (r >> 2) + (r & 3); }
 
@@ -142,24 +165,42 @@ __device__ __forceinline__ int2 tr_off(int lane, int db) {
                    (r + 8) * STR + ((chunk ^ lds_swz<D>(r + 8)) << 4) + (aa & 1) * 8);
 }
 
-// score, and its derivative in the raw dot product, of one (q, k) element (the modifiers
-// are template parameters: no branch per element)
-template <bool SOFTCAP, bool ALIBI>
-__device__ __forceinline__ void score(const BwdArgs& a, float raw, int q, int k, float slope, float& s, float& dsdr) {
-  if constexpr (SOFTCAP) {
-    const float y = raw * a.sc_cap;
-    const float t = 1.f - 2.f * rcp_(exp2_(2.f * kLog2e * y) + 1.f);
-    s = a.cap * t;
-    dsdr = a.scale * (1.f - t * t);
-  } else {
-    s = raw * a.scale;
-    dsdr = a.scale;
-  }
-  if constexpr (ALIBI) s -= slope * (float)(q > k ? q - k : k - q);
+// Per-kernel constants of the score modifiers, folded for the log2 domain.
+struct ScoreConsts {
+  float sl2;    // scale * log2(e)
+  float sce;    // 2 log2(e) scale / cap (softcap: exp2(raw sce) = e^(2 y), y = raw scale / cap)
+  float capl2;  // cap * log2(e)
+};
+__device__ __forceinline__ ScoreConsts score_consts(const BwdArgs& a) {
+  ScoreConsts c;
+  c.sl2 = a.scale * kLog2e;
+  c.sce = 2.f * kLog2e * a.sc_cap;
+  c.capl2 = a.cap * kLog2e;
+  return c;
 }
-// p = exp(s - LSE) for a visible element, 0 for a hidden one (exp2 of -inf: no branch)
-__device__ __forceinline__ float prob(bool vis, float s, float lse2) {
-  return exp2_(vis ? s * kLog2e - lse2 : -__builtin_inff());
+// s log2(e) of one (q, k) element, and ds/dr divided by the scale (the scale is applied
+// to dQ and dK once, at the end); the modifiers are template parameters, so there is no
+// branch per element.  softcap: s = cap tanh(y), tanh(y) = 1 - 2 / (e^(2y) + 1),
+// ds/dr = scale (1 - tanh^2); ALiBi: s -= slope |q - k| (slope2 = slope log2(e)).
+template <bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ float score2(const ScoreConsts& c, float raw, int q, int k, float slope2, float& dsdr) {
+  float x;
+  if constexpr (SOFTCAP) {
+    const float t = 1.f - 2.f * rcp_(exp2_(raw * c.sce) + 1.f);
+    dsdr = __builtin_fmaf(-t, t, 1.f);
+    x = t * c.capl2;
+  } else {
+    x = raw * c.sl2;
+  }
+  if constexpr (ALIBI) x = __builtin_fmaf(-slope2, (float)(q > k ? q - k : k - q), x);
+  return x;
+}
+// p = exp(s - LSE) of an element, x = s log2(e), lse2 = LSE log2(e); a hidden element
+// takes exp2(-inf) = 0 (no branch)
+template <bool MASK>
+__device__ __forceinline__ float prob2(bool vis, float x, float lse2) {
+  if constexpr (MASK) return exp2_(vis ? x - lse2 : -__builtin_inff());
+  return exp2_(x - lse2);
 }
 
 __device__ __forceinline__ float head_slope(const BwdArgs& a, int h) {
@@ -185,6 +226,31 @@ __device__ bool map_invalid(const BwdArgs& a, int b) {
 __device__ __forceinline__ void load_lds16(const unsigned char* base, int bytes, lds_u8* lds, int voffset) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+// The same loads, issued where the compiler does not track them.  After the builtin, the
+// compiler waits for the load before any later LDS read it cannot prove disjoint from
+// the destination -- every read of a buffer array indexed at run time -- which makes a
+// prefetch into one buffer wait before the first read of another.  Here the caller
+// waits itself (s_waitcnt vmcnt, then a barrier) before anything reads the destination.
+// The instruction writes no register (the data goes to LDS at M0 + 16 lane), so nothing
+// the compiler allocates can be overwritten while it is in flight; lds is wave-uniform.
+// (W = 16: one 16-byte chunk per lane, data at M0 + 16 lane; W = 4: one dword per lane,
+// at M0 + 4 lane)
+template <int W>
+__device__ __forceinline__ void load_lds_async(const void* base, int bytes, lds_u8* lds, int voffset) {
+  static_assert(W == 16 || W == 4, "dword or 16-byte loads");
+  typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+  const unsigned long long addr = (unsigned long long)base;
+  const u32x4s rs = {(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)addr),
+                     (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(addr >> 32) & 0xFFFFu)),
+                     (unsigned)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+  const unsigned m0 = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)lds);
+  if constexpr (W == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rs)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rs)
+                 : "memory", "m0");
 }
 
 // ---- D = rowsum(dO * O) ------------------------------------------------------------------
@@ -260,9 +326,9 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
     gf[c] = qvalid ? *(const bf16x8*)(a.dout + qoff + 16 * c + 8 * hh) : bf16x8{};
   }
   const float lse2 = qvalid ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  const float sl2 = a.scale * kLog2e;
+  const ScoreConsts mc = score_consts(a);
   const float dl = qvalid ? a.delta[(size_t)bh * N + qrow] : 0.f;
-  const float slope = ALIBI ? head_slope(a, h) : 0.f;
+  const float slope2 = ALIBI ? head_slope(a, h) * kLog2e : 0.f;
 
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
   int nblk = nqb, npart = 0;
@@ -303,7 +369,10 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   };
   const int nsteps = 2 * nblk;
   if (nsteps > 0) issue(step_k0(0), 0);
-  for (int st_ = 0; st_ < nsteps; ++st_) {
+  // one step; the PARTIAL blocks' steps come first (with the mask), then the FULL ones,
+  // each kind in a loop of its own
+  auto step = [&](const int st_, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = step_k0(st_);
     // this wave's loads of step st_ have landed; after the barrier every wave's have, and
     // every wave is done reading the buffer the next loads go to (step st_ - 1)
@@ -312,56 +381,76 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
     if (st_ + 1 < nsteps) issue(step_k0(st_ + 1), (st_ + 1) & 1);
     const lds_u8* kt = (const lds_u8*)k_sh[st_ & 1];
     const lds_u8* vt = (const lds_u8*)v_sh[st_ & 1];
+    // The step as one stream of MFMA slots: S^T and dP^T of keys 0-31 (SP0), of keys 32-63
+    // (SP1), then dQ^T from keys 0-31 (DQ0) and from keys 32-63 (DQ1).  Every slot reads
+    // its LDS fragment PD slots ahead; dR^T of keys 0-31 is formed on the vector ALU under
+    // SP1, of keys 32-63 under DQ0; scheduling fences keep the slots in this order.  A FULL
+    // block (and every step without a positional mask: keys past N are zero rows of K and
+    // V, so they add nothing to dQ) needs no mask.
+    constexpr int NSP = 2 * NQC, NDQ = 2 * NDB, NM = 2 * (NSP + NDQ), PD = 3;
+    auto frag = [&](auto ic) -> bf16x8 {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < 2 * NSP) {
+        constexpr int bk = i / NSP, c = (i % NSP) / 2;
+        return row_frag<STR>((i & 1) ? vt : kt, 32 * bk, l32, hh, c, rsw);
+      } else {
+        constexpr int t = i - 2 * NSP, ks = t / NDB, db = t % NDB;
+        return tr_frag<STR>(kt, ks, troff[db]);
+      }
+    };
     {
       f32x16 st[2], dp[2];
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        st[bk] = f32x16{};
-        dp[bk] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-          st[bk] = mfma(row_frag<STR>(kt, 32 * bk, l32, hh, c, rsw), qf[c], st[bk]);
-          dp[bk] = mfma(row_frag<STR>(vt, 32 * bk, l32, hh, c, rsw), gf[c], dp[bk]);
-        }
-      }
-      // dR = P (dP - D) ds/dr; without softcap ds/dr is the scale, applied to dQ at the end.
-      // A FULL block (and every step without a positional mask: keys past N are zero rows
-      // of K and V, so they add nothing to dQ) needs no mask.
-      auto elementwise = [&](auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-        for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * bk + 4 * hh + acc_row(r);
-            float p, dsdr = 1.f;
-            if constexpr (!SOFTCAP && !ALIBI && !MASK) {
-              p = exp2_(__builtin_fmaf(st[bk][r], sl2, -lse2));
-            } else {
-              float s;
-              score<SOFTCAP, ALIBI>(a, st[bk][r], qrow, key, slope, s, dsdr);
-              p = MASK ? prob(key >= lo_q && key <= hi_q, s, lse2) : exp2_(s * kLog2e - lse2);
-            }
-            st[bk][r] = SOFTCAP ? p * (dp[bk][r] - dl) * dsdr : p * (dp[bk][r] - dl);
-          }
+      bf16x8 bop[4];
+      // dR^T of accumulator register r of key slice bk
+      auto elem = [&](int bk, int r) {
+        const int key = k0 + 32 * bk + 4 * hh + acc_row(r);
+        float dsdr = 1.f;
+        const float x = score2<SOFTCAP, ALIBI>(mc, st[bk][r], qrow, key, slope2, dsdr);
+        const float p = prob2<MASK>(key >= lo_q && key <= hi_q, x, lse2);
+        const float g = p * (dp[bk][r] - dl);
+        st[bk][r] = SOFTCAP ? g * dsdr : g;
       };
-      if (!MASKED || st_ >= 2 * npart) elementwise(std::false_type{});
-      else elementwise(std::true_type{});
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 bop = pack8(st[ks >> 1], ks & 1);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) dacc[db] = mfma(tr_frag<STR>(kt, ks, troff[db]), bop, dacc[db]);
-      }
+      // elementwise work of slot k of a phase of n slots, and the bf16 operands of a
+      // half once its 8 registers are done
+      auto elems = [&](int bk, int k, int n) {
+        const int r0 = 16 * k / n, r1 = 16 * (k + 1) / n;
+        for (int r = r0; r < r1; ++r) elem(bk, r);
+        if (r0 < 8 && r1 >= 8) bop[2 * bk] = pack8(st[bk], 0);
+        if (r1 == 16) bop[2 * bk + 1] = pack8(st[bk], 1);
+      };
+      bf16x8 fr[PD + 1];
+      static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic); });
+      st[0] = st[1] = dp[0] = dp[1] = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<NM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PD < NM) fr[(i + PD) % (PD + 1)] = frag(std::integral_constant<int, i + PD>{});
+        const bf16x8 f = fr[i % (PD + 1)];
+        if constexpr (i < 2 * NSP) {
+          constexpr int bk = i / NSP, c = (i % NSP) / 2, k = i % NSP;
+          if constexpr (i & 1)
+            dp[bk] = mfma(f, gf[c], dp[bk]);
+          else
+            st[bk] = mfma(f, qf[c], st[bk]);
+          if constexpr (bk == 1) elems(0, k, NSP);
+        } else {
+          constexpr int t = i - 2 * NSP, ks = t / NDB, db = t % NDB;
+          dacc[db] = mfma(f, bop[ks], dacc[db]);
+          if constexpr (t < NDQ) elems(1, t, NDQ);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
-  }
+  };
+  int st_ = 0;
+  if constexpr (MASKED)
+    for (; st_ < 2 * npart; ++st_) step(st_, std::true_type{});
+  for (; st_ < nsteps; ++st_) step(st_, std::false_type{});
   if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
   bf16* dst = a.dq + qoff;
-  if constexpr (!SOFTCAP) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) dacc[db] *= a.scale;
-  }
+  for (int db = 0; db < NDB; ++db) dacc[db] *= a.scale;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -381,14 +470,17 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   constexpr int BM = 64;  // query rows per step
   constexpr int NBQ = BM / 32;
   constexpr int TILE = BM * STR, LPW = TILE / 1024 / 4, RPL = 1024 / ROWB;  // 1 KiB direct loads
-  // Q and dO tiles of a step, double-buffered: step s reads buffer s % 2 while the rows of
-  // step s+1 arrive in the other one straight from HBM; the per-row values likewise
-  __shared__ __attribute__((aligned(1024))) unsigned char q_sh[2][TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char g_sh[2][TILE];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][BM];
-  __shared__ __attribute__((aligned(16))) int lo_s[2][BM];
-  __shared__ __attribute__((aligned(16))) int hi_s[2][BM];
+  static_assert(LPW == 4 || LPW == 2, "the step-top wait counts 2 LPW tile loads");
+  // Q and dO tiles of a step in three buffers: step s reads buffer s % 3 while the rows of
+  // steps s+1 and s+2 arrive in the other two straight from HBM (two steps of latency
+  // cover); the per-row values likewise
+  constexpr int NBUF = 3;
+  __shared__ __attribute__((aligned(1024))) unsigned char q_sh[NBUF][TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char g_sh[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) float lse_s[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) float dl_s[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) int lo_s[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) int hi_s[NBUF][BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int N = a.N, nqb = a.nqb;
@@ -419,8 +511,17 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     dkacc[db] = f32x16{};
     dvacc[db] = f32x16{};
   }
-  cu8* cls = MASKED ? (cu8*)(a.map + a.lay.cls) + (size_t)b * nqb * nqb + kb : nullptr;
-  const float sl2 = a.scale * kLog2e;
+  // class of query block qb against this key block: byte b nqb^2 + qb nqb + kb of the
+  // class section, read as its aligned dword with a scalar load (a byte load would be a
+  // vector memory load, and its wait would also wait for the tile loads in flight; the
+  // section is padded to 256 bytes, so the dword stays inside it)
+  cint* const clsw = MASKED ? (cint*)(a.map + a.lay.cls) : nullptr;
+  const size_t cls0 = (size_t)b * nqb * nqb + kb;
+  auto cls_of = [&](int qb) -> int {
+    const size_t i = cls0 + (size_t)qb * nqb;
+    return (clsw[i >> 2] >> (8 * (int)(i & 3))) & 0xFF;
+  };
+  const ScoreConsts mc = score_consts(a);
   // Steps: (query head of the group, non-empty query block, 32-row sub-block), in that
   // nesting.  next() advances a step state; the next step's rows and per-row values are
   // loaded into registers while the current step computes.
@@ -434,7 +535,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
           if (++hq == grp) return false;
         }
         if constexpr (MASKED) {
-          if (cls[(size_t)qb * nqb] == 0) continue;  // EMPTY block
+          if (cls_of(qb) == 0) continue;  // EMPTY block
         }
         break;
       }
@@ -451,61 +552,66 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     const int row = (wave * LPW + r) * RPL + lane / CPR, pc = lane % CPR;
     ldoff[r] = row * ROWB + ((pc ^ lds_swz<D>(row)) << 4);
   }
-  float p_lse = 0.f, p_dl = 0.f;
-  int p_lo = 0, p_hi = -1;
-  // requests the Q and dO rows of a step into buffer buf, and loads its per-row values
+  // Requests a step's Q and dO rows into buffer buf, and its per-row values into the
+  // per-row arrays: one 256-byte load per wave (wave 0: the LSE, 1: D, 2 and 3: the first
+  // and last visible key; without a positional mask waves 2 and 3 load the LSE and D
+  // again into the interval arrays, which nothing reads), so every wave has 2 LPW + 1
+  // loads in flight per step.  Rows past N read as zero (Q, dO, LSE, D and the interval
+  // [0, 0]): such a row adds nothing to any gradient.
+  constexpr int LPS = 2 * LPW + 1;
   auto fetch = [&](int hq, int qb, int sub, int buf) {
     const int bh = b * a.H + kvh * grp + hq;
     const int q0 = qb * 128 + sub * BM;
-    const int bytes = max(N - q0, 0) * ROWB;
+    const int rows = max(N - q0, 0);
+    const float* lse_src = a.lse + (size_t)bh * N + q0;
+    const float* dl_src = a.delta + (size_t)bh * N + q0;
+    const void* src = (wave & 1) ? (const void*)dl_src : (const void*)lse_src;
+    if constexpr (MASKED) {
+      if (wave >= 2)
+        src = (const int*)(a.map + ((wave & 1) ? a.lay.row_hi : a.lay.row_lo)) + (size_t)b * N + q0;
+    }
+    lds_u8* dst = wave == 0 ? (lds_u8*)lse_s[buf] : wave == 1 ? (lds_u8*)dl_s[buf]
+                : wave == 2 ? (lds_u8*)lo_s[buf] : (lds_u8*)hi_s[buf];
+    load_lds_async<4>(src, rows * 4, dst, 4 * lane);
+    const int bytes = rows * ROWB;
     const unsigned char* qbase = (const unsigned char*)a.q + ((size_t)bh * N + q0) * ROWB;
     const unsigned char* gbase = (const unsigned char*)a.dout + ((size_t)bh * N + q0) * ROWB;
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
-      load_lds16(qbase, bytes, (lds_u8*)q_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
-      load_lds16(gbase, bytes, (lds_u8*)g_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
-    }
-    if (tid < BM) {
-      const int q = q0 + tid;
-      const bool ok = q < N;  // (tid < BM: one row per thread)
-      p_lse = ok ? a.lse[(size_t)bh * N + q] * kLog2e : 0.f;
-      p_dl = ok ? a.delta[(size_t)bh * N + q] : 0.f;
-      p_lo = 0;
-      p_hi = ok ? N - 1 : -1;
-      if constexpr (MASKED) {
-        if (ok) {
-          p_lo = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + q];
-          p_hi = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + q];
-        }
-      }
+      load_lds_async<16>(qbase, bytes, (lds_u8*)q_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      load_lds_async<16>(gbase, bytes, (lds_u8*)g_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
     }
   };
-  auto put_rows = [&](int buf) {
-    if (tid < BM) {
-      lse_s[buf][tid] = p_lse;
-      dl_s[buf][tid] = p_dl;
-      lo_s[buf][tid] = p_lo;
-      hi_s[buf][tid] = p_hi;
-    }
-  };
+  // the current step (hq, qb, sub) and the two after it
   int hq = 0, qb = -1, sub = 128 / BM - 1;
   bool have = !invalid && next(hq, qb, sub);
-  if (have) {
-    fetch(hq, qb, sub, 0);
-    put_rows(0);
-  }
+  int h1 = hq, q1 = qb, s1 = sub;
+  bool have1 = have && next(h1, q1, s1);
+  if (have) fetch(hq, qb, sub, 0);
+  if (have1) fetch(h1, q1, s1, 1);
   int buf = 0;
+  // (K and V of the wave, loaded above, have arrived: a wait the compiler sees, so that it
+  // puts no wait for them inside the loop, where its count would include the tile loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  static_assert(LPS == 9 || LPS == 5, "the step-top wait below counts LPS loads");
   while (have) {
     const int h = kvh * grp + hq;
     const int q0 = qb * 128 + sub * BM;
-    const float slope = ALIBI ? head_slope(a, h) : 0.f;
-    // this wave's loads of the step have landed (and its per-row writes); after the
-    // barrier every wave's have, and every wave is done reading the other buffer
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const float slope2 = ALIBI ? head_slope(a, h) * kLog2e : 0.f;
+    // this wave's loads of the step have landed (only the LPS of the next step may still
+    // be in flight: the loads complete in order); after the barrier every wave's have, and
+    // every wave is done reading the buffers of step - 1, which the loads of step + 2 go to
+    if (have1) {
+      if constexpr (LPS == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    int nh = hq, nq = qb, ns = sub;
-    const bool more = next(nh, nq, ns);
-    if (more) fetch(nh, nq, ns, buf ^ 1);
+    int h2 = h1, q2 = q1, s2 = s1;
+    const bool have2 = have1 && next(h2, q2, s2);
+    const int buf2 = buf >= NBUF - 2 ? buf + 2 - NBUF : buf + 2;
+    if (have2) fetch(h2, q2, s2, buf2);
     const lds_u8* qt = (const lds_u8*)q_sh[buf];
     const lds_u8* gt = (const lds_u8*)g_sh[buf];
     const float* lse_b = lse_s[buf];
@@ -516,10 +622,15 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     // of rows 32-63 (SP1), then dV and dK from rows 0-31 (TR0) and from rows 32-63 (TR1).
     // Every slot reads its LDS fragment PD slots ahead, and the elementwise work of a
     // 32-row slice runs on the vector ALU under the MFMAs of the next phase: P and dR of
-    // rows 0-31 under SP1, of rows 32-63 under TR0.  The per-row values of a slice are
-    // read under its own SP phase.  Scheduling fences keep the slots in this order.
+    // rows 0-31 under SP1, of rows 32-63 under TR0, each group of 4 rows' values read
+    // from LDS RA slots before its first use.  Scheduling fences keep the slots in this
+    // order.  Every step of a kernel with a positional mask applies the rows' key intervals
+    // (a FULL block's hold every key of it; a second, unmasked body for FULL blocks made
+    // the register allocator shuttle the accumulators between the register files every
+    // step); without one every element is visible (rows and keys past N are zero rows of
+    // Q, dO, K and V, so they add nothing to any gradient).
     static_assert(NBQ == 2, "two 32-row slices per step");
-    constexpr int NSP = 2 * NQC, NTR = 4 * NDB, NM = 2 * (NSP + NTR), PD = 4;
+    constexpr int NSP = 2 * NQC, NTR = 4 * NDB, NM = 2 * (NSP + NTR), PD = 4, RA = 4;
     auto frag = [&](auto ic) -> bf16x8 {
       constexpr int i = decltype(ic)::value;
       if constexpr (i < 2 * NSP) {
@@ -530,94 +641,117 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
         return tr_frag<STR>((t & 1) ? qt : gt, 2 * bq + g, troff[db]);
       }
     };
-    // per-row values of slice bq, rows 32bq + 8j + 4hh .. +3 (one 16-byte LDS read each)
-    float4 rl[2][4], rd[2][4];
-    int4 rlo[2][4], rhi[2][4];
-    auto read_rows = [&](int bq, int j) {
-      const int q4 = 32 * bq + 4 * hh + 8 * j;
-      rl[bq][j] = *(const float4*)&lse_b[q4];
-      rd[bq][j] = *(const float4*)&dl_b[q4];
-      if constexpr (MASKED) {
-        rlo[bq][j] = *(const int4*)&lo_b[q4];
-        rhi[bq][j] = *(const int4*)&hi_b[q4];
-      }
-    };
-    f32x16 s[2], dp[2], pm[2], dr[2];
-    bf16x8 pb[2][2], rb[2][2];
-    // P and dR of accumulator register r of slice bq (row 32bq + 8(r/4) + 4hh + r%4).
-    // Without a positional mask every element is visible (rows and keys past N are
-    // zero rows of Q, dO, K and V: they add nothing to any gradient); with one, the row's
-    // key interval decides (a FULL block's intervals hold every key of it).
-    auto elem = [&](int bq, int r) {
-      const int j = r >> 2, e = r & 3;
-      const float ls = rl[bq][j][e], dd = rd[bq][j][e];
-      float p, dsdr = 1.f;
-      if constexpr (!SOFTCAP && !ALIBI && !MASKED) {
-        p = exp2_(__builtin_fmaf(s[bq][r], sl2, -ls));
-      } else {
-        float sv;
-        score<SOFTCAP, ALIBI>(a, s[bq][r], q0 + 32 * bq + 8 * j + 4 * hh + e, key, slope, sv, dsdr);
-        if constexpr (MASKED)
-          p = prob(key >= rlo[bq][j][e] && key <= rhi[bq][j][e], sv, ls);
-        else
-          p = exp2_(sv * kLog2e - ls);
-      }
-      pm[bq][r] = p;
-      dr[bq][r] = SOFTCAP ? p * (dp[bq][r] - dd) * dsdr : p * (dp[bq][r] - dd);
-    };
-    // elementwise work of slot k of a phase of n slots: registers 16k/n .. 16(k+1)/n - 1,
-    // and the bf16 operands of a half once its 8 registers are done
-    auto elems = [&](int bq, int k, int n) {
-      const int r0 = 16 * k / n, r1 = 16 * (k + 1) / n;
-      for (int r = r0; r < r1; ++r) elem(bq, r);
-      if (r0 < 8 && r1 >= 8) {
-        pb[bq][0] = pack8(pm[bq], 0);
-        rb[bq][0] = pack8(dr[bq], 0);
-      }
-      if (r1 == 16) {
-        pb[bq][1] = pack8(pm[bq], 1);
-        rb[bq][1] = pack8(dr[bq], 1);
-      }
-    };
-    bf16x8 fr[PD + 1];
-    static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic); });
-    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<NM>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (i + PD < NM) fr[(i + PD) % (PD + 1)] = frag(std::integral_constant<int, i + PD>{});
-      const bf16x8 f = fr[i % (PD + 1)];
-      if constexpr (i < 2 * NSP) {
-        constexpr int bq = i / NSP, c = (i % NSP) / 2, k = i % NSP;
-        if constexpr (i & 1)
-          dp[bq] = mfma(f, vf[c], dp[bq]);
-        else
-          s[bq] = mfma(f, kf[c], s[bq]);
-        if constexpr (k < 4) read_rows(bq, k);
-        if constexpr (bq == 1) elems(0, k, NSP);
-      } else {
-        constexpr int t = i - 2 * NSP, bq = t / NTR, g = (t % NTR) / (2 * NDB), db = (t % (2 * NDB)) / 2;
-        if constexpr (t & 1)
-          dkacc[db] = mfma(f, rb[bq][g], dkacc[db]);
-        else
-          dvacc[db] = mfma(f, pb[bq][g], dvacc[db]);
-        if constexpr (bq == 0) elems(1, t, NTR);
-      }
+    auto run = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // per-row values of slice bq, rows 32bq + 8j + 4hh .. +3 (one 16-byte LDS read each)
+      float4 rl[2][4], rd[2][4];
+      int4 rlo[2][4], rhi[2][4];
+      auto read_rows = [&](int bq, int j) {
+        const int q4 = 32 * bq + 4 * hh + 8 * j;
+        rl[bq][j] = *(const float4*)&lse_b[q4] * kLog2e;
+        rd[bq][j] = *(const float4*)&dl_b[q4];
+        if constexpr (MASK) {
+          rlo[bq][j] = *(const int4*)&lo_b[q4];
+          rhi[bq][j] = *(const int4*)&hi_b[q4];
+        }
+      };
+      f32x16 s[2], dp[2], pm[2], dr[2];
+      bf16x8 pb[2][2], rb[2][2];
+      // P and dR of accumulator register r of slice bq (row 32bq + 8(r/4) + 4hh + r%4)
+      auto elem = [&](int bq, int r) {
+        const int j = r >> 2, e = r & 3;
+        float dsdr = 1.f;
+        const float x = score2<SOFTCAP, ALIBI>(mc, s[bq][r], q0 + 32 * bq + 8 * j + 4 * hh + e, key, slope2, dsdr);
+        const float p = prob2<MASK>(key >= rlo[bq][j][e] && key <= rhi[bq][j][e], x, rl[bq][j][e]);
+        pm[bq][r] = p;
+        const float g = p * (dp[bq][r] - rd[bq][j][e]);
+        dr[bq][r] = SOFTCAP ? g * dsdr : g;
+      };
+      // elementwise work of slot k of a phase of n slots: registers 16k/n .. 16(k+1)/n - 1,
+      // and the bf16 operands of a half once its 8 registers are done
+      auto elems = [&](int bq, int k, int n) {
+        const int r0 = 16 * k / n, r1 = 16 * (k + 1) / n;
+        for (int r = r0; r < r1; ++r) elem(bq, r);
+        if (r0 < 8 && r1 >= 8) {
+          pb[bq][0] = pack8(pm[bq], 0);
+          rb[bq][0] = pack8(dr[bq], 0);
+        }
+        if (r1 == 16) {
+          pb[bq][1] = pack8(pm[bq], 1);
+          rb[bq][1] = pack8(dr[bq], 1);
+        }
+      };
+      bf16x8 fr[PD + 1];
+      static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic); });
       __builtin_amdgcn_sched_barrier(0);
-    });
-    if (more) put_rows(buf ^ 1);  // (its loads were issued at the step's start)
-    buf ^= 1;
-    hq = nh;
-    qb = nq;
-    sub = ns;
-    have = more;
+      static_for<NM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PD < NM) fr[(i + PD) % (PD + 1)] = frag(std::integral_constant<int, i + PD>{});
+        const bf16x8 f = fr[i % (PD + 1)];
+        if constexpr (i < 2 * NSP) {
+          constexpr int bq = i / NSP, c = (i % NSP) / 2, k = i % NSP;
+          if constexpr (c == 0) {
+            if constexpr (i & 1)
+              mfma_v0(dp[bq], f, vf[c]);
+            else
+              mfma_v0(s[bq], f, kf[c]);
+          } else {
+            if constexpr (i & 1)
+              mfma_v(dp[bq], f, vf[c]);
+            else
+              mfma_v(s[bq], f, kf[c]);
+          }
+          if constexpr (bq == 1) {
+            if constexpr (k == 0) {
+              mfma_result_wait();  // S, dP of rows 0-31 were written in the last two slots
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            elems(0, k, NSP);
+          }
+        } else {
+          constexpr int t = i - 2 * NSP, bq = t / NTR, g = (t % NTR) / (2 * NDB), db = (t % (2 * NDB)) / 2;
+          if constexpr (t & 1)
+            mfma_agpr(dkacc[db], f, rb[bq][g]);
+          else
+            mfma_agpr(dvacc[db], f, pb[bq][g]);
+          if constexpr (bq == 0) {
+            if constexpr (t == 0) {
+              mfma_result_wait();  // S, dP of rows 32-63 were written in the last two SP slots
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            elems(1, t, NTR);
+          }
+        }
+        // row group j of slice 0 is first used at slot NSP + j NSP / 4, of slice 1 at
+        // slot 2 NSP + j NTR / 4
+        static_for<4>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr (i == NSP + j * NSP / 4 - RA) read_rows(0, j);
+          if constexpr (i == 2 * NSP + j * NTR / 4 - RA) read_rows(1, j);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    run(std::bool_constant<MASKED>{});
+    buf = buf == NBUF - 1 ? 0 : buf + 1;
+    hq = h1;
+    qb = q1;
+    sub = s1;
+    have = have1;
+    h1 = h2;
+    q1 = q2;
+    s1 = s2;
+    have1 = have2;
   }
+  // (the accumulators leave the loop in AGPRs; without this pin the allocator copies them
+  // to VGPRs at the loop head for the epilogue, and back before the MFMAs, every step)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(dkacc[db]), "+a"(dvacc[db]));
+  mfma_result_wait();  // the last step's MFMAs wrote the accumulators
   if (!kvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);
-  if constexpr (!SOFTCAP) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) dkacc[db] *= a.scale;
-  }
+  for (int db = 0; db < NDB; ++db) dkacc[db] *= a.scale;
   bf16* dk = a.dk + koff;
   bf16* dv = a.dv + koff;
 #pragma unroll
