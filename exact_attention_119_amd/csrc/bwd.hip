@@ -522,22 +522,54 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     return (clsw[i >> 2] >> (8 * (int)(i & 3))) & 0xFF;
   };
   const ScoreConsts mc = score_consts(a);
-  // Steps: (query head of the group, non-empty query block, 32-row sub-block), in that
-  // nesting.  next() advances a step state; the next step's rows and per-row values are
-  // loaded into registers while the current step computes.
+  // The non-empty query blocks of this key block as a bit mask in LDS (bit qb % 64 of word
+  // qb / 64), built once with one byte load per lane and a ballot per 64 blocks: finding
+  // the next non-empty block is then an LDS read and a bit scan, where reading the class
+  // bytes one by one cost a scalar-cache miss each (a window's key block scans every
+  // block past its window).  Up to kQMaskWords words (N <= 512K); beyond that the bytes are
+  // read one by one.
+  constexpr int kQMaskWords = 64;
+  __shared__ unsigned long long qmask_s[kQMaskWords];
+  const int nqw = (nqb + 63) / 64;
+  const bool use_qmask = MASKED && nqw <= kQMaskWords;
+  if (use_qmask) {
+    cu8* const cls = (cu8*)(a.map + a.lay.cls) + cls0;
+    for (int w = wave; w < nqw; w += 4) {
+      const int q = 64 * w + lane;
+      const bool ne = q < nqb && cls[(size_t)q * nqb] != 0;
+      const unsigned long long m = __ballot(ne);
+      if (lane == 0) qmask_s[w] = m;
+    }
+    __syncthreads();
+  }
+  // first non-empty query block at or after `from` (nqb if none)
+  auto next_block = [&](int from) -> int {
+    if constexpr (!MASKED) return from;
+    if (use_qmask) {
+      for (int w = from >> 6; w < nqw; ++w) {
+        unsigned long long m = qmask_s[w];
+        m = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(m >> 32)) << 32) |
+            (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)m);
+        if (w == (from >> 6)) m &= ~0ull << (from & 63);
+        if (m) return 64 * w + __builtin_ctzll(m);
+      }
+      return nqb;
+    }
+    int q = from;
+    while (q < nqb && cls_of(q) == 0) ++q;
+    return q;
+  };
+  // Steps: (query head of the group, non-empty query block, 64-row sub-block), in that
+  // nesting.  next() advances a step state.
   auto next = [&](int& hq, int& qb, int& sub) -> bool {
     ++sub;
     if (sub == 128 / BM || qb * 128 + sub * BM >= N) {
       sub = 0;
       for (;;) {
-        if (++qb == nqb) {
-          qb = 0;
-          if (++hq == grp) return false;
-        }
-        if constexpr (MASKED) {
-          if (cls_of(qb) == 0) continue;  // EMPTY block
-        }
-        break;
+        qb = next_block(qb + 1);
+        if (qb < nqb) break;
+        qb = -1;
+        if (++hq == grp) return false;
       }
     }
     return true;
@@ -655,32 +687,64 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
           rhi[bq][j] = *(const int4*)&hi_b[q4];
         }
       };
-      f32x16 s[2], dp[2], pm[2], dr[2];
-      bf16x8 pb[2][2], rb[2][2];
-      // P and dR of accumulator register r of slice bq (row 32bq + 8(r/4) + 4hh + r%4)
-      auto elem = [&](int bq, int r) {
+      f32x16 s[2], dp[2];
+      u32x4 pbw[2][2], rbw[2][2];  // bf16 pairs of P and dR: word w of half g = registers 8g + 2w, +1
+      // The elementwise work of an element (accumulator register r of slice bq: row
+      // 32bq + 8(r/4) + 4hh + r%4) in NSTG stages, stage st in the slot st after the
+      // element's entry slot: the slots then carry stages of NSTG different elements,
+      // whose independent chains hide each other's latency (one element per slot, start to
+      // finish, left the vector ALU waiting on each result in turn).
+      //   linear scores: x = s log2 e (ALiBi bias), g = dP - D | arg | p = exp2(arg) | P, dR
+      //   softcap:       e = exp2(2y), g | r = rcp(e + 1) | t = 1 - 2r, x, ds/dr, arg |
+      //                  p = exp2(arg) | P, dR
+      constexpr int NSTG = SOFTCAP ? 5 : 4;
+      float eu[2][16], eg[2][16], ed[2][16], ep[2][16], em[2][16];
+      auto stage = [&](auto stc, int bq, int r) {
+        constexpr int st = decltype(stc)::value;
         const int j = r >> 2, e = r & 3;
-        float dsdr = 1.f;
-        const float x = score2<SOFTCAP, ALIBI>(mc, s[bq][r], q0 + 32 * bq + 8 * j + 4 * hh + e, key, slope2, dsdr);
-        const float p = prob2<MASK>(key >= rlo[bq][j][e] && key <= rhi[bq][j][e], x, rl[bq][j][e]);
-        pm[bq][r] = p;
-        const float g = p * (dp[bq][r] - rd[bq][j][e]);
-        dr[bq][r] = SOFTCAP ? g * dsdr : g;
-      };
-      // elementwise work of slot k of a phase of n slots: registers 16k/n .. 16(k+1)/n - 1,
-      // and the bf16 operands of a half once its 8 registers are done
-      auto elems = [&](int bq, int k, int n) {
-        const int r0 = 16 * k / n, r1 = 16 * (k + 1) / n;
-        for (int r = r0; r < r1; ++r) elem(bq, r);
-        if (r0 < 8 && r1 >= 8) {
-          pb[bq][0] = pack8(pm[bq], 0);
-          rb[bq][0] = pack8(dr[bq], 0);
+        const int q = q0 + 32 * bq + 8 * j + 4 * hh + e;
+        auto alibi = [&](float x) {
+          if constexpr (ALIBI) x = __builtin_fmaf(-slope2, (float)(q > key ? q - key : key - q), x);
+          return x;
+        };
+        auto arg_of = [&](float x) {
+          const float ls = rl[bq][j][e];
+          if constexpr (MASK) return (key >= rlo[bq][j][e] && key <= rhi[bq][j][e]) ? x - ls : -__builtin_inff();
+          return x - ls;
+        };
+        if constexpr (st == 0) {
+          eg[bq][r] = dp[bq][r] - rd[bq][j][e];
+          if constexpr (SOFTCAP) eu[bq][r] = exp2_(s[bq][r] * mc.sce);
+          else eu[bq][r] = alibi(s[bq][r] * mc.sl2);
+        } else if constexpr (SOFTCAP && st == 1) {
+          eu[bq][r] = rcp_(eu[bq][r] + 1.f);
+        } else if constexpr (SOFTCAP && st == 2) {
+          const float t = __builtin_fmaf(-2.f, eu[bq][r], 1.f);
+          ed[bq][r] = __builtin_fmaf(-t, t, 1.f);
+          ep[bq][r] = arg_of(alibi(t * mc.capl2));
+        } else if constexpr (!SOFTCAP && st == 1) {
+          ep[bq][r] = arg_of(eu[bq][r]);
+        } else if constexpr (st == NSTG - 2) {
+          ep[bq][r] = exp2_(ep[bq][r]);
+        } else if constexpr (st == NSTG - 1) {
+          const float p = ep[bq][r];
+          const float g = p * eg[bq][r];
+          em[bq][r] = SOFTCAP ? g * ed[bq][r] : g;
+          if (r & 1) {
+            pbw[bq][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, to_bf16x2(ep[bq][r - 1], p));
+            rbw[bq][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, to_bf16x2(em[bq][r - 1], em[bq][r]));
+          }
         }
-        if (r1 == 16) {
-          pb[bq][1] = pack8(pm[bq], 1);
-          rb[bq][1] = pack8(dr[bq], 1);
-        }
       };
+      // elements of slice 0 enter under SP1, those of slice 1 under TR0, 16 / n per slot of
+      // a phase of n slots; entry(bq, r) is the global slot of element r's first stage
+      auto entry = [](int bq, int r) { return bq == 0 ? NSP + r / (16 / NSP) : 2 * NSP + r / (16 / NTR); };
+      // (the last stage of every element of a half ends before the first MFMA that reads
+      // the half: checked here for both slices and both halves)
+      static_assert(entry(0, 7) + NSTG - 1 < 2 * NSP && entry(0, 15) + NSTG - 1 < 2 * NSP + 2 * NDB,
+                    "P, dR of rows 0-31 are ready before their MFMAs");
+      static_assert(entry(1, 7) + NSTG - 1 < 2 * NSP + NTR && entry(1, 15) + NSTG - 1 < 2 * NSP + NTR + 2 * NDB,
+                    "P, dR of rows 32-63 are ready before their MFMAs");
       bf16x8 fr[PD + 1];
       static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic); });
       __builtin_amdgcn_sched_barrier(0);
@@ -701,27 +765,37 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
             else
               mfma_v(s[bq], f, kf[c]);
           }
-          if constexpr (bq == 1) {
-            if constexpr (k == 0) {
-              mfma_result_wait();  // S, dP of rows 0-31 were written in the last two slots
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            elems(0, k, NSP);
+          if constexpr (bq == 1 && k == 0) {
+            mfma_result_wait();  // S, dP of rows 0-31 were written in the last two slots
+            __builtin_amdgcn_sched_barrier(0);
           }
         } else {
           constexpr int t = i - 2 * NSP, bq = t / NTR, g = (t % NTR) / (2 * NDB), db = (t % (2 * NDB)) / 2;
           if constexpr (t & 1)
-            mfma_agpr(dkacc[db], f, rb[bq][g]);
+            mfma_agpr(dkacc[db], f, __builtin_bit_cast(bf16x8, rbw[bq][g]));
           else
-            mfma_agpr(dvacc[db], f, pb[bq][g]);
-          if constexpr (bq == 0) {
-            if constexpr (t == 0) {
-              mfma_result_wait();  // S, dP of rows 32-63 were written in the last two SP slots
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            elems(1, t, NTR);
+            mfma_agpr(dvacc[db], f, __builtin_bit_cast(bf16x8, pbw[bq][g]));
+          if constexpr (t == 0) {
+            mfma_result_wait();  // S, dP of rows 32-63 were written in the last two SP slots
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
+        // the elementwise stages that fall in this slot (oldest element first): stage st of
+        // the elements that entered in slot i - st
+        static_for<NSTG>([&](auto sc) {
+          constexpr int st = NSTG - 1 - decltype(sc)::value;
+          static_for<2>([&](auto bc) {
+            constexpr int bq = decltype(bc)::value, n = bq == 0 ? NSP : NTR, per = 16 / n;
+            constexpr int k = i - st - (bq == 0 ? NSP : 2 * NSP);  // entry slot within the phase
+            if constexpr (k >= 0 && k < n) {
+              static_for<per>([&](auto uc) {
+                constexpr int r = k * per + decltype(uc)::value;
+                static_assert(entry(bq, r) == i - st, "entry slot");
+                stage(std::integral_constant<int, st>{}, bq, r);
+              });
+            }
+          });
+        });
         // row group j of slice 0 is first used at slot NSP + j NSP / 4, of slice 1 at
         // slot 2 NSP + j NTR / 4
         static_for<4>([&](auto jc) {
