@@ -715,6 +715,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
         if constexpr (st == 0) {
           eg[bq][r] = dp[bq][r] - rd[bq][j][e];
           if constexpr (SOFTCAP) eu[bq][r] = exp2_(s[bq][r] * mc.sce);
+          else if constexpr (!ALIBI) eu[bq][r] = __builtin_fmaf(s[bq][r], mc.sl2, -rl[bq][j][e]);  // x - lse2
           else eu[bq][r] = alibi(s[bq][r] * mc.sl2);
         } else if constexpr (SOFTCAP && st == 1) {
           eu[bq][r] = rcp_(eu[bq][r] + 1.f);
@@ -723,7 +724,12 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
           ed[bq][r] = __builtin_fmaf(-t, t, 1.f);
           ep[bq][r] = arg_of(alibi(t * mc.capl2));
         } else if constexpr (!SOFTCAP && st == 1) {
-          ep[bq][r] = arg_of(eu[bq][r]);
+          if constexpr (ALIBI) {
+            ep[bq][r] = arg_of(eu[bq][r]);
+          } else {  // (eu already holds x - lse2)
+            if constexpr (MASK) ep[bq][r] = (key >= rlo[bq][j][e] && key <= rhi[bq][j][e]) ? eu[bq][r] : -__builtin_inff();
+            else ep[bq][r] = eu[bq][r];
+          }
         } else if constexpr (st == NSTG - 2) {
           ep[bq][r] = exp2_(ep[bq][r]);
         } else if constexpr (st == NSTG - 1) {
