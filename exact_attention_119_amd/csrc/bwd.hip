@@ -221,38 +221,6 @@ __device__ bool map_invalid(const BwdArgs& a, int b) {
   return __syncthreads_or(st) != 0 || bad;
 }
 
-// One 16-byte chunk per lane from base + voffset (bytes; reads past `bytes` give zero)
-// into LDS at lds + 16 * lane.
-__device__ __forceinline__ void load_lds16(const unsigned char* base, int bytes, lds_u8* lds, int voffset) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
-}
-// The same loads, issued where the compiler does not track them.  After the builtin, the
-// compiler waits for the load before any later LDS read it cannot prove disjoint from
-// the destination -- every read of a buffer array indexed at run time -- which makes a
-// prefetch into one buffer wait before the first read of another.  Here the caller
-// waits itself (s_waitcnt vmcnt, then a barrier) before anything reads the destination.
-// The instruction writes no register (the data goes to LDS at M0 + 16 lane), so nothing
-// the compiler allocates can be overwritten while it is in flight; lds is wave-uniform.
-// (W = 16: one 16-byte chunk per lane, data at M0 + 16 lane; W = 4: one dword per lane,
-// at M0 + 4 lane)
-template <int W>
-__device__ __forceinline__ void load_lds_async(const void* base, int bytes, lds_u8* lds, int voffset) {
-  static_assert(W == 16 || W == 4, "dword or 16-byte loads");
-  typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
-  const unsigned long long addr = (unsigned long long)base;
-  const u32x4s rs = {(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)addr),
-                     (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(addr >> 32) & 0xFFFFu)),
-                     (unsigned)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
-  const unsigned m0 = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)lds);
-  if constexpr (W == 16)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rs)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rs)
-                 : "memory", "m0");
-}
-
 // ---- D = rowsum(dO * O) ------------------------------------------------------------------
 // D/8 lanes per row, 16 bytes of O and of dO each (coalesced rows), summed across the
 // row's lanes with shuffles (the groups are aligned, so the xor offsets stay inside them).
@@ -310,12 +278,15 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   }
   const unsigned char* const kbase = (const unsigned char*)a.k + (size_t)bkv * N * ROWB;
   const unsigned char* const vbase = (const unsigned char*)a.v + (size_t)bkv * N * ROWB;
+  // (untracked by the compiler: each step waits for its own tiles before its barrier)
   auto issue = [&](int k0, int buf) {
     const int bytes = max(N - k0, 0) * ROWB;
+    const u32x4 krs = dma_rsrc(kbase + (size_t)k0 * ROWB, bytes);
+    const u32x4 vrs = dma_rsrc(vbase + (size_t)k0 * ROWB, bytes);
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
-      load_lds16(kbase + (size_t)k0 * ROWB, bytes, (lds_u8*)k_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
-      load_lds16(vbase + (size_t)k0 * ROWB, bytes, (lds_u8*)v_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      dma_to_lds<16>(krs, (lds_u8*)k_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      dma_to_lds<16>(vrs, (lds_u8*)v_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
     }
   };
 
@@ -369,6 +340,9 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   };
   const int nsteps = 2 * nblk;
   if (nsteps > 0) issue(step_k0(0), 0);
+  // (the wave's Q, dO rows and per-row values, loaded above, have arrived: a wait the
+  // compiler sees, so that it puts none for them inside the loops)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // one step; the PARTIAL blocks' steps come first (with the mask), then the FULL ones,
   // each kind in a loop of its own
   auto step = [&](const int st_, auto mask_tag) {
@@ -604,14 +578,14 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     }
     lds_u8* dst = wave == 0 ? (lds_u8*)lse_s[buf] : wave == 1 ? (lds_u8*)dl_s[buf]
                 : wave == 2 ? (lds_u8*)lo_s[buf] : (lds_u8*)hi_s[buf];
-    load_lds_async<4>(src, rows * 4, dst, 4 * lane);
+    dma_to_lds<4>(dma_rsrc(src, rows * 4), dst, 4 * lane);
     const int bytes = rows * ROWB;
-    const unsigned char* qbase = (const unsigned char*)a.q + ((size_t)bh * N + q0) * ROWB;
-    const unsigned char* gbase = (const unsigned char*)a.dout + ((size_t)bh * N + q0) * ROWB;
+    const u32x4 qrs = dma_rsrc((const unsigned char*)a.q + ((size_t)bh * N + q0) * ROWB, bytes);
+    const u32x4 grs = dma_rsrc((const unsigned char*)a.dout + ((size_t)bh * N + q0) * ROWB, bytes);
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
-      load_lds_async<16>(qbase, bytes, (lds_u8*)q_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
-      load_lds_async<16>(gbase, bytes, (lds_u8*)g_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      dma_to_lds<16>(qrs, (lds_u8*)q_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
+      dma_to_lds<16>(grs, (lds_u8*)g_sh[buf] + (wave * LPW + r) * 1024, ldoff[r]);
     }
   };
   // the current step (hq, qb, sub) and the two after it

@@ -21,6 +21,41 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ---- direct HBM -> LDS loads the compiler does not track -----------------------------
+// buffer_load ... lds writes each lane's data to LDS at M0 + W * lane.  Issued through the
+// builtin, the compiler waits for such a load before any later LDS read it cannot prove
+// disjoint from the destination (every read of a buffer chosen at run time), which makes
+// a prefetch into one buffer wait before the first read of the other.  These helpers
+// issue it where the compiler does not see it: the caller waits itself (s_waitcnt vmcnt,
+// then a barrier) before anything reads the destination.  The instruction writes no
+// register, so nothing the compiler allocates can be overwritten while it is in flight.
+// The descriptor and the LDS address are wave-uniform (kept in SGPRs).  An SALU write of
+// M0 needs one wait state before an LDS-DMA load reads it (the s_nop 0 between them; the
+// compiler inserts it for its own loads, but not inside an asm statement).
+// Descriptor of the bytes [base, base + bytes) (reads past the end give zero).
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, int bytes) {
+  const unsigned long long addr = (unsigned long long)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xFFFFu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+// W = 16: a 16-byte chunk per lane from descriptor offset voffset to LDS lds + 16 lane;
+// W = 4: a dword per lane to lds + 4 lane.
+template <int W>
+__device__ __forceinline__ void dma_to_lds(u32x4 rs, __attribute__((address_space(3))) unsigned char* lds,
+                                           int voffset) {
+  static_assert(W == 16 || W == 4, "dword or 16-byte loads");
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(unsigned long long)lds);
+  if constexpr (W == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset),
+                 "s"(rs)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset),
+                 "s"(rs)
+                 : "memory", "m0");
+}
+
 // f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {

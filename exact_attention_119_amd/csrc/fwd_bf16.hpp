@@ -106,10 +106,10 @@ __device__ __forceinline__ void pin(T& v) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One 16-byte chunk per lane from a buffer into LDS at lds_base + 16*lane.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* lds_base, int voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voffset, 0, 0, 0);
+// One 16-byte chunk per lane from a buffer into LDS at lds_base + 16*lane, untracked by
+// the compiler (every step waits for its tiles itself, in wait_tiles, before its barrier).
+__device__ __forceinline__ void load_lds16(u32x4 rsrc, lds_u8* lds_base, int voffset) {
+  dma_to_lds<16>(rsrc, lds_base, voffset);
 }
 
 // e4m3 (OCP) codes widen exactly to bf16 and to fp16 (3 mantissa bits; every e4m3
@@ -376,6 +376,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   const unsigned char* const kbase = (const unsigned char*)a.k + kv_row0 * HROWB;
   const unsigned char* const vbase = (const unsigned char*)a.v + kv_row0 * HROWB;
   auto rsrc = [&](const unsigned char* base, int k0) {
+    return dma_rsrc(base + (size_t)k0 * HROWB, max(N - k0, 0) * HROWB);
+  };
+  // (the staged fp8 tiles load into registers through the compiler-tracked builtin)
+  auto rsrc_reg = [&](const unsigned char* base, int k0) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * HROWB), (short)0,
                                              max(N - k0, 0) * HROWB, 0x00020000);
   };
@@ -393,12 +397,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     voff[r] = row * VROWB + ((lane % VCPR) ^ vswz(row)) * 16;
   }
   auto issue_k = [&](int k0, lds_u8* dst) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
+    const u32x4 rs = rsrc(kbase, k0);
 #pragma unroll
     for (int r = 0; r < KLPW; ++r) load_lds16(rs, dst + (wave * KLPW + r) * 1024, koff[r]);
   };
   auto issue_v = [&](int k0, lds_u8* dst) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
+    const u32x4 rs = rsrc(vbase, k0);
 #pragma unroll
     for (int r = 0; r < VLPW; ++r) load_lds16(rs, dst + (wave * VLPW + r) * 1024, voff[r]);
   };
@@ -432,7 +436,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   }
   auto stage_k = [&](int k0) {
     if constexpr (!DIRECT_K) {
-      const __amdgpu_buffer_rsrc_t rs = rsrc(kbase, k0);
+      const __amdgpu_buffer_rsrc_t rs = rsrc_reg(kbase, k0);
 #pragma unroll
       for (int j = 0; j < SCH; ++j)
         kst[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, kldo[j], 0, 0));
@@ -440,7 +444,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   };
   auto stage_v = [&](int k0) {
     if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rs = rsrc(vbase, k0);
+      const __amdgpu_buffer_rsrc_t rs = rsrc_reg(vbase, k0);
 #pragma unroll
       for (int j = 0; j < SCH; ++j)
         vst[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vldo[j], 0, 0));
