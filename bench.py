@@ -366,7 +366,7 @@ def bench_bwd(args):
     flop = 10.0 * p.d * p.H * pairs  # five products of 2*d flop per visible pair
     step_ms = wall * 1e3 / args.steps
     name = workload_name(p)
-    log(f"bench: backward step {step_ms:.4f} ms (wall), three launches avg {avg:.4f} ms (back-to-back, events)")
+    log(f"bench: backward step {step_ms:.4f} ms (wall), two launches avg {avg:.4f} ms (back-to-back, events)")
     out = {"metric": "attention bwd TFLOP/s (five products of 2d flop per visible pair)",
            "value": round(flop / (step_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
@@ -375,7 +375,7 @@ def bench_bwd(args):
                       "step": "row sums + dQ + dK/dV, given O and LSE", "parallelism": "single GPU"},
            "roofline": {"bound": "mfma", "achieved": round(flop / (avg * 1e-3) / 1e12, 3), "peak": PEAK_TFLOPS["bf16"],
                         "unit": "TFLOP/s", "frac": round(flop / (avg * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
-                        "traffic": None, "kernel": "delta + dq + dkdv (three launches)",
+                        "traffic": None, "kernel": "dq (with the row sums D) + dkdv (two launches)",
                         "kernel_avg_ms": round(avg, 5)}}
     if not args.no_cpu:
         import oracle

@@ -7,9 +7,9 @@
 //   P = exp(s - LSE) (recomputed from Q, K and the saved LSE), dV = P^T dO,
 //   dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D), dR = dS * ds/dr,
 //   dQ = dR K, dK = dR^T Q   (ds/dr = scale, or scale * (1 - tanh^2) with softcap).
-// Deterministic: no atomics.  Three launches:
-//   delta_kernel : D for every query row (one thread per row).
+// Deterministic: no atomics.  Two launches:
 //   dq_kernel    : one workgroup per (b*H + h, 128 query rows), a wave per 32 rows; it
+//                  forms D of its rows (written for the second launch), then
 //                  walks the row block's non-empty key blocks in 64-key steps:
 //                  S^T = K Q^T and dP^T = V dO^T (Q and dO of the wave resident as
 //                  B operands), dR^T elementwise, dQ^T += K^T dR^T.
@@ -221,31 +221,6 @@ __device__ bool map_invalid(const BwdArgs& a, int b) {
   return __syncthreads_or(st) != 0 || bad;
 }
 
-// ---- D = rowsum(dO * O) ------------------------------------------------------------------
-// D/8 lanes per row, 16 bytes of O and of dO each (coalesced rows), summed across the
-// row's lanes with shuffles (the groups are aligned, so the xor offsets stay inside them).
-template <int D>
-__global__ void __launch_bounds__(256) delta_kernel(const BwdArgs a) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per workgroup
-  const size_t rows = (size_t)a.B * a.H * a.N;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint4 x = ((const uint4*)(a.o + row * D))[part];
-    const uint4 y = ((const uint4*)(a.dout + row * D))[part];
-    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc = __builtin_fmaf(__uint_as_float(xs[t] << 16), __uint_as_float(ys[t] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(xs[t] & 0xFFFF0000u), __uint_as_float(ys[t] & 0xFFFF0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) a.delta[row] = acc;
-}
-
 // ---- dQ ----------------------------------------------------------------------------------
 template <int D, bool MASKED, bool SOFTCAP, bool ALIBI>
 __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
@@ -298,7 +273,22 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   }
   const float lse2 = qvalid ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   const ScoreConsts mc = score_consts(a);
-  const float dl = qvalid ? a.delta[(size_t)bh * N + qrow] : 0.f;
+  // D = rowsum(dO * O) of the lane's row: the lane holds the dO values 16c + 8hh .. +7 of
+  // the row, its partner lane (lane ^ 32) the others; the O values at the same places
+  // are loaded beside them.  D is written here for the dK/dV kernel, launched after.
+  float dl = 0.f;
+#pragma unroll
+  for (int c = 0; c < NQC; ++c) {
+    const u32x4 ov = qvalid ? *(const u32x4*)(a.o + qoff + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
+    const u32x4 gv = __builtin_bit_cast(u32x4, gf[c]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dl = __builtin_fmaf(__uint_as_float(ov[t] << 16), __uint_as_float(gv[t] << 16), dl);
+      dl = __builtin_fmaf(__uint_as_float(ov[t] & 0xFFFF0000u), __uint_as_float(gv[t] & 0xFFFF0000u), dl);
+    }
+  }
+  dl = pair_sum(dl);
+  if (qvalid && hh == 0) a.delta[(size_t)bh * N + qrow] = dl;
   const float slope2 = ALIBI ? head_slope(a, h) * kLog2e : 0.f;
 
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
@@ -839,9 +829,6 @@ void launch_m(const BwdArgs& a, hipStream_t st) {
 }
 template <int D>
 hipError_t launch_d(const BwdArgs& a, bool masked, hipStream_t st) {
-  const size_t rows = (size_t)a.B * a.H * a.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a);
   if (masked) launch_m<D, true>(a, st);
   else launch_m<D, false>(a, st);
   return hipGetLastError();
@@ -891,8 +878,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
 // ends; host code never passes the array's name (a host-side stand-in) to a kernel, only
 // the device address hipGetSymbolAddress returns for the current device, looked up once
 // per device.  Every call on a GPU shares that GPU's array, so calls that overlap on one
-// GPU race; D is fully written by the row-sum kernel before anything reads it, so nothing
-// needs clearing.
+// GPU race; D is fully written by the dQ kernel before the dK/dV kernel reads it, so
+// nothing needs clearing.
 constexpr size_t kScratchRows = size_t(1) << 22;  // 4,194,304 rows of D = 16 MiB per GPU
 static __device__ __align__(256) float scratch[kScratchRows];
 

@@ -71,30 +71,6 @@ __device__ __forceinline__ bf16x2 to_bf16x2(float lo, float hi) {
   return __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
 }
 
-// v_permlane32_swap(a, b) exchanges the upper 32 lanes of a with the lower 32 lanes
-// of b.  With a = b = x, lane l < 32 ends with (x[l], x[l+32]) and lane l >= 32 with
-// (x[l-32], x[l]): both halves see the pair.  (The two results are copied out as
-// integers before the bit casts: a bit cast applied to an element of the returned
-// vector reads element 0 in this compiler.)
-__device__ __forceinline__ void pair_of(float x, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                                  false, false);
-  const int r0 = r[0], r1 = r[1];
-  a = __builtin_bit_cast(float, r0);
-  b = __builtin_bit_cast(float, r1);
-}
-// max / sum of x over lanes l and l^32 (the two halves holding one query row)
-__device__ __forceinline__ float pair_max(float x) {
-  float a, b;
-  pair_of(x, a, b);
-  return __builtin_fmaxf(a, b);
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  float a, b;
-  pair_of(x, a, b);
-  return a + b;
-}
-
 // Pins v to this point of the program (an empty volatile asm that reads and rewrites
 // it in a VGPR): whatever computes v stays before it, whatever uses the new v stays
 // after it, so neither can drift across the scheduling fences around it.
