@@ -1200,21 +1200,42 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   // ---- epilogue -------------------------------------------------------------------------
   l_sum = pair_sum(l_sum);
   if constexpr (PV != 0) lq_sum = pair_sum(lq_sum);
-  if (!qvalid) return;
   const float nanv = __builtin_bit_cast(float, 0x7fc00000u);  // quiet NaN (a bit pattern, not folded)
   const float onorm = PV != 0 ? lq_sum : l_sum;
   const float inv = invalid ? nanv : (onorm > 0.f ? (FP8 ? vs_max : 1.f) / onorm : 0.f);
-  bf16* op = (bf16*)a.o + (head_row0 + qrow) * D;
+  // O leaves through LDS, so that each store instruction writes whole rows (a lane holds
+  // 8-byte pieces of one row, which would make every store touch 32 rows).  The wave's
+  // 32 x D tile goes to a region of its own in K buffer 0 (waves 0, 1) or V buffer 0
+  // (waves 2, 3), which no step reads any more: the step count is even, so the last step
+  // reads only buffers 1, and the barrier at its start saw every read of buffers 0 done.
+  // Chunk ch (16 bytes) of row r sits at chunk position ch ^ (r % CPR), its two 8-byte
+  // halves swapped when (r / CPR) is odd; then the wave stores RPR whole rows per
+  // instruction, 16 bytes per lane.
+  {
+    constexpr int RPR = 64 / CPR;  // rows per 1 KiB store
+    lds_u8* const ot = (wave < 2 ? kl0 : vl0) + (wave & 1) * (32 * ROWB);
+    const int wsw = (l32 / CPR) & 1;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x2 v01 = to_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
-      const bf16x2 v23 = to_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-      const u32x2 st = {__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
-      *(u32x2*)(op + db * 32 + 8 * i + 4 * hh) = st;
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 v01 = to_bf16x2(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
+        const bf16x2 v23 = to_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+        const u32x2 st = {__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
+        const int pos = (4 * db + i) ^ (l32 % CPR);  // chunk of d = 32 db + 8 i + 4 hh
+        *(__attribute__((address_space(3))) u32x2*)(ot + l32 * ROWB + pos * 16 + 8 * (hh ^ wsw)) = st;
+      }
+    const int rl = lane / CPR, ch = lane % CPR;
+    bf16* const orow0 = (bf16*)a.o + (head_row0 + q0 + wave * 32) * D;
+#pragma unroll
+    for (int k = 0; k < 32 / RPR; ++k) {
+      const int r = RPR * k + rl;
+      u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ot + r * ROWB + ((ch ^ (r % CPR)) * 16));
+      if (((RPR * k) / CPR) & 1) v = u32x4{v.z, v.w, v.x, v.y};  // (the swapped halves)
+      if (q0 + wave * 32 + r < N) *(u32x4*)(orow0 + r * D + ch * 8) = v;
     }
-  if (hh == 0) {
+  }
+  if (qvalid && hh == 0) {
     float lse;
     if (invalid) lse = nanv;
     else if (l_sum > 0.f) lse = (m_used + __builtin_amdgcn_logf(l_sum)) * 0.6931471805599453f;
