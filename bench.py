@@ -333,7 +333,7 @@ def traffic_record(name: str, files=None):
 
 
 def bench_bwd(args):
-    """One step = the three backward launches for the configuration's workload."""
+    """One step = the two backward launches for the configuration's workload."""
     import numpy as np
     import torch
     import workload as W
