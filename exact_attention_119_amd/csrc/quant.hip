@@ -60,6 +60,15 @@ __device__ __forceinline__ float e4m3_quotient(float y, float g, float s) {
   return __builtin_copysignf(at, y);
 }
 
+// Whether e4m3_quotient may move q: in the normal range (|q| >= 2^-6) the midpoint of
+// q's e4m3 interval has fp32 mantissa bits 19..0 equal to 0x80000, so q lies within four
+// ulps of it exactly when those bits are in [0x7FFFC, 0x80004]; below 2^-6 (rare after the
+// block scaling) every value counts as near.
+__device__ __forceinline__ bool maybe_near_tie(float q) {
+  const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
+  return b < 0x3C800000u || ((b & 0xFFFFFu) - 0x7FFFCu) <= 8u;
+}
+
 // Lane layout: four lanes per row; lane k (0..3) of a row holds the 16-byte chunks
 // q = 4c + k, c = 0 .. D/32 - 1, i.e. elements e = 8q + i.  Element bits 0-2 and 5-6 are
 // in registers, bits 3-4 are the lane, so the transform strides 8 and 16 are quad
@@ -187,9 +196,19 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
       unsigned char* dst = a.codes + ((size_t)bh * a.N + row) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        // y * g, and the exact tie resolution only for the chunks of the wave where some
+        // value lies near a tie (a wave-uniform branch: most chunks skip it)
         float w[8];
+        bool near = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = e4m3_quotient(v[p][c][i], g, sc);
+        for (int i = 0; i < 8; ++i) {
+          w[i] = v[p][c][i] * g;
+          near |= maybe_near_tie(w[i]);
+        }
+        if (__builtin_amdgcn_ballot_w64(near)) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = e4m3_quotient(v[p][c][i], g, sc);
+        }
         int lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[0], w[1], 0, false);
         lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[2], w[3], lo, true);
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(w[4], w[5], 0, false);
