@@ -637,6 +637,13 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
         return tr_frag<STR>((t & 1) ? qt : gt, 2 * bq + g, troff[db]);
       }
     };
+    // Without softcap the mask can ride on the S accumulators: S starts as a bias of 0 where
+    // the row sees the lane's key and -inf where it does not, so a hidden score stays -inf
+    // through the products and the ALiBi term and its p is 0 -- and only the steps of
+    // PARTIAL blocks compute the bias (FULL blocks start S at 0).  With softcap a hidden
+    // score would come out finite (tanh saturates), so there the elementwise stage applies
+    // the mask in every step.
+    constexpr bool BIAS = MASKED && !SOFTCAP;
     auto run = [&](auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       // per-row values of slice bq, rows 32bq + 8j + 4hh .. +3 (one 16-byte LDS read each)
@@ -715,6 +722,27 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
                     "P, dR of rows 0-31 are ready before their MFMAs");
       static_assert(entry(1, 7) + NSTG - 1 < 2 * NSP + NTR && entry(1, 15) + NSTG - 1 < 2 * NSP + NTR + 2 * NDB,
                     "P, dR of rows 32-63 are ready before their MFMAs");
+      if constexpr (BIAS) {
+        if (cls_of(qb) != 2) {  // a PARTIAL block: the rows' key intervals
+#pragma unroll
+          for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int q4 = 32 * bq + 4 * hh + 8 * j;
+              const int4 lo = *(const int4*)&lo_b[q4], hi = *(const int4*)&hi_b[q4];
+              const int los[4] = {lo.x, lo.y, lo.z, lo.w}, his[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                s[bq][4 * j + e] = (key >= los[e] && key <= his[e]) ? 0.f : -__builtin_inff();
+            }
+        } else {
+          s[0] = f32x16{};
+          s[1] = f32x16{};
+        }
+        // (a VALU write of a register an MFMA then reads as its accumulator needs wait
+        // states the compiler does not add for these asm MFMAs)
+        asm volatile("s_nop 7" ::: "memory");
+      }
       bf16x8 fr[PD + 1];
       static_for<PD>([&](auto ic) { fr[ic.value] = frag(ic); });
       __builtin_amdgcn_sched_barrier(0);
@@ -727,6 +755,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
           if constexpr (c == 0) {
             if constexpr (i & 1)
               mfma_v0(dp[bq], f, vf[c]);
+            else if constexpr (BIAS)
+              mfma_v(s[bq], f, kf[c]);  // onto the bias
             else
               mfma_v0(s[bq], f, kf[c]);
           } else {
@@ -776,7 +806,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    run(std::bool_constant<MASKED>{});
+    run(std::bool_constant<MASKED && !BIAS>{});
     buf = buf == NBUF - 1 ? 0 : buf + 1;
     hq = h1;
     qb = q1;
