@@ -232,7 +232,8 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_sh[2][TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v_sh[2][TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave choices stay scalar
   const int N = a.N, nqb = a.nqb;
   int bh, qb;
   bwd_item(blockIdx.x, a.B * a.H, nqb, a.heavy, false, bh, qb);
@@ -446,7 +447,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) int lo_s[NBUF][BM];
   __shared__ __attribute__((aligned(16))) int hi_s[NBUF][BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave choices stay scalar
   const int N = a.N, nqb = a.nqb;
   int bkv, kb;
   bwd_item(blockIdx.x, a.B * a.Hkv, nqb, a.heavy, true, bkv, kb);
@@ -680,7 +682,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
         };
         auto arg_of = [&](float x) {
           const float ls = rl[bq][j][e];
-          if constexpr (MASK) return (key >= rlo[bq][j][e] && key <= rhi[bq][j][e]) ? x - ls : -__builtin_inff();
+          if constexpr (MASK) return ((key >= rlo[bq][j][e]) & (key <= rhi[bq][j][e])) ? x - ls : -__builtin_inff();
           return x - ls;
         };
         if constexpr (st == 0) {
@@ -698,7 +700,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
           if constexpr (ALIBI) {
             ep[bq][r] = arg_of(eu[bq][r]);
           } else {  // (eu already holds x - lse2)
-            if constexpr (MASK) ep[bq][r] = (key >= rlo[bq][j][e] && key <= rhi[bq][j][e]) ? eu[bq][r] : -__builtin_inff();
+            if constexpr (MASK) ep[bq][r] = ((key >= rlo[bq][j][e]) & (key <= rhi[bq][j][e])) ? eu[bq][r] : -__builtin_inff();
             else ep[bq][r] = eu[bq][r];
           }
         } else if constexpr (st == NSTG - 2) {
@@ -732,8 +734,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
               const int4 lo = *(const int4*)&lo_b[q4], hi = *(const int4*)&hi_b[q4];
               const int los[4] = {lo.x, lo.y, lo.z, lo.w}, his[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                s[bq][4 * j + e] = (key >= los[e] && key <= his[e]) ? 0.f : -__builtin_inff();
+              for (int e = 0; e < 4; ++e) {
+                const bool vis = (key >= los[e]) & (key <= his[e]);  // (both compares, no branch)
+                s[bq][4 * j + e] = vis ? 0.f : -__builtin_inff();
+              }
             }
         } else {
           s[0] = f32x16{};
