@@ -353,9 +353,7 @@ def bench_bwd(args):
         L.attn_bwd_gqa(dp.q, dp.k, dp.v, dp.o, dp.lse, dout, dq, dk, dv, delta, scale=p.scale, mask=dp.mask,
                        blockmap=dp.blockmap)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(torch, step, args.warmup, args.warmup_s)  # (the clock settles, as for the forward pass)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -413,9 +411,7 @@ def bench_quant(args):
         for i in range(3):
             L.attn_fp8_quantize(xs[i], codes[i], scales[i], signs[i])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(torch, step, args.warmup, args.warmup_s)  # (the clock settles, as for the forward pass)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
