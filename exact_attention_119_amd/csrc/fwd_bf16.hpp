@@ -192,22 +192,34 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
   //      is read-only here and every index is uniform over the workgroup) -------------
   typedef const __attribute__((address_space(4))) int cint;
   int nfull, npart;
-  cint* flist = nullptr;
-  cint* plist = nullptr;
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
   int kb_first = 0;  // first block of the order (masked: read beside the counts)
   bool invalid = false;
-  // Without a map (causal and window masks, no documents) the lists follow from the
-  // flags.  Every row q sees the keys [lo(q), hi(q)], both ends non-decreasing in q and
-  // q itself inside, so the block's rows r0..r1 together see [lo(r0), hi(r1)] without a
-  // gap: the non-empty key blocks are the range ua..ub; a block is FULL when it lies in
-  // every row's interval, [lo(r1), hi(r0)], and the block has 128 rows; the PARTIAL ones
-  // are the pl blocks left of the FULL range and those right of it.  In the block order
-  // (PARTIAL ascending, then FULL ascending) entry j is block map_entry(j).
+  // Every mask here makes row q see the keys [lo(q), hi(q)], both ends non-decreasing in
+  // q and q itself inside (a document mask within documents whose ids do not decrease --
+  // a batch row where they do is poisoned below).  So the block's rows r0..r1 together see
+  // [lo(r0), hi(r1)] without a gap: the non-empty key blocks are the range ua..ub; a block
+  // is FULL when it lies in every row's interval, [lo(r1), hi(r0)], and the block has 128
+  // rows; the PARTIAL ones are the pl blocks left of the FULL range and those right of it
+  // -- the block map's lists, in the map's order (PARTIAL ascending, then FULL ascending):
+  // entry j is block map_entry(j).  Without a map (causal and window masks) lo and hi
+  // follow from the flags; with one they are the map's row intervals, of which the four
+  // of rows r0 and r1 give the ranges (the map's lists are not read).
   const bool derive = MASKED && a.map == nullptr;
   int ua = 0, fa = 0, fb = -1, pl = 0;
   auto map_entry = [&](int j) -> int {
     return j < pl ? ua + j : (j < npart ? fb + 1 + (j - pl) : fa + (j - npart));
+  };
+  auto set_ranges = [&](int lo0, int lo1, int hi0, int hi1, int r0, int r1) {
+    ua = min(max(lo0 >> 7, 0), nqb - 1);
+    const int ub = min(max(hi1 >> 7, ua), nqb - 1);
+    fa = max(ua, (lo1 + 127) >> 7);
+    fb = min(ub, ((hi0 + 1) >> 7) - 1);
+    if (r1 - r0 != 127 || fa > fb) { fa = ub + 1; fb = ub; }  // no FULL block
+    nfull = fb - fa + 1;
+    npart = ub - ua + 1 - nfull;
+    pl = fa - ua;
+    kb_first = map_entry(0);
   };
   if (MASKED && derive) {
     const int W = a.window;
@@ -217,34 +229,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       return (mf & kCausal) ? q : ((mf & kWindow) ? min(N - 1, q + (W - 1)) : N - 1);
     };
     const int r0 = q0, r1 = min(N, q0 + 128) - 1;
-    ua = lo_of(r0) >> 7;
-    const int ub = hi_of(r1) >> 7;
-    fa = max(ua, (lo_of(r1) + 127) >> 7);
-    fb = min(ub, ((hi_of(r0) + 1) >> 7) - 1);
-    if (r1 - r0 != 127 || fa > fb) { fa = ub + 1; fb = ub; }  // no FULL block
-    nfull = fb - fa + 1;
-    npart = ub - ua + 1 - nfull;
-    pl = fa - ua;
+    set_ranges(lo_of(r0), lo_of(r1), hi_of(r0), hi_of(r1), r0, r1);
     if (qvalid) {
       lo_q = lo_of(qrow);
       hi_q = hi_of(qrow);
     }
-    kb_first = map_entry(0);
   } else if constexpr (MASKED) {
     const __attribute__((address_space(4))) MapHeader* hd =
         (const __attribute__((address_space(4))) MapHeader*)a.map;
     invalid = hd->magic != kMapMagic || hd->B != a.B || hd->N != N || hd->flags != a.mflags ||
               hd->window != a.window;
-    cint* cnt = (cint*)(a.map + a.lay.counts) + ((size_t)b * nqb + qb) * 2;
-    nfull = min(max(cnt[0], 0), nqb);
-    npart = min(max(cnt[1], 0), nqb - nfull);
-    flist = (cint*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
-    plist = flist + nqb;
     {
-      // both list heads are loaded with the counts, so the first tiles can be requested
-      // without waiting for the block order below
-      const int p0 = plist[0], f0 = flist[0];
-      kb_first = min(max(npart > 0 ? p0 : f0, 0), nqb - 1);
+      cint* rlo = (cint*)(a.map + a.lay.row_lo) + (size_t)b * N;
+      cint* rhi = (cint*)(a.map + a.lay.row_hi) + (size_t)b * N;
+      const int r0 = q0, r1 = min(N, q0 + 128) - 1;
+      set_ranges(rlo[r0], rlo[r1], rhi[r0], rhi[r1], r0, r1);
     }
     if (qvalid) {
       lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
@@ -277,8 +276,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     for (int r = 0; r < NKV; ++r) {
       const int j = 64 * r + lane;
       int kb = 0;
-      if (j < nblk) kb = derive ? map_entry(j) : (j < npart ? plist[j] : flist[j - npart]);
-      kbv[r] = min(max(kb, 0), nqb - 1);  // a corrupted map never addresses outside the head
+      if (j < nblk) kb = map_entry(j);
+      kbv[r] = min(max(kb, 0), nqb - 1);  // (never outside the head, whatever the map holds)
     }
   }
   auto step_k0 = [&](int s) -> int {
@@ -290,11 +289,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
       } else if (blk < 64 * NKV) {
         kb = __builtin_amdgcn_readlane(kbv[1], blk - 64);
       } else {
-        // (the empty asm keeps the compiler from hoisting this rare scalar load, and its
-        // wait, above the branch into every step)
-        asm volatile("" ::: "memory");
-        kb = derive ? map_entry(blk) : (blk < npart ? plist[blk] : flist[blk - npart]);
-        kb = min(max(kb, 0), nqb - 1);
+        kb = min(max(map_entry(blk), 0), nqb - 1);
       }
     } else {
       kb = blk < npart ? nqb - 1 : blk - npart;  // the ragged tail block is the PARTIAL one
