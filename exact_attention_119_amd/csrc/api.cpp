@@ -14,7 +14,7 @@
 
 namespace attn119 {
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
-                           const int32_t* doc_id, const int32_t* cu, int nseq, hipStream_t stream);
+                           const int32_t* doc_id, const int32_t* cu, int nseq, bool compact, hipStream_t stream);
 hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t* doc, hipStream_t stream);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
@@ -117,8 +117,8 @@ attn_status check_shape(int32_t B, int32_t N) {
   return ATTN_OK;
 }
 
-// Variable-length workspace: the block map of (B = 1, N = total), then the doc ids.
-size_t varlen_doc_offset(int32_t total) { return map_layout(1, total).total; }
+// Variable-length workspace: the compact block map of (B = 1, N = total), then the doc ids.
+size_t varlen_doc_offset(int32_t total) { return map_layout(1, total, true).total; }
 size_t varlen_bytes(int32_t total) { return varlen_doc_offset(total) + align256((size_t)total * 4); }
 
 attn_status check_varlen_mask(const attn_mask* mask) {
@@ -192,7 +192,7 @@ attn_status attn_blockmap_build(int32_t B, int32_t N, const attn_mask* mask, voi
   const uint32_t flags = mask ? mask->flags : 0u;
   const int window = (mask && (flags & ATTN_WINDOW)) ? mask->window : 0;
   const int32_t* doc = (mask && (flags & ATTN_DOCUMENT)) ? mask->doc_id : nullptr;
-  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, (hipStream_t)stream) !=
+  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, false, (hipStream_t)stream) !=
       hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -204,8 +204,11 @@ attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
   MapHeader hd;
   if (hipMemcpy(&hd, map, sizeof(hd), hipMemcpyDeviceToHost) != hipSuccess) return ATTN_ERR_HIP;
   if (hd.magic != kMapMagic || check_shape(hd.B, hd.N) != ATTN_OK) return ATTN_ERR_BAD_BLOCKMAP;
-  const MapLayout m = map_layout(hd.B, hd.N);
-  if (bytes != m.total) return ATTN_ERR_BAD_BLOCKMAP;
+  if (hd.compact != 0 && (hd.compact != 1 || hd.B != 1)) return ATTN_ERR_BAD_BLOCKMAP;
+  const MapLayout m = map_layout(hd.B, hd.N, hd.compact != 0);
+  // a compact map comes inside a packed batch's workspace: the map alone or the whole
+  // workspace
+  if (bytes != m.total && !(hd.compact && bytes == varlen_bytes(hd.N))) return ATTN_ERR_BAD_BLOCKMAP;
   const size_t n = (size_t)hd.B * hd.nqb;
   int32_t* st = new int32_t[n];
   const hipError_t e = hipMemcpy(st, (const unsigned char*)map + m.status, n * 4, hipMemcpyDeviceToHost);
@@ -216,10 +219,16 @@ attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
   return bad ? ATTN_ERR_BAD_DOC_ID : ATTN_OK;
 }
 
-attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                                int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
-                                const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
-                                const attn_fp8* fp8, float rescale_tau) {
+}  // extern "C"
+
+namespace {
+
+// attn_check_args_gqa; compact_map: the map is the compact form of a packed batch's
+// workspace
+attn_status check_args_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
+                            int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
+                            const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
+                            bool compact_map) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARG;
@@ -253,10 +262,22 @@ attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, voi
     const bool need = (mask->flags & ATTN_DOCUMENT) != 0;
     if (blockmap || need) {
       if (!blockmap || !aligned16(blockmap)) return ATTN_ERR_BAD_BLOCKMAP;
-      if (blockmap_bytes != map_layout(B, N).total) return ATTN_ERR_BAD_BLOCKMAP;
+      if (blockmap_bytes != map_layout(B, N, compact_map).total) return ATTN_ERR_BAD_BLOCKMAP;
     }
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                                int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
+                                const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                                const attn_fp8* fp8, float rescale_tau) {
+  return check_args_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap, blockmap_bytes, fp8,
+                         rescale_tau, false);
 }
 
 attn_status attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
@@ -284,9 +305,9 @@ namespace {
 attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
                      int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
                      const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
-                     int32_t* counts, void* stream) {
-  const attn_status st = attn_check_args_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap,
-                                             blockmap_bytes, fp8, rescale_tau);
+                     int32_t* counts, void* stream, bool compact_map = false) {
+  const attn_status st = check_args_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap,
+                                         blockmap_bytes, fp8, rescale_tau, compact_map);
   if (st != ATTN_OK) return st;
   const uint32_t flags = mask ? mask->flags : 0u;
   const bool masked = positional(mask);
@@ -321,7 +342,8 @@ attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float
   }
   if (masked) {
     a.map = (const unsigned char*)blockmap;
-    a.lay = map_layout(B, N);
+    a.lay = map_layout(B, N, compact_map);
+    a.compact = compact_map ? 1 : 0;
     a.mflags = flags & (ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT);
     a.window = (flags & ATTN_WINDOW) ? mask->window : 0;
   }
@@ -417,7 +439,7 @@ attn_status attn_varlen_prepare(const int32_t* cu_seqlens, int32_t nseq, int32_t
   const hipStream_t s = (hipStream_t)stream;
   if (launch_varlen_doc_ids(cu_seqlens, nseq, total, (int32_t*)m.doc_id, s) != hipSuccess) return ATTN_ERR_HIP;
   const int window = (m.flags & ATTN_WINDOW) ? m.window : 0;
-  if (launch_blockmap((unsigned char*)workspace, 1, total, m.flags, window, m.doc_id, cu_seqlens, nseq, s) !=
+  if (launch_blockmap((unsigned char*)workspace, 1, total, m.flags, window, m.doc_id, cu_seqlens, nseq, true, s) !=
       hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -433,8 +455,25 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
   if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
   const attn_mask m = varlen_mask(mask, workspace, total);
-  return attn_fwd_gqa(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace,
-                      varlen_doc_offset(total), fp8, rescale_tau, stream);
+  return fwd_impl(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace, varlen_doc_offset(total), fp8,
+                  rescale_tau, nullptr, stream, true);
+}
+
+attn_status attn_varlen_layout_of(int32_t total, attn_blockmap_layout* layout) {
+  if (!layout) return ATTN_ERR_INVALID_ARG;
+  const attn_status st = check_shape(1, total);
+  if (st != ATTN_OK) return st;
+  const MapLayout m = map_layout(1, total, true);
+  layout->cls = m.cls;
+  layout->counts = m.counts;
+  layout->idx = m.idx;
+  layout->row_lo = m.row_lo;
+  layout->row_hi = m.row_hi;
+  layout->pairs = m.pairs;
+  layout->status = m.status;
+  layout->order = m.order;
+  layout->total = m.total;
+  return ATTN_OK;
 }
 
 attn_status attn_fp8_quantize(const void* x, void* codes, float* scales, int32_t B, int32_t H, int32_t N,

@@ -14,6 +14,13 @@
 //          such word is invalid);
 //   its row of blocks: the class of every 128x128 block, the ascending lists of FULL
 //          and PARTIAL key blocks and the visible-pair count of the query block.
+// The compact form (the workspace of a packed batch, read only by the forward pass) has
+// no class and list sections, so that it grows as O(N): its FULL and PARTIAL counts come
+// from the intervals of the block's first and last rows r0 and r1 alone.  Every row sees
+// itself and both ends of the intervals are non-decreasing in the row, so the rows'
+// intervals together cover [lo(r0), hi(r1)] without a gap (the non-empty key blocks are
+// those that meet it), and a key block is FULL exactly when it lies inside
+// [lo(r1), hi(r0)] with 128 keys and the query block has 128 rows.
 // A second launch, for document masks only, fills the work-order section: the
 // (batch row, query block) pairs heaviest-first by the work of their block lists (other
 // masks keep the identity order the first launch writes; their work is known from the
@@ -33,6 +40,7 @@ struct MapArgs {
   int window;
   const int32_t* cu;  // packed variable-length batch (B = 1): offsets [nseq + 1], else null
   int nseq;
+  int compact;        // 1: the compact form (no class and list sections)
 };
 
 // Narrows a search interval [lo, hi] after a round whose probes lo + t*step (t < 256)
@@ -173,56 +181,67 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   if (lane == 0) s_pairs[wave] = my_pairs;
   __syncthreads();
 
-  unsigned char* cls = a.map + a.lay.cls + ((size_t)b * nb + qb) * nb;
-  int32_t* idx_full = (int32_t*)(a.map + a.lay.idx) + ((size_t)b * nb + qb) * 2 * nb;
-  int32_t* idx_part = idx_full + nb;
-
-  // classes and ascending CSR lists, up to 256 key blocks per round.  Wave w holds rows
-  // 64*(w%2) + lane (their intervals in registers) and tests the key blocks of parity w/2
-  // against all of them at once: one ballot for "some row sees a key of the block", one
-  // for "every row sees all of it".
-  __shared__ unsigned char s_any[2][256], s_all[2][256];
-  const int half = wave & 1;
-  const int my_lo = s_lo[64 * half + lane], my_hi = s_hi[64 * half + lane];
   int full_base = 0, part_base = 0;
-  for (int kb0 = 0; kb0 < nb; kb0 += 256) {
-    const int K = min(256, nb - kb0);
-    for (int kl = wave >> 1; kl < K; kl += 2) {
-      const int k0 = (kb0 + kl) * kBlock, k1 = min(N, k0 + kBlock) - 1;
-      const uint64_t any = __ballot(max(my_lo, k0) <= min(my_hi, k1));
-      const uint64_t all = __ballot(my_lo <= k0 && my_hi >= k1);
-      if (lane == 0) {
-        s_any[half][kl] = any != 0;
-        s_all[half][kl] = all == ~0ull;
+  if (a.compact) {
+    // counts from the first and last rows' intervals (an empty row, possible only in a
+    // batch row marked invalid, has [0, -1])
+    const int lo0 = s_lo[0], lo1 = s_lo[nrows - 1], hi0 = s_hi[0], hi1 = s_hi[nrows - 1];
+    const int ua = lo0 / kBlock, ub = hi1 < 0 ? -1 : hi1 / kBlock;
+    const int nne = max(0, ub - ua + 1);
+    const int fa = (lo1 + kBlock - 1) / kBlock, fz = (hi0 + 1) / kBlock - 1;
+    full_base = nrows == kBlock ? min(max(0, fz - fa + 1), nne) : 0;
+    part_base = nne - full_base;
+  } else {
+    unsigned char* cls = a.map + a.lay.cls + ((size_t)b * nb + qb) * nb;
+    int32_t* idx_full = (int32_t*)(a.map + a.lay.idx) + ((size_t)b * nb + qb) * 2 * nb;
+    int32_t* idx_part = idx_full + nb;
+
+    // classes and ascending CSR lists, up to 256 key blocks per round.  Wave w holds rows
+    // 64*(w%2) + lane (their intervals in registers) and tests the key blocks of parity w/2
+    // against all of them at once: one ballot for "some row sees a key of the block", one
+    // for "every row sees all of it".
+    __shared__ unsigned char s_any[2][256], s_all[2][256];
+    const int half = wave & 1;
+    const int my_lo = s_lo[64 * half + lane], my_hi = s_hi[64 * half + lane];
+    for (int kb0 = 0; kb0 < nb; kb0 += 256) {
+      const int K = min(256, nb - kb0);
+      for (int kl = wave >> 1; kl < K; kl += 2) {
+        const int k0 = (kb0 + kl) * kBlock, k1 = min(N, k0 + kBlock) - 1;
+        const uint64_t any = __ballot(max(my_lo, k0) <= min(my_hi, k1));
+        const uint64_t all = __ballot(my_lo <= k0 && my_hi >= k1);
+        if (lane == 0) {
+          s_any[half][kl] = any != 0;
+          s_all[half][kl] = all == ~0ull;
+        }
       }
+      __syncthreads();
+      const int kb = kb0 + tid;
+      int c = 0;
+      if (tid < K) {
+        const int k0 = kb * kBlock, k1 = min(N, k0 + kBlock) - 1;
+        const bool any = s_any[0][tid] | s_any[1][tid];
+        const bool all = s_all[0][tid] & s_all[1][tid] & (nrows == kBlock) & (k1 - k0 + 1 == kBlock);
+        c = !any ? 0 : (all ? 2 : 1);
+        cls[kb] = (unsigned char)c;
+      }
+      const uint64_t mfull = __ballot(c == 2);
+      const uint64_t mpart = __ballot(c == 1);
+      if (lane == 0) {
+        s_wave_full[wave] = __popcll(mfull);
+        s_wave_part[wave] = __popcll(mpart);
+      }
+      __syncthreads();
+      int fb = full_base, pbase = part_base;
+      for (int w = 0; w < wave; ++w) { fb += s_wave_full[w]; pbase += s_wave_part[w]; }
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      if (c == 2) idx_full[fb + __popcll(mfull & below)] = kb;
+      if (c == 1) idx_part[pbase + __popcll(mpart & below)] = kb;
+      for (int w = 0; w < 4; ++w) { full_base += s_wave_full[w]; part_base += s_wave_part[w]; }
+      __syncthreads();
     }
-    __syncthreads();
-    const int kb = kb0 + tid;
-    int c = 0;
-    if (tid < K) {
-      const int k0 = kb * kBlock, k1 = min(N, k0 + kBlock) - 1;
-      const bool any = s_any[0][tid] | s_any[1][tid];
-      const bool all = s_all[0][tid] & s_all[1][tid] & (nrows == kBlock) & (k1 - k0 + 1 == kBlock);
-      c = !any ? 0 : (all ? 2 : 1);
-      cls[kb] = (unsigned char)c;
-    }
-    const uint64_t mfull = __ballot(c == 2);
-    const uint64_t mpart = __ballot(c == 1);
-    if (lane == 0) {
-      s_wave_full[wave] = __popcll(mfull);
-      s_wave_part[wave] = __popcll(mpart);
-    }
-    __syncthreads();
-    int fb = full_base, pbase = part_base;
-    for (int w = 0; w < wave; ++w) { fb += s_wave_full[w]; pbase += s_wave_part[w]; }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (c == 2) idx_full[fb + __popcll(mfull & below)] = kb;
-    if (c == 1) idx_part[pbase + __popcll(mpart & below)] = kb;
-    for (int w = 0; w < 4; ++w) { full_base += s_wave_full[w]; part_base += s_wave_part[w]; }
-    __syncthreads();
+    for (int i = full_base + tid; i < nb; i += 256) idx_full[i] = -1;
+    for (int i = part_base + tid; i < nb; i += 256) idx_part[i] = -1;
   }
-  for (int i = full_base + tid; i < nb; i += 256) idx_full[i] = -1;
-  for (int i = part_base + tid; i < nb; i += 256) idx_part[i] = -1;
   if (tid == 0 && b == 0 && qb == 0) {
     MapHeader* hd = (MapHeader*)a.map;
     hd->magic = kMapMagic;
@@ -234,7 +253,8 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
     hd->window = a.window;
     hd->order_full_cost = kOrderFullCost;
     hd->order_partial_cost = kOrderPartialCost;
-    for (int i = 0; i < 7; ++i) hd->reserved[i] = 0;
+    hd->compact = a.compact;
+    for (int i = 0; i < 6; ++i) hd->reserved[i] = 0;
   }
   if (tid == 0) {
     int32_t* counts = (int32_t*)(a.map + a.lay.counts) + ((size_t)b * nb + qb) * 2;
@@ -295,10 +315,11 @@ hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t
 }
 
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
-                           const int32_t* doc_id, const int32_t* cu, int nseq, hipStream_t stream) {
+                           const int32_t* doc_id, const int32_t* cu, int nseq, bool compact, hipStream_t stream) {
   MapArgs a;
   a.map = map;
-  a.lay = map_layout(B, N);
+  a.lay = map_layout(B, N, compact);
+  a.compact = compact ? 1 : 0;
   a.doc_id = doc_id;
   a.B = B;
   a.N = N;

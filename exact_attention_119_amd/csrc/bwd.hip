@@ -212,7 +212,7 @@ __device__ __forceinline__ float head_slope(const BwdArgs& a, int h) {
 __device__ bool map_invalid(const BwdArgs& a, int b) {
   const MapHeader* hd = (const MapHeader*)a.map;
   bool bad = hd->magic != kMapMagic || hd->B != a.B || hd->N != a.N || hd->flags != (a.flags & kPositional) ||
-             hd->window != ((a.flags & kWindow) ? a.window : 0);
+             hd->window != ((a.flags & kWindow) ? a.window : 0) || hd->compact != 0;
   int st = 0;
   if (a.flags & kDocument) {
     const int* s = (const int*)(a.map + a.lay.status) + (size_t)b * a.nqb;

@@ -100,23 +100,25 @@ constexpr int kOrderFullCost = 2, kOrderPartialCost = 5;
 constexpr uint32_t kCausal = 1, kWindow = 2, kDocument = 4, kAlibi = 8, kSoftcap = 16;
 constexpr uint32_t kPositional = kCausal | kWindow | kDocument;
 
-// Byte offsets of the block-map sections (see attn_blockmap_header in attn119.h).
+// Byte offsets of the block-map sections (see attn_blockmap_header in attn119.h).  The
+// compact form (the workspace of a packed batch) has no class and list sections; their
+// offsets are 0 there, and every other section is O(N).
 struct MapLayout {
   size_t cls, counts, idx, row_lo, row_hi, pairs, status, order, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline MapLayout map_layout(int B, int N) {
+__host__ __device__ inline MapLayout map_layout(int B, int N, bool compact = false) {
   const size_t nb = (size_t)((N + kBlock - 1) / kBlock);
   MapLayout m;
   size_t off = 256;  // header
-  m.cls = off;
-  off = align256(off + (size_t)B * nb * nb);
+  m.cls = compact ? 0 : off;
+  if (!compact) off = align256(off + (size_t)B * nb * nb);
   m.counts = off;
   off = align256(off + (size_t)B * nb * 2 * 4);
-  m.idx = off;
-  off = align256(off + (size_t)B * nb * 2 * nb * 4);
+  m.idx = compact ? 0 : off;
+  if (!compact) off = align256(off + (size_t)B * nb * 2 * nb * 4);
   m.row_lo = off;
   off = align256(off + (size_t)B * N * 4);
   m.row_hi = off;
@@ -137,7 +139,8 @@ struct MapHeader {
   uint32_t flags;
   int32_t window;
   int32_t order_full_cost, order_partial_cost;  // weights of the work order (kOrder*Cost)
-  int32_t reserved[7];
+  int32_t compact;                              // 1: the compact form (no cls, no idx)
+  int32_t reserved[6];
 };
 
 }  // namespace attn119

@@ -25,6 +25,7 @@ struct FwdArgs {
   const float* v_scale;
   const unsigned char* map;   // block map (masked variants)
   MapLayout lay;
+  int compact;                // 1: the map is the compact form (a packed batch's workspace)
   uint32_t mflags;            // positional mask flags the map was built for
   int window;
   int order;                  // work order: kOrderHeadMajor or kOrderHeavyFirst

@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(const FwdArgs a) 
     const __attribute__((address_space(4))) MapHeader* hd =
         (const __attribute__((address_space(4))) MapHeader*)a.map;
     invalid = hd->magic != kMapMagic || hd->B != a.B || hd->N != N || hd->flags != a.mflags ||
-              hd->window != a.window;
+              hd->window != a.window || hd->compact != a.compact;
     {
       cint* rlo = (cint*)(a.map + a.lay.row_lo) + (size_t)b * N;
       cint* rhi = (cint*)(a.map + a.lay.row_hi) + (size_t)b * N;

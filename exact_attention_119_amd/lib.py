@@ -44,7 +44,7 @@ EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_buil
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
            "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa", "attn_bwd_gqa_noalloc",
-           "attn_fwd_rescale_counts")
+           "attn_fwd_rescale_counts", "attn_varlen_layout_of")
 
 
 class AttnError(RuntimeError):
@@ -107,6 +107,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_rescale_counts.restype = i32
     lib.attn_varlen_workspace_bytes.argtypes = [i32, ctypes.POINTER(attn_mask), ctypes.POINTER(sz)]
     lib.attn_varlen_workspace_bytes.restype = i32
+    lib.attn_varlen_layout_of.argtypes = [i32, ctypes.POINTER(attn_blockmap_layout)]
+    lib.attn_varlen_layout_of.restype = i32
     lib.attn_varlen_prepare.argtypes = [vp, i32, i32, ctypes.POINTER(attn_mask), vp, sz, vp]
     lib.attn_varlen_prepare.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
@@ -173,6 +175,14 @@ def attn_blockmap_bytes(B: int, N: int, mask: Optional[attn_mask] = None) -> int
 def attn_blockmap_layout_of(B: int, N: int) -> dict:
     lay = attn_blockmap_layout()
     _check(load().attn_blockmap_layout_of(B, N, ctypes.byref(lay)), "attn_blockmap_layout_of")
+    return {n: getattr(lay, n) for n, _ in attn_blockmap_layout._fields_}
+
+
+def attn_varlen_layout_of(total: int) -> dict:
+    """Offsets of the compact block map inside a packed batch's workspace (cls and idx 0:
+    absent; the sequence ids start at `total`)."""
+    lay = attn_blockmap_layout()
+    _check(load().attn_varlen_layout_of(int(total), ctypes.byref(lay)), "attn_varlen_layout_of")
     return {n: getattr(lay, n) for n, _ in attn_blockmap_layout._fields_}
 
 
@@ -322,21 +332,26 @@ def attn_bwd_gqa_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, scale: float, mas
            "attn_bwd_gqa_noalloc")
 
 
-def read_blockmap(blockmap, B: int, N: int) -> dict:
-    """Splits a block map copied back to the host into its sections (numpy)."""
+def read_blockmap(blockmap, B: int, N: int, compact: bool = False) -> dict:
+    """Splits a block map copied back to the host into its sections (numpy); the compact
+    form (a packed batch's workspace, B = 1) has no "cls" and "idx" (None)."""
     raw = blockmap.detach().cpu().numpy() if hasattr(blockmap, "detach") else np.asarray(blockmap)
     raw = raw.view(np.uint8)
-    lay = attn_blockmap_layout_of(B, N)
+    if compact:
+        assert B == 1
+    lay = attn_varlen_layout_of(N) if compact else attn_blockmap_layout_of(B, N)
     nb = (N + 127) // 128
     hdr = raw[:64].view(np.int32)
 
     def sec(name, dtype, shape):
+        if compact and name in ("cls", "idx"):
+            return None
         n = int(np.prod(shape)) * np.dtype(dtype).itemsize
         return raw[lay[name]:lay[name] + n].view(dtype).reshape(shape)
 
     return dict(header=dict(magic=int(hdr.view(np.uint32)[0]), B=int(hdr[1]), N=int(hdr[2]), nqb=int(hdr[3]),
                             nkb=int(hdr[4]), flags=int(hdr.view(np.uint32)[5]), window=int(hdr[6]),
-                            order_full_cost=int(hdr[7]), order_partial_cost=int(hdr[8])),
+                            order_full_cost=int(hdr[7]), order_partial_cost=int(hdr[8]), compact=int(hdr[9])),
                 cls=sec("cls", np.uint8, (B, nb, nb)), counts=sec("counts", np.int32, (B, nb, 2)),
                 idx=sec("idx", np.int32, (B, nb, 2, nb)), row_lo=sec("row_lo", np.int32, (B, N)),
                 row_hi=sec("row_hi", np.int32, (B, N)), pairs=sec("pairs", np.int64, (B, nb)),

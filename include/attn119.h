@@ -157,6 +157,14 @@ typedef struct attn_fp8 {
  *                                       order_partial_cost * #PARTIAL (weights in the
  *                                       header), equal work in increasing e; without it the
  *                                       identity 0 .. B*nqb-1
+ *
+ * The compact form, inside the workspace of a packed batch (attn_varlen_prepare), has
+ * B = 1, header.compact = 1 and the sections above without cls and idx, so that it
+ * grows as O(N) rather than O(N^2 / 128^2) (attn_varlen_layout_of gives its offsets,
+ * with cls = idx = 0).  Only the forward pass reads it: every query row's visible keys
+ * form one interval [row_lo, row_hi] whose ends never decrease from row to row, so a
+ * query block's non-empty and FULL key blocks follow from the intervals of its first
+ * and last rows, and the class and list sections are not needed.
  */
 typedef struct attn_blockmap_header {
   uint32_t magic; /* 0x39313141 */
@@ -165,7 +173,8 @@ typedef struct attn_blockmap_header {
   int32_t window;
   int32_t order_full_cost;    /* work of a FULL key block in the work order */
   int32_t order_partial_cost; /* work of a PARTIAL key block in the work order */
-  int32_t reserved[7];
+  int32_t compact;            /* 0: the layout above; 1: the compact form (packed batches) */
+  int32_t reserved[6];
 } attn_blockmap_header;
 
 typedef struct attn_blockmap_layout {
@@ -188,7 +197,12 @@ attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* 
 attn_status attn_blockmap_build(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes,
                                 void* stream);
 
-/* Synchronises `stream`, then reads the map's status section: ATTN_OK or ATTN_ERR_BAD_DOC_ID. */
+/*
+ * Synchronises `stream`, then reads the map's status section: ATTN_OK or
+ * ATTN_ERR_BAD_DOC_ID.  `bytes` is the map's size (attn_blockmap_bytes; for the compact
+ * form of a packed batch attn_varlen_layout_of's total, or the whole workspace's
+ * attn_varlen_workspace_bytes).
+ */
 attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream);
 
 /*
@@ -281,18 +295,22 @@ attn_status attn_fwd_rescale_counts(const void* q, const void* k, const void* v,
  *               cu_seqlens[i+1]-1 (empty sequences allowed).  An offset array that
  *               breaks this (a decrease, a first entry other than 0, a last entry other
  *               than total) is reported by attn_blockmap_status(workspace,
- *               attn_blockmap_bytes(1, total, mask)) as ATTN_ERR_BAD_DOC_ID, and O and
- *               LSE are then NaN.
+ *               attn_varlen_workspace_bytes(total, mask)) as ATTN_ERR_BAD_DOC_ID, and O
+ *               and LSE are then NaN.
  *   q, o : [H][total][d];  k, v : [H_kv][total][d];  lse : [H][total]   (B = 1 layout)
  *   fp8 scales: q_scale [H][ceil(total/128)], k_scale and v_scale [H_kv][ceil(total/128)],
  *               one scale per 128 tokens of the packed stream.
  *   workspace : caller-owned device memory of attn_varlen_workspace_bytes, 16-byte
- *               aligned: the block map of (1, total), then the int32 sequence id of
- *               every token.  attn_varlen_prepare fills it once per batch; any number
+ *               aligned: the compact block map of (1, total) (offsets from
+ *               attn_varlen_layout_of), then the int32 sequence id of every token at
+ *               the layout's total; O(total) bytes.  attn_varlen_prepare fills it once per batch; any number
  *               of attn_fwd_varlen calls (say, one per layer) then read it.
  * Errors as attn_check_args_gqa; a workspace of the wrong size is ATTN_ERR_BAD_BLOCKMAP.
  */
 attn_status attn_varlen_workspace_bytes(int32_t total, const attn_mask* mask, size_t* bytes);
+/* Byte offsets of the compact block map's sections in the workspace (cls = idx = 0: absent;
+ * total: the map's size, where the sequence ids start).  Host only. */
+attn_status attn_varlen_layout_of(int32_t total, attn_blockmap_layout* layout);
 attn_status attn_varlen_prepare(const int32_t* cu_seqlens, int32_t nseq, int32_t total, const attn_mask* mask,
                                 void* workspace, size_t bytes, void* stream);
 attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int32_t H,

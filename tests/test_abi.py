@@ -137,11 +137,22 @@ def test_check_args_grouped_heads(L):
 
 
 def test_varlen_validation(L):
-    """Packed variable-length batches: workspace = block map of (1, total), then int32 ids."""
+    """Packed variable-length batches: workspace = the compact block map of (1, total)
+    (no class and list sections: O(total) bytes), then int32 ids."""
     m = L.make_mask(L.ATTN_CAUSAL)
-    for total in (1, 300, 4096):
-        mb = L.attn_blockmap_bytes(1, total, m)
-        assert L.attn_varlen_workspace_bytes(total, m) == mb + ((4 * total + 255) // 256) * 256
+    for total in (1, 300, 4096, 1 << 20):
+        lay = L.attn_varlen_layout_of(total)
+        nb = (total + 127) // 128
+        full = L.attn_blockmap_layout_of(1, total)
+        assert lay["cls"] == 0 and lay["idx"] == 0 and lay["counts"] == 256
+        names = ["counts", "row_lo", "row_hi", "pairs", "status", "order", "total"]
+        for a, b in zip(names, names[1:]):
+            assert lay[a] < lay[b] and lay[b] % 256 == 0
+            if a != "counts":  # the same sections as the full map's, without cls and idx
+                assert lay[b] - lay[a] == full[b] - full[a]
+        assert lay["row_lo"] - lay["counts"] >= 8 * nb
+        assert lay["total"] <= 256 * 7 + 8 * total + 24 * nb  # O(total)
+        assert L.attn_varlen_workspace_bytes(total, m) == lay["total"] + ((4 * total + 255) // 256) * 256
         assert L.attn_varlen_workspace_bytes(total, None) == L.attn_varlen_workspace_bytes(total, m)
     with pytest.raises(L.AttnError):
         L.attn_varlen_workspace_bytes(300, L.make_mask(L.ATTN_DOCUMENT, doc_id=P))

@@ -1,6 +1,6 @@
 """GPU parity for packed variable-length batches: attn_varlen_prepare (sequence ids and
-block map, bit-exact against the oracle's) and attn_fwd_varlen against the fp64 oracle,
-which runs every sequence on its own."""
+the compact block map, bit-exact against the oracle's) and attn_fwd_varlen against the
+fp64 oracle, which runs every sequence on its own."""
 
 import numpy as np
 import pytest
@@ -60,24 +60,49 @@ def _run(p, tau=8.0):
     return dp, o, lse
 
 
+def _classes_from_intervals(row_lo, row_hi, N):
+    """Class of every 128x128 block from the intervals of each query block's first and
+    last rows alone: non-empty where the key block meets [lo(r0), hi(r1)], FULL where it
+    lies inside [lo(r1), hi(r0)] (128 rows, 128 keys)."""
+    nb = (N + 127) // 128
+    cls = np.zeros((nb, nb), dtype=np.uint8)
+    for qb in range(nb):
+        r0, r1 = 128 * qb, min(N, 128 * qb + 128) - 1
+        lo0, lo1, hi0, hi1 = (int(x) for x in (row_lo[r0], row_lo[r1], row_hi[r0], row_hi[r1]))
+        if hi1 >= lo0:
+            cls[qb, lo0 // 128:hi1 // 128 + 1] = 1
+        if r1 - r0 == 127:
+            fa, fz = -(-lo1 // 128), (hi0 + 1) // 128 - 1
+            if fz >= fa:
+                cls[qb, fa:fz + 1] = 2
+    return cls
+
+
 def _check_prepared(dp):
-    """Sequence ids and block map in the workspace equal the oracle's byte for byte."""
+    """Sequence ids and the compact block map in the workspace equal the oracle's byte for
+    byte, and the intervals give the oracle's block classes."""
     p = dp.p
-    mb = L.attn_blockmap_bytes(1, p.N, dp.mask)
+    lay = L.attn_varlen_layout_of(p.N)
+    mb = lay["total"]
+    assert lay["cls"] == 0 and lay["idx"] == 0
+    assert dp.blockmap.numel() == mb + (4 * p.N + 255) // 256 * 256
     raw = dp.blockmap.cpu().numpy()
     ids = raw[mb:mb + 4 * p.N].view(np.int32)
     ids_ref = oracle.varlen_doc_ids_ref(p.cu_seqlens, p.N)
     np.testing.assert_array_equal(ids, ids_ref)
-    got = L.read_blockmap(dp.blockmap[:mb], 1, p.N)
+    got = L.read_blockmap(dp.blockmap[:mb], 1, p.N, compact=True)
     flags = (p.flags & L.POSITIONAL) | L.ATTN_DOCUMENT
     ref = oracle.blockmap_ref(1, p.N, flags, p.window, ids_ref[None])
-    assert (got["header"]["B"], got["header"]["N"], got["header"]["flags"]) == (1, p.N, flags)
+    hd = got["header"]
+    assert (hd["B"], hd["N"], hd["flags"], hd["compact"]) == (1, p.N, flags, 1)
     np.testing.assert_array_equal(got["status"], ref["status"])
-    for key in ("cls", "counts", "idx", "row_lo", "row_hi"):
+    for key in ("counts", "row_lo", "row_hi"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    np.testing.assert_array_equal(_classes_from_intervals(got["row_lo"][0], got["row_hi"][0], p.N), ref["cls"][0])
     check_work_order(got["order"], got["counts"], got["header"], True)
     np.testing.assert_array_equal(got["pairs"], ref["qb_pairs"])
     assert L.attn_blockmap_status(dp.blockmap[:mb]) == L.ATTN_OK
+    assert L.attn_blockmap_status(dp.blockmap) == L.ATTN_OK
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -134,8 +159,9 @@ def test_varlen_bad_offsets_reported_and_output_poisoned(cu):
     p.cu_seqlens = np.asarray(cu, dtype=np.int32)
     _announce("varlen bad offsets", cu)
     dp, o, lse = _run(p)
-    mb = L.attn_blockmap_bytes(1, p.N, dp.mask)
+    mb = L.attn_varlen_layout_of(p.N)["total"]
     assert L.attn_blockmap_status(dp.blockmap[:mb]) == L.ATTN_ERR_BAD_DOC_ID
+    assert L.attn_blockmap_status(dp.blockmap) == L.ATTN_ERR_BAD_DOC_ID
     assert np.isnan(o).all() and np.isnan(lse).all()
 
 
