@@ -177,3 +177,35 @@ def test_varlen_full_size_sampled():
     heads = [(0, h) for h in range(p.H)]
     o_ref, lse_ref = oracle.attention_problem(p, rows=rows, heads=heads, workers=8)
     assert_close(p, o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, "varlen full size sampled")
+
+
+def test_varlen_million_tokens_compact_workspace():
+    """1,048,576 packed tokens in causal sequences of 512 .. 8192 (H1 d64): the workspace
+    is the compact map plus the ids, under 16 bytes per token (the map with classes and
+    lists would take 0.62 GB); its row intervals on sampled rows and its FULL/PARTIAL
+    counts on sampled query blocks equal the oracle's, and so do O and LSE on sampled rows."""
+    rng = np.random.default_rng([119, 79])
+    lengths = W.draw_doc_lengths(rng, 1 << 20, 512, 8192)
+    p = W.make_varlen_problem(lengths, 1, 64, flags=C, seed=79)
+    _announce("varlen 1M tokens", p.name, len(lengths))
+    dp, o, lse = _run(p)
+    N = p.N
+    lay = L.attn_varlen_layout_of(N)
+    assert dp.blockmap.numel() == L.attn_varlen_workspace_bytes(N, dp.mask) < 16 * N
+    assert L.attn_blockmap_status(dp.blockmap) == L.ATTN_OK
+    got = L.read_blockmap(dp.blockmap[:lay["total"]], 1, N, compact=True)
+    ids = oracle.varlen_doc_ids_ref(p.cu_seqlens, N)
+    flags = C | L.ATTN_DOCUMENT
+    kpos = np.arange(N)
+    rows = sample_rows(N, 64, seed=79)
+    vis = oracle.visible(rows, kpos, flags, 0, ids)
+    np.testing.assert_array_equal(got["row_lo"][0][rows], vis.argmax(axis=1))
+    np.testing.assert_array_equal(got["row_hi"][0][rows], N - 1 - vis[:, ::-1].argmax(axis=1))
+    nb = N // 128
+    for qb in sorted({0, 1, nb - 1, *np.random.default_rng(79).choice(nb, 3, replace=False).tolist()}):
+        blk = oracle.visible(np.arange(128 * qb, 128 * qb + 128), kpos, flags, 0, ids).reshape(128, nb, 128)
+        anyv, allv = blk.any(axis=(0, 2)), blk.all(axis=(0, 2))
+        full, part = int(allv.sum()), int((anyv & ~allv).sum())
+        assert tuple(got["counts"][0, qb]) == (full, part), qb
+    o_ref, lse_ref = oracle.attention_problem(p, rows=rows)
+    assert_close(p, o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, "varlen 1M tokens sampled")
