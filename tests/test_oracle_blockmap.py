@@ -152,3 +152,40 @@ def test_work_order_checker_accepts_the_order_and_rejects_mistakes():
     check_work_order(np.arange(len(work)), m["counts"], hd, False)
     with pytest.raises(AssertionError):
         check_work_order(order, m["counts"], hd, False)
+
+
+def _classes_from_end_rows(lo, hi, N, block):
+    """The rule the kernels use to find a query block's key blocks without listing them:
+    non-empty are the key blocks that meet [lo(r0), hi(r1)] of its first and last rows r0,
+    r1; FULL are those inside [lo(r1), hi(r0)], for a block of `block` rows and keys."""
+    nb = -(-N // block)
+    cls = np.zeros((nb, nb), np.uint8)
+    for qb in range(nb):
+        r0, r1 = qb * block, min(N, qb * block + block) - 1
+        if hi[r1] >= lo[r0]:
+            cls[qb, lo[r0] // block:hi[r1] // block + 1] = PARTIAL
+        if r1 - r0 + 1 == block:
+            fa, fz = -(-lo[r1] // block), (hi[r0] + 1) // block - 1
+            if fz >= fa:
+                cls[qb, fa:fz + 1] = FULL
+    return cls
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_end_row_interval_rule_gives_every_class(seed):
+    """Every supported mask (causal, window, contiguous documents and their conjunctions)
+    gives each row one interval of keys whose ends never decrease and which holds the row
+    itself, so a block's classes follow from its first and last rows' intervals alone:
+    checked against the brute-force classes on random masks, lengths and block sizes."""
+    rng = np.random.default_rng([119, 57, seed])
+    block = int(rng.choice([4, 8, 16]))
+    N = int(rng.integers(1, 12 * block))
+    flags = int(rng.choice([CAUSAL, WINDOW, DOCUMENT, CAUSAL | WINDOW, CAUSAL | DOCUMENT, WINDOW | DOCUMENT,
+                            CAUSAL | WINDOW | DOCUMENT]))
+    W = int(rng.integers(1, 3 * block))
+    doc = np.repeat(np.arange(N), rng.integers(1, 3 * block, N))[:N].astype(np.int32)
+    m = O.blockmap_ref(1, N, flags, W, doc[None], block=block)
+    lo, hi, contiguous = O.row_intervals_ref(N, flags, W, doc)
+    assert contiguous and np.all(np.diff(lo) >= 0) and np.all(np.diff(hi) >= 0)
+    assert np.all((lo <= np.arange(N)) & (np.arange(N) <= hi))
+    np.testing.assert_array_equal(_classes_from_end_rows(lo, hi, N, block), m["cls"][0])
