@@ -93,8 +93,10 @@ def compare_with_definition(bits, signs, codes, scales, what):
 
 @pytest.mark.parametrize("rotate", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 1), (1, 1, 129), (1, 4, 1000)])
+@pytest.mark.parametrize("shape", [(1, 2, 300), (2, 3, 1), (1, 1, 129), (1, 4, 1000), (1, 5, 16647)])
 def test_codes_and_scales_against_the_definition(shape, d, rotate):
+    """(1, 5, 16647): 655 blocks, more than the grid's workgroups, so workgroups take
+    a second block, and a last block of 7 rows."""
     B, H, N = shape
     p = W.make_problem(B, H, N, d, n_outliers=4, outlier_gain=20.0, seed=(B, H, N, d))
     bits = p.q.copy()
