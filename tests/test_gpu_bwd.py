@@ -105,3 +105,15 @@ def test_full_size_sampled_heads():
     ref = oracle.attention_bwd_problem(p, dO, heads=heads)
     sel = lambda t, hs: np.stack([t[b, h] for b, h in hs])
     _check([sel(g, heads) for g in got], [sel(r, heads) for r in ref], "bwd B4 H16 N2048 causal")
+
+
+def test_full_size_causal_window_softcap_sampled_heads():
+    """B2 H32 N8192 d128 causal + window 1024 + softcap 50 (the default forward workload,
+    and the backward bench's second configuration): two whole heads, one per batch row."""
+    p = W.config_problem(3)
+    dO = W.make_dout(p, seed=3)
+    _announce("bwd full size causal+window+softcap")
+    got = _bwd(p, dO)
+    for b, h in ((0, 5), (1, 30)):
+        ref = oracle.attention_bwd_problem(p, dO, heads=[(b, h)])
+        _check([g[b, h] for g in got], [r[b, h] for r in ref], f"bwd B2 H32 N8192 cfg3 head ({b}, {h})")
