@@ -19,7 +19,7 @@ hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
                       uint32_t flags, int window, float softcap, const float* slopes, const void* map,
-                      hipStream_t stream);
+                      hipStream_t stream, bool compact_map = false);
 hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                               float scale, uint32_t flags, int window, float softcap, const float* slopes,
@@ -165,6 +165,8 @@ attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* 
   layout->idx = m.idx;
   layout->row_lo = m.row_lo;
   layout->row_hi = m.row_hi;
+  layout->col_lo = m.col_lo;
+  layout->col_hi = m.col_hi;
   layout->pairs = m.pairs;
   layout->status = m.status;
   layout->order = m.order;
@@ -469,6 +471,8 @@ attn_status attn_varlen_layout_of(int32_t total, attn_blockmap_layout* layout) {
   layout->idx = m.idx;
   layout->row_lo = m.row_lo;
   layout->row_hi = m.row_hi;
+  layout->col_lo = m.col_lo;
+  layout->col_hi = m.col_hi;
   layout->pairs = m.pairs;
   layout->status = m.status;
   layout->order = m.order;
@@ -528,6 +532,32 @@ attn_status attn_bwd_gqa_noalloc(const void* q, const void* k, const void* v, co
   const float* slopes = (mask && (flags & ATTN_ALIBI)) ? mask->alibi_slopes : nullptr;
   if (launch_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, scale, flags, window, cap, slopes,
                          positional(mask) ? blockmap : nullptr, (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, float* delta, int32_t H, int32_t H_kv,
+                            int32_t total, int32_t d, float scale, const attn_mask* mask, const void* workspace,
+                            size_t bytes, void* stream) {
+  size_t need = 0;
+  attn_status st = attn_varlen_workspace_bytes(total, mask, &need);
+  if (st != ATTN_OK) return st;
+  if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
+  const attn_mask m = varlen_mask(mask, workspace, total);
+  st = check_args_impl(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), 1, H, H_kv, total, d, scale,
+                       ATTN_BF16, &m, workspace, varlen_doc_offset(total), nullptr, 8.f, true);
+  if (st != ATTN_OK) return st;
+  if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  const int window = (m.flags & ATTN_WINDOW) ? m.window : 0;
+  const float cap = (m.flags & ATTN_SOFTCAP) ? m.softcap : 0.f;
+  const float* slopes = (m.flags & ATTN_ALIBI) ? m.alibi_slopes : nullptr;
+  if (launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, 1, H, H_kv, total, d, scale, m.flags, window, cap,
+                 slopes, workspace, (hipStream_t)stream, true) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

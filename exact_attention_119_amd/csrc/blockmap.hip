@@ -7,7 +7,8 @@
 // leaves each query row a single interval of visible keys [row_lo, row_hi], so
 // the map is built from those intervals, in one launch with one workgroup per
 // 128-row query block:
-//   its rows (one thread each): the interval, and a flag for any place where doc_id
+//   its rows (one thread each): the interval of keys the row sees and the interval of
+//          rows that see the row's position as a key, and a flag for any place where doc_id
 //          decreases (documents must be contiguous runs), giving the block's status
 //          word: 1 if doc_id decreases at one of its rows, or, for a packed batch, if
 //          its share of the sequence offsets is out of order (a batch row with any
@@ -149,14 +150,28 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
         lo = max(lo, q - (a.window - 1));
         if (!(a.flags & kCausal)) hi = min(hi, q + (a.window - 1));
       }
+      // the rows that see key q (position q as a key): the same predicates with the
+      // roles swapped
+      int clo = (a.flags & kCausal) ? q : 0, chi = N - 1;
+      if (a.flags & kWindow) {
+        if (!(a.flags & kCausal)) clo = max(0, q - (a.window - 1));
+        chi = min(chi, q + (a.window - 1));
+      }
       if (a.flags & kDocument) {
         if (q + 1 < N && s_doc[tid + 1] < s_doc[tid]) bad = 1;
-        lo = max(lo, run_first == 0 ? first0 : q0 + run_first);
-        hi = min(hi, run_last == nrows - 1 ? last1 : q0 + run_last);
+        const int ds = run_first == 0 ? first0 : q0 + run_first;
+        const int de = run_last == nrows - 1 ? last1 : q0 + run_last;
+        lo = max(lo, ds);
+        hi = min(hi, de);
+        clo = max(clo, ds);
+        chi = min(chi, de);
       }
       if (hi < lo) { lo = 0; hi = -1; }
+      if (chi < clo) { clo = 0; chi = -1; }
       ((int32_t*)(a.map + a.lay.row_lo))[(size_t)b * N + q] = lo;
       ((int32_t*)(a.map + a.lay.row_hi))[(size_t)b * N + q] = hi;
+      ((int32_t*)(a.map + a.lay.col_lo))[(size_t)b * N + q] = clo;
+      ((int32_t*)(a.map + a.lay.col_hi))[(size_t)b * N + q] = chi;
     }
     s_lo[tid] = lo;
     s_hi[tid] = hi;

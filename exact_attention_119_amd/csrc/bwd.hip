@@ -59,6 +59,7 @@ struct BwdArgs {
   int window;
   const unsigned char* map;  // block map (positional masks)
   MapLayout lay;
+  int compact;  // 1: the map is the compact form (a packed batch's workspace)
   int heavy;  // causal mask without documents: workgroups take the heaviest blocks first
 };
 
@@ -212,7 +213,7 @@ __device__ __forceinline__ float head_slope(const BwdArgs& a, int h) {
 __device__ bool map_invalid(const BwdArgs& a, int b) {
   const MapHeader* hd = (const MapHeader*)a.map;
   bool bad = hd->magic != kMapMagic || hd->B != a.B || hd->N != a.N || hd->flags != (a.flags & kPositional) ||
-             hd->window != ((a.flags & kWindow) ? a.window : 0) || hd->compact != 0;
+             hd->window != ((a.flags & kWindow) ? a.window : 0) || hd->compact != a.compact;
   int st = 0;
   if (a.flags & kDocument) {
     const int* s = (const int*)(a.map + a.lay.status) + (size_t)b * a.nqb;
@@ -294,17 +295,32 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
 
   int lo_q = 0, hi_q = qvalid ? N - 1 : -1;
   int nblk = nqb, npart = 0;
-  cint* flist = nullptr;
-  cint* plist = nullptr;
+  // The key blocks of this query block, from the map's row intervals of its first and
+  // last rows r0, r1 (every row sees [row_lo, row_hi], both ends non-decreasing, the row
+  // itself inside): non-empty are ua .. ub, FULL fa .. fb (inside [lo(r1), hi(r0)], 128
+  // rows and keys), PARTIAL the pl blocks left of the FULL range and those right of it;
+  // step order: the PARTIAL blocks ascending, then the FULL ones (the map's lists are not
+  // read).
+  int ua = 0, fa = 0, fb = -1, pl = 0;
   bool invalid = false;
   if constexpr (MASKED) {
     invalid = map_invalid(a, b);
-    cint* cnt = (cint*)(a.map + a.lay.counts) + ((size_t)b * nqb + qb) * 2;
-    const int nfull = min(max(cnt[0], 0), nqb);
-    npart = min(max(cnt[1], 0), nqb - nfull);
-    nblk = invalid ? 0 : nfull + npart;
-    flist = (cint*)(a.map + a.lay.idx) + ((size_t)b * nqb + qb) * 2 * nqb;
-    plist = flist + nqb;
+    {
+      typedef const __attribute__((address_space(4))) int cint4;
+      cint4* rlo = (cint4*)(a.map + a.lay.row_lo) + (size_t)b * N;
+      cint4* rhi = (cint4*)(a.map + a.lay.row_hi) + (size_t)b * N;
+      const int r0 = qb * 128, r1 = min(N, r0 + 128) - 1;
+      const int lo0 = rlo[r0], lo1 = rlo[r1], hi0 = rhi[r0], hi1 = rhi[r1];
+      ua = min(max(lo0 >> 7, 0), nqb - 1);
+      const int ub = hi1 < lo0 ? ua - 1 : min(hi1 >> 7, nqb - 1);
+      fa = max(ua, (lo1 + 127) >> 7);
+      fb = min(ub, ((hi0 + 1) >> 7) - 1);
+      if (r1 - r0 != 127 || fa > fb) { fa = ub + 1; fb = ub; }  // no FULL block
+      const int nfull = fb - fa + 1;
+      npart = max(ub - ua + 1 - nfull, 0);
+      pl = fa - ua;
+      nblk = invalid ? 0 : nfull + npart;
+    }
     if (qvalid) {
       lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
       hi_q = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
@@ -325,7 +341,8 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
     int kb = st_ >> 1;
     if constexpr (MASKED) {
       const int i = st_ >> 1;
-      kb = min(max(i < npart ? plist[i] : flist[i - npart], 0), nqb - 1);
+      kb = i < pl ? ua + i : (i < npart ? fb + 1 + (i - pl) : fa + (i - npart));
+      kb = min(max(kb, 0), nqb - 1);
     }
     return kb * 128 + (st_ & 1) * BN;
   };
@@ -477,53 +494,35 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     dkacc[db] = f32x16{};
     dvacc[db] = f32x16{};
   }
-  // class of query block qb against this key block: byte b nqb^2 + qb nqb + kb of the
-  // class section, read as its aligned dword with a scalar load (a byte load would be a
-  // vector memory load, and its wait would also wait for the tile loads in flight; the
-  // section is padded to 256 bytes, so the dword stays inside it)
-  cint* const clsw = MASKED ? (cint*)(a.map + a.lay.cls) : nullptr;
-  const size_t cls0 = (size_t)b * nqb * nqb + kb;
-  auto cls_of = [&](int qb) -> int {
-    const size_t i = cls0 + (size_t)qb * nqb;
-    return (clsw[i >> 2] >> (8 * (int)(i & 3))) & 0xFF;
-  };
   const ScoreConsts mc = score_consts(a);
-  // The non-empty query blocks of this key block as a bit mask in LDS (bit qb % 64 of word
-  // qb / 64), built once with one byte load per lane and a ballot per 64 blocks: finding
-  // the next non-empty block is then an LDS read and a bit scan, where reading the class
-  // bytes one by one cost a scalar-cache miss each (a window's key block scans every
-  // block past its window).  Up to kQMaskWords words (N <= 512K); beyond that the bytes are
-  // read one by one.
-  constexpr int kQMaskWords = 64;
-  __shared__ unsigned long long qmask_s[kQMaskWords];
-  const int nqw = (nqb + 63) / 64;
-  const bool use_qmask = MASKED && nqw <= kQMaskWords;
-  if (use_qmask) {
-    cu8* const cls = (cu8*)(a.map + a.lay.cls) + cls0;
-    for (int w = wave; w < nqw; w += 4) {
-      const int q = 64 * w + lane;
-      const bool ne = q < nqb && cls[(size_t)q * nqb] != 0;
-      const unsigned long long m = __ballot(ne);
-      if (lane == 0) qmask_s[w] = m;
-    }
-    __syncthreads();
+  // The query blocks this key block is visible from, from the map's column intervals: the
+  // rows that see key k are [col_lo(k), col_hi(k)], both ends non-decreasing in k and k
+  // itself inside (every mask here), so the rows that see some key of the block form the
+  // one range [col_lo(k0), col_hi(k1)] of its first and last keys k0, k1 -- non-empty
+  // query blocks qa .. qz -- and a query block is FULL (every row sees every key) when it
+  // lies in [col_lo(k1), col_hi(k0)] with 128 rows, and the key block has 128 keys.  (The
+  // same argument as the forward pass's, with rows and keys swapped; the map's class and
+  // list sections are not read.)
+  int qa = 0, qz = nqb - 1, qfa = 0, qfz = nqb - 1;
+  if constexpr (MASKED) {
+    typedef const __attribute__((address_space(4))) int cint4;
+    cint4* clo = (cint4*)(a.map + a.lay.col_lo) + (size_t)b * N;
+    cint4* chi = (cint4*)(a.map + a.lay.col_hi) + (size_t)b * N;
+    const int k0 = kb * 128, k1 = min(N, k0 + 128) - 1;
+    const int lo0 = clo[k0], lo1 = clo[k1], hi0 = chi[k0], hi1 = chi[k1];
+    qa = min(max(lo0 >> 7, 0), nqb);
+    qz = hi1 < lo0 ? -1 : min(hi1 >> 7, nqb - 1);
+    qfa = max(qa, (lo1 + 127) >> 7);
+    qfz = min(qz, ((hi0 + 1) >> 7) - 1);
+    if (k1 - k0 != 127) qfz = qfa - 1;  // a key block cut by N is never FULL
   }
+  // class of query block qb (in qa .. qz) against this key block: 2 FULL, 1 PARTIAL
+  auto cls_of = [&](int qb) -> int { return (qb >= qfa) & (qb <= qfz) ? 2 : 1; };
   // first non-empty query block at or after `from` (nqb if none)
   auto next_block = [&](int from) -> int {
     if constexpr (!MASKED) return from;
-    if (use_qmask) {
-      for (int w = from >> 6; w < nqw; ++w) {
-        unsigned long long m = qmask_s[w];
-        m = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(m >> 32)) << 32) |
-            (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)m);
-        if (w == (from >> 6)) m &= ~0ull << (from & 63);
-        if (m) return 64 * w + __builtin_ctzll(m);
-      }
-      return nqb;
-    }
-    int q = from;
-    while (q < nqb && cls_of(q) == 0) ++q;
-    return q;
+    const int q = max(from, qa);
+    return q <= qz ? q : nqb;
   };
   // Steps: (query head of the group, non-empty query block, 64-row sub-block), in that
   // nesting.  next() advances a step state.
@@ -873,7 +872,7 @@ hipError_t launch_d(const BwdArgs& a, bool masked, hipStream_t st) {
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
                       uint32_t flags, int window, float softcap, const float* slopes, const void* map,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool compact_map) {
   bwd::BwdArgs a;
   a.q = (const bf16*)q;
   a.k = (const bf16*)k;
@@ -898,7 +897,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.flags = flags;
   a.window = window;
   a.map = (const unsigned char*)map;
-  a.lay = map_layout(B, N);
+  a.lay = map_layout(B, N, compact_map);
+  a.compact = compact_map ? 1 : 0;
   a.heavy = (flags & kCausal) && !(flags & kDocument);
   const bool masked = (flags & kPositional) != 0;
   if (masked && !map) return hipErrorInvalidValue;
@@ -952,7 +952,7 @@ hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const
   const hipError_t e = bwd_scratch_ptr(&delta);
   if (e != hipSuccess) return e;
   return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, flags, window, softcap,
-                    slopes, map, stream);
+                    slopes, map, stream, false);
 }
 
 }  // namespace attn119

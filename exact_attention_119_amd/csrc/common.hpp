@@ -104,7 +104,7 @@ constexpr uint32_t kPositional = kCausal | kWindow | kDocument;
 // compact form (the workspace of a packed batch) has no class and list sections; their
 // offsets are 0 there, and every other section is O(N).
 struct MapLayout {
-  size_t cls, counts, idx, row_lo, row_hi, pairs, status, order, total;
+  size_t cls, counts, idx, row_lo, row_hi, col_lo, col_hi, pairs, status, order, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -122,6 +122,10 @@ __host__ __device__ inline MapLayout map_layout(int B, int N, bool compact = fal
   m.row_lo = off;
   off = align256(off + (size_t)B * N * 4);
   m.row_hi = off;
+  off = align256(off + (size_t)B * N * 4);
+  m.col_lo = off;
+  off = align256(off + (size_t)B * N * 4);
+  m.col_hi = off;
   off = align256(off + (size_t)B * N * 4);
   m.pairs = off;
   off = align256(off + (size_t)B * nb * 8);

@@ -44,7 +44,7 @@ EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_buil
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
            "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa", "attn_bwd_gqa_noalloc",
-           "attn_fwd_rescale_counts", "attn_varlen_layout_of")
+           "attn_fwd_rescale_counts", "attn_varlen_layout_of", "attn_bwd_varlen")
 
 
 class AttnError(RuntimeError):
@@ -64,8 +64,8 @@ class attn_fp8(ctypes.Structure):
 
 
 class attn_blockmap_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status", "order",
-                                               "total")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("cls", "counts", "idx", "row_lo", "row_hi", "col_lo", "col_hi", "pairs",
+                                               "status", "order", "total")]
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -125,6 +125,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, ctypes.POINTER(attn_mask),
                              vp, sz, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                    ctypes.POINTER(attn_mask), vp, sz, vp]
+    lib.attn_bwd_varlen.restype = i32
     lib.attn_fwd_kernel_name.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(attn_fp8)]
     lib.attn_fwd_kernel_name.restype = ctypes.c_char_p
     _LIB = lib
@@ -291,6 +294,19 @@ def attn_fwd_varlen(q, k, v, o, lse, *, scale: float, workspace, dtype: int = AT
            "attn_fwd_varlen")
 
 
+def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, delta, *, scale: float, workspace,
+                    mask: Optional[attn_mask] = None, stream=None) -> None:
+    """Packed variable-length backward pass (bf16).  q, o, dout, dq: [H][total][d]; k, v, dk,
+    dv: [H_kv][total][d]; lse, delta: [H][total]; workspace prepared by attn_varlen_prepare."""
+    H, total, d = (int(x) for x in q.shape[-3:])
+    H_kv = int(k.shape[-3])
+    _check(load().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(delta), H, H_kv, total, d, float(scale),
+                                  ctypes.byref(mask) if mask else None, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "attn_bwd_varlen")
+
+
 def attn_fp8_quantize(x, codes, scales, rotate_signs=None, stream=None) -> None:
     """Block-quantise bf16 x [B][H][N][d] to e4m3 codes (uint8, same shape) and fp32 scales
     [B][H][ceil(N/128)] on the device; rotate_signs: d/32 sign words (host) or None."""
@@ -354,5 +370,6 @@ def read_blockmap(blockmap, B: int, N: int, compact: bool = False) -> dict:
                             order_full_cost=int(hdr[7]), order_partial_cost=int(hdr[8]), compact=int(hdr[9])),
                 cls=sec("cls", np.uint8, (B, nb, nb)), counts=sec("counts", np.int32, (B, nb, 2)),
                 idx=sec("idx", np.int32, (B, nb, 2, nb)), row_lo=sec("row_lo", np.int32, (B, N)),
-                row_hi=sec("row_hi", np.int32, (B, N)), pairs=sec("pairs", np.int64, (B, nb)),
+                row_hi=sec("row_hi", np.int32, (B, N)), col_lo=sec("col_lo", np.int32, (B, N)),
+                col_hi=sec("col_hi", np.int32, (B, N)), pairs=sec("pairs", np.int64, (B, nb)),
                 status=sec("status", np.int32, (B, nb)), order=sec("order", np.int32, (B * nb,)))

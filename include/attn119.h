@@ -145,6 +145,8 @@ typedef struct attn_fp8 {
  *   idx      : int32  [B][nqb][2][nkb]  ascending FULL kb, then -1; ascending PARTIAL kb, then -1
  *   row_lo   : int32  [B][N]            smallest visible key of each query
  *   row_hi   : int32  [B][N]            largest visible key of each query
+ *   col_lo   : int32  [B][N]            smallest query that sees each key
+ *   col_hi   : int32  [B][N]            largest query that sees each key
  *   pairs    : int64  [B][nqb]          visible (q, k) pairs of each query block
  *   status   : int32  [B][nqb]          1 if doc_id[b] decreases from a row of this block to
  *                                       the next row (packed batches: or the share of the
@@ -161,10 +163,11 @@ typedef struct attn_fp8 {
  * The compact form, inside the workspace of a packed batch (attn_varlen_prepare), has
  * B = 1, header.compact = 1 and the sections above without cls and idx, so that it
  * grows as O(N) rather than O(N^2 / 128^2) (attn_varlen_layout_of gives its offsets,
- * with cls = idx = 0).  Only the forward pass reads it: every query row's visible keys
- * form one interval [row_lo, row_hi] whose ends never decrease from row to row, so a
- * query block's non-empty and FULL key blocks follow from the intervals of its first
- * and last rows, and the class and list sections are not needed.
+ * with cls = idx = 0).  No kernel needs those two sections: every query row's visible
+ * keys form one interval [row_lo, row_hi] whose ends never decrease from row to row (and
+ * likewise every key's rows [col_lo, col_hi]), so a query block's non-empty and FULL key
+ * blocks follow from the intervals of its first and last rows, and a key block's query
+ * blocks from those of its first and last keys.
  */
 typedef struct attn_blockmap_header {
   uint32_t magic; /* 0x39313141 */
@@ -178,7 +181,7 @@ typedef struct attn_blockmap_header {
 } attn_blockmap_header;
 
 typedef struct attn_blockmap_layout {
-  size_t cls, counts, idx, row_lo, row_hi, pairs, status, order, total;
+  size_t cls, counts, idx, row_lo, row_hi, col_lo, col_hi, pairs, status, order, total;
 } attn_blockmap_layout;
 
 /* Size in bytes of the block-map workspace for (B, N, mask).  Host only. */
@@ -370,6 +373,22 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv, float* delta, int32_t B, int32_t H, int32_t N, int32_t d,
                      float scale, const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
                      void* stream);
+
+/*
+ * The backward pass of a packed variable-length batch (the gradients of attn_fwd_varlen,
+ * bf16 inputs): every sequence attends only to itself, so it is attn_bwd_gqa with B = 1,
+ * N = total and the sequences as documents, walking the workspace's compact block map
+ * (prepared by attn_varlen_prepare for the same offsets and mask; the backward kernels
+ * take every block range from the map's row and column intervals, so the workspace stays
+ * O(total)).
+ *   q, o, dout, dq : bf16 [H][total][d];  k, v, dk, dv : bf16 [H_kv][total][d];
+ *   lse, delta     : fp32 [H][total] (lse from attn_fwd_varlen, delta overwritten with D).
+ * Errors as attn_bwd_gqa; a workspace of the wrong size is ATTN_ERR_BAD_BLOCKMAP.
+ */
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, float* delta, int32_t H, int32_t H_kv,
+                            int32_t total, int32_t d, float scale, const attn_mask* mask, const void* workspace,
+                            size_t bytes, void* stream);
 
 /*
  * The backward pass of attn_bwd_gqa without the delta workspace, for callers that cannot

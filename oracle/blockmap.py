@@ -14,6 +14,8 @@ visibility predicate, evaluated for every (query, key) position:
   idx[b][qb][1][:] = PARTIAL kb in ascending order, then -1 padding
   row_lo[b][q], row_hi[b][q] = smallest and largest visible key of query q
       (0 and -1 for a row with no visible key)
+  col_lo[b][k], col_hi[b][k] = smallest and largest query that sees key k
+      (0 and -1 for a key no query sees)
   qb_pairs[b][qb] = visible (q, k) pairs of the query rows of block qb
   status[b][qb] = 1 if doc_id[b][q + 1] < doc_id[b][q] for some row q of block qb
       (documents must be contiguous runs; only evaluated with the DOCUMENT flag)
@@ -46,6 +48,8 @@ def blockmap_ref(B: int, N: int, flags: int, window: int = 0, doc_id: Optional[n
     idx = np.full((B, nqb, 2, nqb), -1, dtype=np.int32)
     row_lo = np.zeros((B, N), dtype=np.int32)
     row_hi = np.full((B, N), -1, dtype=np.int32)
+    col_lo = np.zeros((B, N), dtype=np.int32)
+    col_hi = np.full((B, N), -1, dtype=np.int32)
     pairs = np.zeros(B, dtype=np.int64)
     qb_pairs = np.zeros((B, nqb), dtype=np.int64)
     status = np.zeros((B, nqb), dtype=np.int32)
@@ -64,6 +68,12 @@ def blockmap_ref(B: int, N: int, flags: int, window: int = 0, doc_id: Optional[n
             r = np.nonzero(anyv)[0]
             row_lo[b, q0 + r] = vis[r].argmax(axis=1)
             row_hi[b, q0 + r] = N - 1 - vis[r, ::-1].argmax(axis=1)
+            # blocks go by increasing query: a key's first seeing block gives col_lo, its
+            # last one col_hi
+            seen = vis.any(axis=0)
+            first = seen & (col_hi[b] < 0)
+            col_lo[b, first] = q0 + vis[:, first].argmax(axis=0)
+            col_hi[b, seen] = q1 - 1 - vis[::-1, seen].argmax(axis=0)
             for kb in range(nqb):
                 k0, k1 = kb * block, min(N, (kb + 1) * block)
                 sub = vis[:, k0:k1]
@@ -79,7 +89,8 @@ def blockmap_ref(B: int, N: int, flags: int, window: int = 0, doc_id: Optional[n
             counts[b, qb] = (len(full), len(part))
             idx[b, qb, 0, :len(full)] = full
             idx[b, qb, 1, :len(part)] = part
-    return dict(cls=cls, counts=counts, idx=idx, row_lo=row_lo, row_hi=row_hi, pairs=pairs,
+    return dict(cls=cls, counts=counts, idx=idx, row_lo=row_lo, row_hi=row_hi, col_lo=col_lo, col_hi=col_hi,
+                pairs=pairs,
                 qb_pairs=qb_pairs, status=status, visible_pairs=int(pairs.sum()))
 
 

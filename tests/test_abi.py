@@ -44,7 +44,7 @@ def test_blockmap_layout(L):
     lay = L.attn_blockmap_layout_of(2, 300)
     nb = 3
     assert lay["cls"] == 256
-    order = ["cls", "counts", "idx", "row_lo", "row_hi", "pairs", "status", "order", "total"]
+    order = ["cls", "counts", "idx", "row_lo", "row_hi", "col_lo", "col_hi", "pairs", "status", "order", "total"]
     for a, b in zip(order, order[1:]):
         assert lay[a] < lay[b] and lay[b] % 256 == 0
     assert lay["counts"] - lay["cls"] >= 2 * nb * nb
@@ -145,13 +145,13 @@ def test_varlen_validation(L):
         nb = (total + 127) // 128
         full = L.attn_blockmap_layout_of(1, total)
         assert lay["cls"] == 0 and lay["idx"] == 0 and lay["counts"] == 256
-        names = ["counts", "row_lo", "row_hi", "pairs", "status", "order", "total"]
+        names = ["counts", "row_lo", "row_hi", "col_lo", "col_hi", "pairs", "status", "order", "total"]
         for a, b in zip(names, names[1:]):
             assert lay[a] < lay[b] and lay[b] % 256 == 0
             if a != "counts":  # the same sections as the full map's, without cls and idx
                 assert lay[b] - lay[a] == full[b] - full[a]
         assert lay["row_lo"] - lay["counts"] >= 8 * nb
-        assert lay["total"] <= 256 * 7 + 8 * total + 24 * nb  # O(total)
+        assert lay["total"] <= 256 * 9 + 16 * total + 24 * nb  # O(total)
         assert L.attn_varlen_workspace_bytes(total, m) == lay["total"] + ((4 * total + 255) // 256) * 256
         assert L.attn_varlen_workspace_bytes(total, None) == L.attn_varlen_workspace_bytes(total, m)
     with pytest.raises(L.AttnError):

@@ -117,3 +117,42 @@ def test_full_size_causal_window_softcap_sampled_heads():
     for b, h in ((0, 5), (1, 30)):
         ref = oracle.attention_bwd_problem(p, dO, heads=[(b, h)])
         _check([g[b, h] for g in got], [r[b, h] for r in ref], f"bwd B2 H32 N8192 cfg3 head ({b}, {h})")
+
+
+VARLEN_MIXES = {"ragged": [0, 5, 129, 0, 1, 200, 64, 3], "mixed": [37, 300, 128, 1, 211, 90]}
+
+
+@pytest.mark.parametrize("variant", ["plain", "causal", "cfg3like", "alibi_causal", "bidir_window"])
+@pytest.mark.parametrize("mix", list(VARLEN_MIXES))
+def test_varlen_against_oracle_and_document_mask(mix, variant):
+    """attn_bwd_varlen on a packed batch (the compact workspace of attn_varlen_prepare)
+    against the oracle's gradients of the document-masked pass over the sequence ids, and
+    bit for bit against attn_bwd_gqa with that document mask and the full block map."""
+    lengths = VARLEN_MIXES[mix]
+    kw = VARIANTS[variant]
+    p = W.make_varlen_problem(lengths, 4, 128, seed=(21, sorted(VARIANTS).index(variant)), H_kv=2, **kw)
+    dO = W.make_dout(p, seed=21)
+    _announce("bwd varlen", mix, variant, p.N)
+    dp = WD.to_device(p)
+    WD.step(dp)
+    dout = torch.from_numpy(dO.view(np.int16)).cuda().view(torch.bfloat16)
+    outs = [torch.full_like(t, float("nan")) for t in (dp.q, dp.k, dp.v)] + [torch.empty_like(dp.lse)]
+    L.attn_bwd_varlen(dp.q[0], dp.k[0], dp.v[0], dp.o[0], dp.lse[0], dout[0], *(t[0] for t in outs),
+                      scale=p.scale, workspace=dp.blockmap, mask=dp.mask)
+    doc = torch.from_numpy(W.doc_ids_from_lengths(lengths)[None].copy()).cuda()
+    m = L.make_mask(kw["flags"] | DOC, kw.get("window", 0), kw.get("softcap", 0.0), doc)
+    mp = torch.empty(L.attn_blockmap_bytes(1, p.N, m), dtype=torch.uint8, device="cuda")
+    L.attn_blockmap_build(1, p.N, m, mp)
+    outs2 = [torch.full_like(t, float("nan")) for t in (dp.q, dp.k, dp.v)] + [torch.empty_like(dp.lse)]
+    L.attn_bwd_gqa(dp.q, dp.k, dp.v, dp.o, dp.lse, dout, *outs2, scale=p.scale, mask=m, blockmap=mp)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    got = [f(t) for t in outs]
+    for a_, b_ in zip(outs, outs2):
+        assert torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_.view(torch.int32),
+                           b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_.view(torch.int32))
+    ids = oracle.varlen_doc_ids_ref(p.cu_seqlens, p.N)
+    Q, K, V = (oracle.decode_bf16(x) for x in (p.q, p.k, p.v))
+    ref = oracle.attention_bwd_ref(Q, K, V, oracle.decode_bf16(dO), scale=p.scale, flags=p.flags | DOC,
+                                   window=p.window, softcap=p.softcap, doc_id=ids[None], alibi_slopes=p.alibi_slopes)
+    _check(got, ref, f"bwd varlen {mix} {variant}")

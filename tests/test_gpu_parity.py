@@ -61,7 +61,7 @@ def _check_map(dp, rows=None):
     # counts are unspecified) by the cost the map states
     check_work_order(got["order"], got["counts"], hd, bool(p.flags & L.ATTN_DOCUMENT))
     sel = slice(None) if rows is None else rows
-    for key in ("cls", "counts", "idx", "row_lo", "row_hi"):
+    for key in ("cls", "counts", "idx", "row_lo", "row_hi", "col_lo", "col_hi"):
         np.testing.assert_array_equal(got[key][sel], ref[key][sel], err_msg=key)
     np.testing.assert_array_equal(got["pairs"][sel], ref["qb_pairs"][sel])
     return ref

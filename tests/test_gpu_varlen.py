@@ -96,7 +96,7 @@ def _check_prepared(dp):
     hd = got["header"]
     assert (hd["B"], hd["N"], hd["flags"], hd["compact"]) == (1, p.N, flags, 1)
     np.testing.assert_array_equal(got["status"], ref["status"])
-    for key in ("counts", "row_lo", "row_hi"):
+    for key in ("counts", "row_lo", "row_hi", "col_lo", "col_hi"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
     np.testing.assert_array_equal(_classes_from_intervals(got["row_lo"][0], got["row_hi"][0], p.N), ref["cls"][0])
     check_work_order(got["order"], got["counts"], got["header"], True)
@@ -181,9 +181,10 @@ def test_varlen_full_size_sampled():
 
 def test_varlen_million_tokens_compact_workspace():
     """1,048,576 packed tokens in causal sequences of 512 .. 8192 (H1 d64): the workspace
-    is the compact map plus the ids, under 16 bytes per token (the map with classes and
-    lists would take 0.62 GB); its row intervals on sampled rows and its FULL/PARTIAL
-    counts on sampled query blocks equal the oracle's, and so do O and LSE on sampled rows."""
+    is the compact map plus the ids, under 24 bytes per token (the map with classes and
+    lists would take 0.62 GB); its row and column intervals on sampled positions and its
+    FULL/PARTIAL counts on sampled query blocks equal the oracle's, and so do O and LSE on
+    sampled rows."""
     rng = np.random.default_rng([119, 79])
     lengths = W.draw_doc_lengths(rng, 1 << 20, 512, 8192)
     p = W.make_varlen_problem(lengths, 1, 64, flags=C, seed=79)
@@ -191,7 +192,7 @@ def test_varlen_million_tokens_compact_workspace():
     dp, o, lse = _run(p)
     N = p.N
     lay = L.attn_varlen_layout_of(N)
-    assert dp.blockmap.numel() == L.attn_varlen_workspace_bytes(N, dp.mask) < 16 * N
+    assert dp.blockmap.numel() == L.attn_varlen_workspace_bytes(N, dp.mask) < 24 * N
     assert L.attn_blockmap_status(dp.blockmap) == L.ATTN_OK
     got = L.read_blockmap(dp.blockmap[:lay["total"]], 1, N, compact=True)
     ids = oracle.varlen_doc_ids_ref(p.cu_seqlens, N)
@@ -201,6 +202,9 @@ def test_varlen_million_tokens_compact_workspace():
     vis = oracle.visible(rows, kpos, flags, 0, ids)
     np.testing.assert_array_equal(got["row_lo"][0][rows], vis.argmax(axis=1))
     np.testing.assert_array_equal(got["row_hi"][0][rows], N - 1 - vis[:, ::-1].argmax(axis=1))
+    visk = oracle.visible(kpos, rows, flags, 0, ids)  # [every query][sampled keys]
+    np.testing.assert_array_equal(got["col_lo"][0][rows], visk.argmax(axis=0))
+    np.testing.assert_array_equal(got["col_hi"][0][rows], N - 1 - visk[::-1].argmax(axis=0))
     nb = N // 128
     for qb in sorted({0, 1, nb - 1, *np.random.default_rng(79).choice(nb, 3, replace=False).tolist()}):
         blk = oracle.visible(np.arange(128 * qb, 128 * qb + 128), kpos, flags, 0, ids).reshape(128, nb, 128)

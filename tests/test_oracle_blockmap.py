@@ -116,6 +116,41 @@ def test_row_intervals_closed_forms():
     assert not contiguous
 
 
+def test_column_intervals_closed_forms_and_brute_force():
+    """col_lo/col_hi: the first and last query that sees each key, in closed form for the
+    flag masks and documents, and against a scalar scan of the predicate on small cases
+    (with block sizes that cut the sequence and documents across blocks)."""
+    N, W = 500, 64
+    k = np.arange(N)
+    m = O.blockmap_ref(1, N, CAUSAL)
+    assert np.array_equal(m["col_lo"][0], k) and np.array_equal(m["col_hi"][0], np.full(N, N - 1))
+    m = O.blockmap_ref(1, N, CAUSAL | WINDOW, W)
+    assert np.array_equal(m["col_lo"][0], k) and np.array_equal(m["col_hi"][0], np.minimum(N - 1, k + W - 1))
+    m = O.blockmap_ref(1, N, WINDOW, W)
+    assert np.array_equal(m["col_lo"][0], np.maximum(0, k - W + 1))
+    assert np.array_equal(m["col_hi"][0], np.minimum(N - 1, k + W - 1))
+    lengths = [100, 250, 150]
+    starts = np.repeat(np.cumsum([0] + lengths[:-1]), lengths)
+    ends = np.repeat(np.cumsum(lengths) - 1, lengths)
+    doc = np.repeat(np.arange(3), lengths).astype(np.int32)[None]
+    m = O.blockmap_ref(1, N, DOCUMENT | CAUSAL, 0, doc)
+    assert np.array_equal(m["col_lo"][0], k) and np.array_equal(m["col_hi"][0], ends)
+    m = O.blockmap_ref(1, N, DOCUMENT, 0, doc)
+    assert np.array_equal(m["col_lo"][0], starts) and np.array_equal(m["col_hi"][0], ends)
+    rng = np.random.default_rng([119, 58])
+    for _ in range(8):
+        n = int(rng.integers(1, 40))
+        flags = int(rng.choice([CAUSAL, WINDOW, DOCUMENT, CAUSAL | WINDOW, CAUSAL | WINDOW | DOCUMENT]))
+        w = int(rng.integers(1, 9))
+        dd = np.repeat(np.arange(n), rng.integers(1, 8, n))[:n].astype(np.int32)
+        m = O.blockmap_ref(1, n, flags, w, dd[None], block=4)
+        for key in range(n):
+            rows = [q for q in range(n)
+                    if (not flags & CAUSAL or key <= q) and (not flags & WINDOW or abs(q - key) < w)
+                    and (not flags & DOCUMENT or dd[q] == dd[key])]
+            assert (m["col_lo"][0, key], m["col_hi"][0, key]) == (min(rows), max(rows)), (flags, w, key)
+
+
 def test_qb_pairs_and_doc_status():
     doc = np.array([[0] * 100 + [1] * 200 + [2] * 20, [0] * 130 + [2] * 10 + [1] * 180]).astype(np.int32)
     m = O.blockmap_ref(2, 320, CAUSAL | DOCUMENT, 0, doc)
