@@ -19,11 +19,11 @@ hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
                       uint32_t flags, int window, float softcap, const float* slopes, const void* map,
-                      hipStream_t stream, bool compact_map = false);
+                      hipStream_t stream, bool compact_map);
 hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                               float scale, uint32_t flags, int window, float softcap, const float* slopes,
-                              const void* map, hipStream_t stream);
+                              const void* map, hipStream_t stream, bool compact_map);
 size_t bwd_scratch_rows();
 hipError_t launch_quant(const void* x, void* codes, float* scales, int BH, int N, int d, const uint32_t* signs,
                         hipStream_t stream);
@@ -117,6 +117,57 @@ attn_status check_shape(int32_t B, int32_t N) {
   return ATTN_OK;
 }
 
+// Offsets of the block map of (B, N): the general form or the compact one (no class and
+// list sections).
+attn_status layout_of(int32_t B, int32_t N, bool compact, attn_blockmap_layout* layout) {
+  if (!layout) return ATTN_ERR_INVALID_ARG;
+  const attn_status st = check_shape(B, N);
+  if (st != ATTN_OK) return st;
+  const MapLayout m = map_layout(B, N, compact);
+  layout->cls = m.cls;
+  layout->counts = m.counts;
+  layout->idx = m.idx;
+  layout->row_lo = m.row_lo;
+  layout->row_hi = m.row_hi;
+  layout->col_lo = m.col_lo;
+  layout->col_hi = m.col_hi;
+  layout->pairs = m.pairs;
+  layout->status = m.status;
+  layout->order = m.order;
+  layout->total = m.total;
+  return ATTN_OK;
+}
+
+attn_status map_bytes(int32_t B, int32_t N, const attn_mask* mask, bool compact, size_t* bytes) {
+  if (!bytes) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_shape(B, N);
+  if (st != ATTN_OK) return st;
+  st = check_mask(mask);
+  if (st != ATTN_OK) return st;
+  *bytes = map_layout(B, N, compact).total;
+  return ATTN_OK;
+}
+
+attn_status build_map(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes, bool compact,
+                      void* stream) {
+  size_t need = 0;
+  attn_status st = map_bytes(B, N, mask, compact, &need);
+  if (st != ATTN_OK) return st;
+  if (!map || !aligned16(map)) return ATTN_ERR_INVALID_ARG;
+  if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
+  const uint32_t flags = mask ? mask->flags : 0u;
+  const int window = (mask && (flags & ATTN_WINDOW)) ? mask->window : 0;
+  const int32_t* doc = (mask && (flags & ATTN_DOCUMENT)) ? mask->doc_id : nullptr;
+  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, compact, (hipStream_t)stream) !=
+      hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+// The form of a block map of (B, N) passed with `bytes` bytes: the compact one when the
+// size is the compact layout's (the general layout is always larger).
+bool compact_form(int32_t B, int32_t N, size_t bytes) { return bytes == map_layout(B, N, true).total; }
+
 // Variable-length workspace: the compact block map of (B = 1, N = total), then the doc ids.
 size_t varlen_doc_offset(int32_t total) { return map_layout(1, total, true).total; }
 size_t varlen_bytes(int32_t total) { return varlen_doc_offset(total) + align256((size_t)total * 4); }
@@ -156,61 +207,40 @@ const char* attn_status_str(int32_t s) {
 }
 
 attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* layout) {
-  if (!layout) return ATTN_ERR_INVALID_ARG;
-  const attn_status st = check_shape(B, N);
-  if (st != ATTN_OK) return st;
-  const MapLayout m = map_layout(B, N);
-  layout->cls = m.cls;
-  layout->counts = m.counts;
-  layout->idx = m.idx;
-  layout->row_lo = m.row_lo;
-  layout->row_hi = m.row_hi;
-  layout->col_lo = m.col_lo;
-  layout->col_hi = m.col_hi;
-  layout->pairs = m.pairs;
-  layout->status = m.status;
-  layout->order = m.order;
-  layout->total = m.total;
-  return ATTN_OK;
+  return layout_of(B, N, false, layout);
+}
+
+attn_status attn_blockmap_compact_layout_of(int32_t B, int32_t N, attn_blockmap_layout* layout) {
+  return layout_of(B, N, true, layout);
 }
 
 attn_status attn_blockmap_bytes(int32_t B, int32_t N, const attn_mask* mask, size_t* bytes) {
-  if (!bytes) return ATTN_ERR_INVALID_ARG;
-  attn_status st = check_shape(B, N);
-  if (st != ATTN_OK) return st;
-  st = check_mask(mask);
-  if (st != ATTN_OK) return st;
-  *bytes = map_layout(B, N).total;
-  return ATTN_OK;
+  return map_bytes(B, N, mask, false, bytes);
+}
+
+attn_status attn_blockmap_compact_bytes(int32_t B, int32_t N, const attn_mask* mask, size_t* bytes) {
+  return map_bytes(B, N, mask, true, bytes);
 }
 
 attn_status attn_blockmap_build(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes,
                                 void* stream) {
-  size_t need = 0;
-  attn_status st = attn_blockmap_bytes(B, N, mask, &need);
-  if (st != ATTN_OK) return st;
-  if (!map || !aligned16(map)) return ATTN_ERR_INVALID_ARG;
-  if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
-  const uint32_t flags = mask ? mask->flags : 0u;
-  const int window = (mask && (flags & ATTN_WINDOW)) ? mask->window : 0;
-  const int32_t* doc = (mask && (flags & ATTN_DOCUMENT)) ? mask->doc_id : nullptr;
-  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, false, (hipStream_t)stream) !=
-      hipSuccess)
-    return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return build_map(B, N, mask, map, bytes, false, stream);
 }
 
+attn_status attn_blockmap_build_compact(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes,
+                                        void* stream) {
+  return build_map(B, N, mask, map, bytes, true, stream);
+}
 attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
   if (!map || bytes < 256) return ATTN_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
   MapHeader hd;
   if (hipMemcpy(&hd, map, sizeof(hd), hipMemcpyDeviceToHost) != hipSuccess) return ATTN_ERR_HIP;
   if (hd.magic != kMapMagic || check_shape(hd.B, hd.N) != ATTN_OK) return ATTN_ERR_BAD_BLOCKMAP;
-  if (hd.compact != 0 && (hd.compact != 1 || hd.B != 1)) return ATTN_ERR_BAD_BLOCKMAP;
+  if (hd.compact != 0 && hd.compact != 1) return ATTN_ERR_BAD_BLOCKMAP;
   const MapLayout m = map_layout(hd.B, hd.N, hd.compact != 0);
-  // a compact map comes inside a packed batch's workspace: the map alone or the whole
-  // workspace
-  if (bytes != m.total && !(hd.compact && bytes == varlen_bytes(hd.N))) return ATTN_ERR_BAD_BLOCKMAP;
+  // a packed batch's compact map may come with the rest of its workspace
+  if (bytes != m.total && !(hd.compact && hd.B == 1 && bytes == varlen_bytes(hd.N))) return ATTN_ERR_BAD_BLOCKMAP;
   const size_t n = (size_t)hd.B * hd.nqb;
   int32_t* st = new int32_t[n];
   const hipError_t e = hipMemcpy(st, (const unsigned char*)map + m.status, n * 4, hipMemcpyDeviceToHost);
@@ -221,16 +251,10 @@ attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
   return bad ? ATTN_ERR_BAD_DOC_ID : ATTN_OK;
 }
 
-}  // extern "C"
-
-namespace {
-
-// attn_check_args_gqa; compact_map: the map is the compact form of a packed batch's
-// workspace
-attn_status check_args_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
-                            int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
-                            const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
-                            bool compact_map) {
+attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                                int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
+                                const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
+                                const attn_fp8* fp8, float rescale_tau) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARG;
@@ -264,22 +288,12 @@ attn_status check_args_impl(const void* q, const void* k, const void* v, void* o
     const bool need = (mask->flags & ATTN_DOCUMENT) != 0;
     if (blockmap || need) {
       if (!blockmap || !aligned16(blockmap)) return ATTN_ERR_BAD_BLOCKMAP;
-      if (blockmap_bytes != map_layout(B, N, compact_map).total) return ATTN_ERR_BAD_BLOCKMAP;
+      // either form of the map (told apart by its size)
+      if (blockmap_bytes != map_layout(B, N).total && !compact_form(B, N, blockmap_bytes))
+        return ATTN_ERR_BAD_BLOCKMAP;
     }
   }
   return ATTN_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-attn_status attn_check_args_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                                int32_t H, int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype,
-                                const attn_mask* mask, const void* blockmap, size_t blockmap_bytes,
-                                const attn_fp8* fp8, float rescale_tau) {
-  return check_args_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap, blockmap_bytes, fp8,
-                         rescale_tau, false);
 }
 
 attn_status attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
@@ -307,9 +321,9 @@ namespace {
 attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t H,
                      int32_t H_kv, int32_t N, int32_t d, float scale, int32_t dtype, const attn_mask* mask,
                      const void* blockmap, size_t blockmap_bytes, const attn_fp8* fp8, float rescale_tau,
-                     int32_t* counts, void* stream, bool compact_map = false) {
-  const attn_status st = check_args_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap,
-                                         blockmap_bytes, fp8, rescale_tau, compact_map);
+                     int32_t* counts, void* stream) {
+  const attn_status st = attn_check_args_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, dtype, mask, blockmap,
+                                             blockmap_bytes, fp8, rescale_tau);
   if (st != ATTN_OK) return st;
   const uint32_t flags = mask ? mask->flags : 0u;
   const bool masked = positional(mask);
@@ -344,6 +358,7 @@ attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float
   }
   if (masked) {
     a.map = (const unsigned char*)blockmap;
+    const bool compact_map = compact_form(B, N, blockmap_bytes);
     a.lay = map_layout(B, N, compact_map);
     a.compact = compact_map ? 1 : 0;
     a.mflags = flags & (ATTN_CAUSAL | ATTN_WINDOW | ATTN_DOCUMENT);
@@ -458,7 +473,7 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
   const attn_mask m = varlen_mask(mask, workspace, total);
   return fwd_impl(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace, varlen_doc_offset(total), fp8,
-                  rescale_tau, nullptr, stream, true);
+                  rescale_tau, nullptr, stream);
 }
 
 attn_status attn_varlen_layout_of(int32_t total, attn_blockmap_layout* layout) {
@@ -510,7 +525,8 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
   const float cap = (flags & ATTN_SOFTCAP) ? mask->softcap : 0.f;
   const float* slopes = (mask && (flags & ATTN_ALIBI)) ? mask->alibi_slopes : nullptr;
   if (launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, scale, flags, window, cap, slopes,
-                 positional(mask) ? blockmap : nullptr, (hipStream_t)stream) != hipSuccess)
+                 positional(mask) ? blockmap : nullptr, (hipStream_t)stream,
+                 positional(mask) && compact_form(B, N, blockmap_bytes)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -531,7 +547,8 @@ attn_status attn_bwd_gqa_noalloc(const void* q, const void* k, const void* v, co
   const float cap = (flags & ATTN_SOFTCAP) ? mask->softcap : 0.f;
   const float* slopes = (mask && (flags & ATTN_ALIBI)) ? mask->alibi_slopes : nullptr;
   if (launch_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, scale, flags, window, cap, slopes,
-                         positional(mask) ? blockmap : nullptr, (hipStream_t)stream) != hipSuccess)
+                         positional(mask) ? blockmap : nullptr, (hipStream_t)stream,
+                         positional(mask) && compact_form(B, N, blockmap_bytes)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -546,20 +563,8 @@ attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const v
   if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
   if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
   const attn_mask m = varlen_mask(mask, workspace, total);
-  st = check_args_impl(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), 1, H, H_kv, total, d, scale,
-                       ATTN_BF16, &m, workspace, varlen_doc_offset(total), nullptr, 8.f, true);
-  if (st != ATTN_OK) return st;
-  if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_INVALID_ARG;
-  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      (reinterpret_cast<uintptr_t>(delta) & 3u))
-    return ATTN_ERR_INVALID_ARG;
-  const int window = (m.flags & ATTN_WINDOW) ? m.window : 0;
-  const float cap = (m.flags & ATTN_SOFTCAP) ? m.softcap : 0.f;
-  const float* slopes = (m.flags & ATTN_ALIBI) ? m.alibi_slopes : nullptr;
-  if (launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, 1, H, H_kv, total, d, scale, m.flags, window, cap,
-                 slopes, workspace, (hipStream_t)stream, true) != hipSuccess)
-    return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, 1, H, H_kv, total, d, scale, &m, workspace,
+                      varlen_doc_offset(total), stream);
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

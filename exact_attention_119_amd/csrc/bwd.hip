@@ -946,13 +946,13 @@ hipError_t bwd_scratch_ptr(float** out) {
 hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                               float scale, uint32_t flags, int window, float softcap, const float* slopes,
-                              const void* map, hipStream_t stream) {
+                              const void* map, hipStream_t stream, bool compact_map) {
   if ((size_t)B * H * N > kScratchRows) return hipErrorInvalidValue;
   float* delta = nullptr;
   const hipError_t e = bwd_scratch_ptr(&delta);
   if (e != hipSuccess) return e;
   return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Hkv, N, d, scale, flags, window, softcap,
-                    slopes, map, stream, false);
+                    slopes, map, stream, compact_map);
 }
 
 }  // namespace attn119

@@ -44,7 +44,8 @@ EXPORTS = ("attn_blockmap_bytes", "attn_blockmap_layout_of", "attn_blockmap_buil
            "attn_blockmap_status", "attn_check_args", "attn_check_args_gqa", "attn_fwd", "attn_fwd_gqa",
            "attn_fwd_kernel_name", "attn_status_str", "attn_varlen_workspace_bytes", "attn_varlen_prepare",
            "attn_fwd_varlen", "attn_fp8_quantize", "attn_bwd", "attn_bwd_gqa", "attn_bwd_gqa_noalloc",
-           "attn_fwd_rescale_counts", "attn_varlen_layout_of", "attn_bwd_varlen")
+           "attn_fwd_rescale_counts", "attn_varlen_layout_of", "attn_bwd_varlen", "attn_blockmap_compact_bytes",
+           "attn_blockmap_compact_layout_of", "attn_blockmap_build_compact")
 
 
 class AttnError(RuntimeError):
@@ -88,6 +89,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_blockmap_layout_of.restype = i32
     lib.attn_blockmap_build.argtypes = [i32, i32, ctypes.POINTER(attn_mask), vp, sz, vp]
     lib.attn_blockmap_build.restype = i32
+    lib.attn_blockmap_compact_bytes.argtypes = [i32, i32, ctypes.POINTER(attn_mask), ctypes.POINTER(sz)]
+    lib.attn_blockmap_compact_bytes.restype = i32
+    lib.attn_blockmap_compact_layout_of.argtypes = [i32, i32, ctypes.POINTER(attn_blockmap_layout)]
+    lib.attn_blockmap_compact_layout_of.restype = i32
+    lib.attn_blockmap_build_compact.argtypes = [i32, i32, ctypes.POINTER(attn_mask), vp, sz, vp]
+    lib.attn_blockmap_build_compact.restype = i32
     lib.attn_blockmap_status.argtypes = [vp, sz, vp]
     lib.attn_blockmap_status.restype = i32
     lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, ctypes.POINTER(attn_mask),
@@ -194,6 +201,26 @@ def attn_blockmap_build(B: int, N: int, mask: Optional[attn_mask], blockmap, str
     _check(load().attn_blockmap_build(B, N, ctypes.byref(mask) if mask else None, _ptr(blockmap),
                                       blockmap.numel() * blockmap.element_size(), _stream(stream)),
            "attn_blockmap_build")
+
+
+def attn_blockmap_compact_bytes(B: int, N: int, mask: Optional[attn_mask] = None) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().attn_blockmap_compact_bytes(B, N, ctypes.byref(mask) if mask else None, ctypes.byref(out)),
+           "attn_blockmap_compact_bytes")
+    return out.value
+
+
+def attn_blockmap_compact_layout_of(B: int, N: int) -> dict:
+    lay = attn_blockmap_layout()
+    _check(load().attn_blockmap_compact_layout_of(B, N, ctypes.byref(lay)), "attn_blockmap_compact_layout_of")
+    return {n: getattr(lay, n) for n, _ in attn_blockmap_layout._fields_}
+
+
+def attn_blockmap_build_compact(B: int, N: int, mask: Optional[attn_mask], blockmap, stream=None) -> None:
+    """Builds the compact block map (no class and list sections) into `blockmap`."""
+    _check(load().attn_blockmap_build_compact(B, N, ctypes.byref(mask) if mask else None, _ptr(blockmap),
+                                              blockmap.numel() * blockmap.element_size(), _stream(stream)),
+           "attn_blockmap_build_compact")
 
 
 def attn_blockmap_status(blockmap, stream=None) -> int:
@@ -350,12 +377,10 @@ def attn_bwd_gqa_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, scale: float, mas
 
 def read_blockmap(blockmap, B: int, N: int, compact: bool = False) -> dict:
     """Splits a block map copied back to the host into its sections (numpy); the compact
-    form (a packed batch's workspace, B = 1) has no "cls" and "idx" (None)."""
+    form has no "cls" and "idx" (None)."""
     raw = blockmap.detach().cpu().numpy() if hasattr(blockmap, "detach") else np.asarray(blockmap)
     raw = raw.view(np.uint8)
-    if compact:
-        assert B == 1
-    lay = attn_varlen_layout_of(N) if compact else attn_blockmap_layout_of(B, N)
+    lay = attn_blockmap_compact_layout_of(B, N) if compact else attn_blockmap_layout_of(B, N)
     nb = (N + 127) // 128
     hdr = raw[:64].view(np.int32)
 

@@ -160,10 +160,12 @@ typedef struct attn_fp8 {
  *                                       header), equal work in increasing e; without it the
  *                                       identity 0 .. B*nqb-1
  *
- * The compact form, inside the workspace of a packed batch (attn_varlen_prepare), has
- * B = 1, header.compact = 1 and the sections above without cls and idx, so that it
- * grows as O(N) rather than O(N^2 / 128^2) (attn_varlen_layout_of gives its offsets,
- * with cls = idx = 0).  No kernel needs those two sections: every query row's visible
+ * The compact form (attn_blockmap_compact_bytes, _layout_of, _build_compact; also the map
+ * inside the workspace of a packed batch, attn_varlen_prepare) has header.compact = 1 and
+ * the sections above without cls and idx, so that it grows as O(N) rather than
+ * O(B N^2 / 128^2) (its layout has cls = idx = 0).  Every call that takes a block map
+ * takes either form and tells them apart by the byte count (the general form is always
+ * larger).  No kernel needs those two sections: every query row's visible
  * keys form one interval [row_lo, row_hi] whose ends never decrease from row to row (and
  * likewise every key's rows [col_lo, col_hi]), so a query block's non-empty and FULL key
  * blocks follow from the intervals of its first and last rows, and a key block's query
@@ -189,6 +191,13 @@ attn_status attn_blockmap_bytes(int32_t B, int32_t N, const attn_mask* mask, siz
 
 /* Byte offset of every section of the block-map workspace.  Host only. */
 attn_status attn_blockmap_layout_of(int32_t B, int32_t N, attn_blockmap_layout* layout);
+
+/* The same three for the compact form (no cls and idx sections: O(B N) bytes); its
+ * sections hold the same values as the general form's. */
+attn_status attn_blockmap_compact_bytes(int32_t B, int32_t N, const attn_mask* mask, size_t* bytes);
+attn_status attn_blockmap_compact_layout_of(int32_t B, int32_t N, attn_blockmap_layout* layout);
+attn_status attn_blockmap_build_compact(int32_t B, int32_t N, const attn_mask* mask, void* map, size_t bytes,
+                                        void* stream);
 
 /*
  * Builds the block map for (B, N, mask) into `map` (device, `bytes` bytes, as

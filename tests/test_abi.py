@@ -56,6 +56,30 @@ def test_blockmap_layout(L):
         L.attn_blockmap_bytes(1, 300, L.make_mask(L.ATTN_WINDOW, window=0))
 
 
+def test_compact_blockmap_layout_and_either_form_accepted(L):
+    """The compact form: the general layout without cls and idx, O(B N) bytes; every call
+    that takes a map accepts either form (told apart by the byte count) and nothing else."""
+    full, comp = L.attn_blockmap_layout_of(2, 300), L.attn_blockmap_compact_layout_of(2, 300)
+    assert comp["cls"] == 0 and comp["idx"] == 0 and comp["counts"] == 256
+    names = ["counts", "row_lo", "row_hi", "col_lo", "col_hi", "pairs", "status", "order", "total"]
+    for a, b in zip(names, names[1:]):
+        assert comp[a] < comp[b] and comp[b] % 256 == 0
+        if a != "counts":
+            assert comp[b] - comp[a] == full[b] - full[a]
+    m = L.make_mask(L.ATTN_CAUSAL | L.ATTN_DOCUMENT, doc_id=P)
+    assert L.attn_blockmap_compact_bytes(2, 300, m) == comp["total"] < L.attn_blockmap_bytes(2, 300, m)
+    for B, N in ((1, 1), (3, 129), (1, 1 << 20)):
+        assert L.attn_blockmap_compact_bytes(B, N) < L.attn_blockmap_bytes(B, N)
+    lib = L.load()
+    chk = lambda nbytes: lib.attn_check_args(P, P, P, P, P, 2, 4, 300, 128, 0.1, 0, ctypes.byref(m), P, nbytes,
+                                             None, 8.0)
+    assert chk(full["total"]) == L.ATTN_OK and chk(comp["total"]) == L.ATTN_OK
+    for bad in (comp["total"] - 256, comp["total"] + 256, full["total"] - 256, 0):
+        assert chk(bad) == L.ATTN_ERR_BAD_BLOCKMAP
+    build = lambda nbytes: lib.attn_blockmap_build_compact(2, 300, ctypes.byref(m), P, nbytes, None)
+    assert build(full["total"]) == L.ATTN_ERR_BAD_BLOCKMAP
+
+
 P = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced by validation
 
 
