@@ -231,6 +231,7 @@ attn_status attn_blockmap_build_compact(int32_t B, int32_t N, const attn_mask* m
                                         void* stream) {
   return build_map(B, N, mask, map, bytes, true, stream);
 }
+
 attn_status attn_blockmap_status(const void* map, size_t bytes, void* stream) {
   if (!map || bytes < 256) return ATTN_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ATTN_ERR_HIP;
@@ -472,27 +473,12 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
   if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
   const attn_mask m = varlen_mask(mask, workspace, total);
-  return fwd_impl(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace, varlen_doc_offset(total), fp8,
-                  rescale_tau, nullptr, stream);
+  return attn_fwd_gqa(q, k, v, o, lse, 1, H, H_kv, total, d, scale, dtype, &m, workspace,
+                      varlen_doc_offset(total), fp8, rescale_tau, stream);
 }
 
 attn_status attn_varlen_layout_of(int32_t total, attn_blockmap_layout* layout) {
-  if (!layout) return ATTN_ERR_INVALID_ARG;
-  const attn_status st = check_shape(1, total);
-  if (st != ATTN_OK) return st;
-  const MapLayout m = map_layout(1, total, true);
-  layout->cls = m.cls;
-  layout->counts = m.counts;
-  layout->idx = m.idx;
-  layout->row_lo = m.row_lo;
-  layout->row_hi = m.row_hi;
-  layout->col_lo = m.col_lo;
-  layout->col_hi = m.col_hi;
-  layout->pairs = m.pairs;
-  layout->status = m.status;
-  layout->order = m.order;
-  layout->total = m.total;
-  return ATTN_OK;
+  return layout_of(1, total, true, layout);
 }
 
 attn_status attn_fp8_quantize(const void* x, void* codes, float* scales, int32_t B, int32_t H, int32_t N,
