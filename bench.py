@@ -488,8 +488,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path would "
-              f"shard over (b, h) heads with no communication.",
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); the attention pass "
+              f"would shard over (b, h) heads with no communication.",
               file=sys.stderr)
         return 2
 
