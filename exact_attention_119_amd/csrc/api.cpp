@@ -501,7 +501,6 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
   attn_status st = attn_check_args_gqa(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, H_kv, N, d,
                                        scale, ATTN_BF16, mask, blockmap, blockmap_bytes, nullptr, 8.f);
   if (st != ATTN_OK) return st;
-  if (positional(mask) && !blockmap) return ATTN_ERR_BAD_BLOCKMAP;  // the backward kernels walk the map
   if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(delta) & 3u))
@@ -524,7 +523,6 @@ attn_status attn_bwd_gqa_noalloc(const void* q, const void* k, const void* v, co
   attn_status st = attn_check_args_gqa(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, H_kv, N, d,
                                        scale, ATTN_BF16, mask, blockmap, blockmap_bytes, nullptr, 8.f);
   if (st != ATTN_OK) return st;
-  if (positional(mask) && !blockmap) return ATTN_ERR_BAD_BLOCKMAP;
   if (!dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_INVALID_ARG;
   if ((uint64_t)B * (uint64_t)H * (uint64_t)N > (uint64_t)bwd_scratch_rows()) return ATTN_ERR_INVALID_ARG;

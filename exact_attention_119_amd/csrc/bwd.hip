@@ -208,6 +208,22 @@ __device__ __forceinline__ float head_slope(const BwdArgs& a, int h) {
   return a.alibi_slopes ? a.alibi_slopes[h] : exp2_(a.alibi_exp * (float)(h + 1));
 }
 
+// Causal and window masks without documents, when the call passes no map: the keys row q
+// sees, [row_lo_of(q), row_hi_of(q)], and the rows that see key k, [col_lo_of(k),
+// col_hi_of(k)], from the flags (the values the map's interval sections would hold)
+__device__ __forceinline__ int row_lo_of(const BwdArgs& a, int q) {
+  return (a.flags & kWindow) ? max(0, q - (a.window - 1)) : 0;
+}
+__device__ __forceinline__ int row_hi_of(const BwdArgs& a, int q) {
+  return (a.flags & kCausal) ? q : ((a.flags & kWindow) ? min(a.N - 1, q + (a.window - 1)) : a.N - 1);
+}
+__device__ __forceinline__ int col_lo_of(const BwdArgs& a, int k) {
+  return (a.flags & kCausal) ? k : ((a.flags & kWindow) ? max(0, k - (a.window - 1)) : 0);
+}
+__device__ __forceinline__ int col_hi_of(const BwdArgs& a, int k) {
+  return (a.flags & kWindow) ? min(a.N - 1, k + (a.window - 1)) : a.N - 1;
+}
+
 // header of the block map matches the call, and (document masks) no batch row is
 // marked invalid; uniform over the workgroup
 __device__ bool map_invalid(const BwdArgs& a, int b) {
@@ -300,17 +316,29 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
   // itself inside): non-empty are ua .. ub, FULL fa .. fb (inside [lo(r1), hi(r0)], 128
   // rows and keys), PARTIAL the pl blocks left of the FULL range and those right of it;
   // step order: the PARTIAL blocks ascending, then the FULL ones (the map's lists are not
-  // read).
+  // read).  Without a map (causal and window masks) the intervals follow from the flags.
   int ua = 0, fa = 0, fb = -1, pl = 0;
   bool invalid = false;
   if constexpr (MASKED) {
-    invalid = map_invalid(a, b);
+    const bool derive = a.map == nullptr;
+    if (!derive) invalid = map_invalid(a, b);
     {
-      typedef const __attribute__((address_space(4))) int cint4;
-      cint4* rlo = (cint4*)(a.map + a.lay.row_lo) + (size_t)b * N;
-      cint4* rhi = (cint4*)(a.map + a.lay.row_hi) + (size_t)b * N;
       const int r0 = qb * 128, r1 = min(N, r0 + 128) - 1;
-      const int lo0 = rlo[r0], lo1 = rlo[r1], hi0 = rhi[r0], hi1 = rhi[r1];
+      int lo0, lo1, hi0, hi1;
+      if (derive) {
+        lo0 = row_lo_of(a, r0);
+        lo1 = row_lo_of(a, r1);
+        hi0 = row_hi_of(a, r0);
+        hi1 = row_hi_of(a, r1);
+      } else {
+        typedef const __attribute__((address_space(4))) int cint4;
+        cint4* rlo = (cint4*)(a.map + a.lay.row_lo) + (size_t)b * N;
+        cint4* rhi = (cint4*)(a.map + a.lay.row_hi) + (size_t)b * N;
+        lo0 = rlo[r0];
+        lo1 = rlo[r1];
+        hi0 = rhi[r0];
+        hi1 = rhi[r1];
+      }
       ua = min(max(lo0 >> 7, 0), nqb - 1);
       const int ub = hi1 < lo0 ? ua - 1 : min(hi1 >> 7, nqb - 1);
       fa = max(ua, (lo1 + 127) >> 7);
@@ -322,8 +350,8 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const BwdArgs a) {
       nblk = invalid ? 0 : nfull + npart;
     }
     if (qvalid) {
-      lo_q = ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
-      hi_q = ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
+      lo_q = derive ? row_lo_of(a, qrow) : ((const int*)(a.map + a.lay.row_lo))[(size_t)b * N + qrow];
+      hi_q = derive ? row_hi_of(a, qrow) : ((const int*)(a.map + a.lay.row_hi))[(size_t)b * N + qrow];
     }
   }
   int2 troff[NDB];
@@ -482,7 +510,10 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     vf[c] = kvalid ? *(const bf16x8*)(a.v + koff + 16 * c + 8 * hh) : bf16x8{};
   }
   bool invalid = false;
-  if constexpr (MASKED) invalid = map_invalid(a, b);
+  const bool derive = MASKED && a.map == nullptr;  // causal and window masks without a map
+  if constexpr (MASKED) {
+    if (!derive) invalid = map_invalid(a, b);
+  }
   int2 troff[NDB];
   const int rsw = lds_swz<D>(l32);
 #pragma unroll
@@ -505,11 +536,22 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   // list sections are not read.)
   int qa = 0, qz = nqb - 1, qfa = 0, qfz = nqb - 1;
   if constexpr (MASKED) {
-    typedef const __attribute__((address_space(4))) int cint4;
-    cint4* clo = (cint4*)(a.map + a.lay.col_lo) + (size_t)b * N;
-    cint4* chi = (cint4*)(a.map + a.lay.col_hi) + (size_t)b * N;
     const int k0 = kb * 128, k1 = min(N, k0 + 128) - 1;
-    const int lo0 = clo[k0], lo1 = clo[k1], hi0 = chi[k0], hi1 = chi[k1];
+    int lo0, lo1, hi0, hi1;
+    if (derive) {
+      lo0 = col_lo_of(a, k0);
+      lo1 = col_lo_of(a, k1);
+      hi0 = col_hi_of(a, k0);
+      hi1 = col_hi_of(a, k1);
+    } else {
+      typedef const __attribute__((address_space(4))) int cint4;
+      cint4* clo = (cint4*)(a.map + a.lay.col_lo) + (size_t)b * N;
+      cint4* chi = (cint4*)(a.map + a.lay.col_hi) + (size_t)b * N;
+      lo0 = clo[k0];
+      lo1 = clo[k1];
+      hi0 = chi[k0];
+      hi1 = chi[k1];
+    }
     qa = min(max(lo0 >> 7, 0), nqb);
     qz = hi1 < lo0 ? -1 : min(hi1 >> 7, nqb - 1);
     qfa = max(qa, (lo1 + 127) >> 7);
@@ -552,10 +594,13 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
   // Requests a step's Q and dO rows into buffer buf, and its per-row values into the
   // per-row arrays: one 256-byte load per wave (wave 0: the LSE, 1: D, 2 and 3: the first
   // and last visible key; without a positional mask waves 2 and 3 load the LSE and D
-  // again into the interval arrays, which nothing reads), so every wave has 2 LPW + 1
-  // loads in flight per step.  Rows past N read as zero (Q, dO, LSE, D and the interval
-  // [0, 0]): such a row adds nothing to any gradient.
+  // again into the interval arrays, which nothing reads; with a positional mask but no
+  // map waves 2 and 3 load them into arrays of their own that nothing reads, and write
+  // the intervals from the flags), so every wave has 2 LPW + 1 loads in flight per step.
+  // Rows past N read as zero (Q, dO, LSE, D and the interval [0, 0]): such a row adds
+  // nothing to any gradient.
   constexpr int LPS = 2 * LPW + 1;
+  __shared__ __attribute__((aligned(16))) int unread_s[2][NBUF][BM];
   auto fetch = [&](int hq, int qb, int sub, int buf) {
     const int bh = b * a.H + kvh * grp + hq;
     const int q0 = qb * 128 + sub * BM;
@@ -564,12 +609,18 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(const BwdArgs a) {
     const float* dl_src = a.delta + (size_t)bh * N + q0;
     const void* src = (wave & 1) ? (const void*)dl_src : (const void*)lse_src;
     if constexpr (MASKED) {
-      if (wave >= 2)
+      if (wave >= 2 && !derive)
         src = (const int*)(a.map + ((wave & 1) ? a.lay.row_hi : a.lay.row_lo)) + (size_t)b * N + q0;
     }
     lds_u8* dst = wave == 0 ? (lds_u8*)lse_s[buf] : wave == 1 ? (lds_u8*)dl_s[buf]
                 : wave == 2 ? (lds_u8*)lo_s[buf] : (lds_u8*)hi_s[buf];
+    if (derive && wave >= 2) dst = (lds_u8*)unread_s[wave & 1][buf];
     dma_to_lds<4>(dma_rsrc(src, rows * 4), dst, 4 * lane);
+    if (derive && wave >= 2) {  // row q0 + lane of the step (BM = 64 rows, one per lane)
+      const int q = q0 + lane;
+      const int v = q < N ? ((wave & 1) ? row_hi_of(a, q) : row_lo_of(a, q)) : 0;
+      ((wave & 1) ? hi_s[buf] : lo_s[buf])[lane] = v;
+    }
     const int bytes = rows * ROWB;
     const u32x4 qrs = dma_rsrc((const unsigned char*)a.q + ((size_t)bh * N + q0) * ROWB, bytes);
     const u32x4 grs = dma_rsrc((const unsigned char*)a.dout + ((size_t)bh * N + q0) * ROWB, bytes);
@@ -901,7 +952,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   a.compact = compact_map ? 1 : 0;
   a.heavy = (flags & kCausal) && !(flags & kDocument);
   const bool masked = (flags & kPositional) != 0;
-  if (masked && !map) return hipErrorInvalidValue;
+  if (masked && !map && (flags & kDocument)) return hipErrorInvalidValue;  // (causal/window: derived)
   return d == 128 ? bwd::launch_d<128>(a, masked, stream) : bwd::launch_d<64>(a, masked, stream);
 }
 

@@ -369,7 +369,9 @@ attn_status attn_fp8_quantize(const void* x, void* codes, float* scales, int32_t
  *   q, o, dout, dq : bf16 [B][H][N][d];  k, v, dk, dv : bf16 [B][H_kv][N][d];
  *   lse  : fp32 [B][H][N], the forward call's output for the same q, k, v;
  *   delta: fp32 [B][H][N] caller-owned scratch, overwritten with D;
- *   mask, blockmap: as for the forward call (positional masks need the block map).
+ *   mask, blockmap: as for the forward call (a document mask needs the block map, in
+ *           either form; causal and window masks may pass none: the kernels then take
+ *           the key intervals from the flags).
  * Deterministic (no atomics): equal inputs give equal bits.  Errors as attn_check_args_gqa,
  * plus ATTN_ERR_INVALID_ARG for a null or misaligned dout, dq, dk, dv (16 B) or delta (4 B).
  * attn_bwd is the case H_kv = H.

@@ -156,3 +156,27 @@ def test_varlen_against_oracle_and_document_mask(mix, variant):
     ref = oracle.attention_bwd_ref(Q, K, V, oracle.decode_bf16(dO), scale=p.scale, flags=p.flags | DOC,
                                    window=p.window, softcap=p.softcap, doc_id=ids[None], alibi_slopes=p.alibi_slopes)
     _check(got, ref, f"bwd varlen {mix} {variant}")
+
+
+@pytest.mark.parametrize("N", [7, 300, 1500])
+@pytest.mark.parametrize("variant", ["causal", "window", "bidir_window", "alibi_causal", "cfg3like"])
+def test_without_map_bit_identical(variant, N):
+    """Causal and window masks without a block map: the kernels take the intervals from
+    the flags, and every gradient is bit for bit the one the map gives."""
+    p = W.make_problem(2, 4, N, 128, seed=(33, N, sorted(VARIANTS).index(variant)), H_kv=2, **VARIANTS[variant])
+    dO = W.make_dout(p, seed=33)
+    _announce("bwd without map", variant, N)
+    dp = WD.to_device(p)
+    WD.step(dp)
+    dout = torch.from_numpy(dO.view(np.int16)).cuda().view(torch.bfloat16)
+    res = []
+    for mp in (dp.blockmap, None):
+        outs = [torch.full_like(t, float("nan")) for t in (dp.q, dp.k, dp.v)] + [torch.empty_like(dp.lse)]
+        L.attn_bwd_gqa(dp.q, dp.k, dp.v, dp.o, dp.lse, dout, *outs, scale=p.scale, mask=dp.mask, blockmap=mp)
+        res.append(outs)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(*res):
+        assert not torch.isnan(a_.float()).any()
+        va = a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_.view(torch.int32)
+        vb = b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_.view(torch.int32)
+        assert torch.equal(va, vb)
