@@ -158,12 +158,13 @@ def test_varlen_against_oracle_and_document_mask(mix, variant):
     _check(got, ref, f"bwd varlen {mix} {variant}")
 
 
-@pytest.mark.parametrize("N", [7, 300, 1500])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 300, 1500])
 @pytest.mark.parametrize("variant", ["causal", "window", "bidir_window", "alibi_causal", "cfg3like"])
-def test_without_map_bit_identical(variant, N):
+def test_without_map_bit_identical(variant, N, d):
     """Causal and window masks without a block map: the kernels take the intervals from
     the flags, and every gradient is bit for bit the one the map gives."""
-    p = W.make_problem(2, 4, N, 128, seed=(33, N, sorted(VARIANTS).index(variant)), H_kv=2, **VARIANTS[variant])
+    p = W.make_problem(2, 4, N, d, seed=(33, N, sorted(VARIANTS).index(variant)), H_kv=2, **VARIANTS[variant])
     dO = W.make_dout(p, seed=33)
     _announce("bwd without map", variant, N)
     dp = WD.to_device(p)
