@@ -531,7 +531,10 @@ def main(argv=None):
     log(f"bench: {name}; generating done, staging to HBM")
     from exact_attention_119_amd import lib as L
     pv_mode = {"f16": L.ATTN_PV_F16, "e4m3": L.ATTN_PV_E4M3, "fp4": L.ATTN_PV_FP4}[args.pv]
-    dp = WD.to_device(p, qk_mode=L.ATTN_QK_E4M3 if args.qk8 else L.ATTN_QK_BF16, pv_mode=pv_mode)
+    # (the forward pass reads only the map's interval, status and order sections: the compact
+    # form, without the class and list sections the backward tests compare, is what it needs)
+    dp = WD.to_device(p, qk_mode=L.ATTN_QK_E4M3 if args.qk8 else L.ATTN_QK_BF16, pv_mode=pv_mode,
+                      compact_map=True)
     pairs = visible_pairs(p)
     flop_per_step = 4.0 * p.d * p.H * pairs
     stream = torch.cuda.current_stream()
@@ -601,7 +604,7 @@ def main(argv=None):
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": name, "B": p.B, "H": p.H, "N": p.N, "d": p.d, "visible_pairs": pairs,
                    "unmasked_flop_per_step": flop_per_step, "rescale_tau": args.tau, "input_dtype": dtype,
-                   "step": "block-map build + forward pass" if map_in_step else
+                   "step": "block-map build (compact form) + forward pass" if map_in_step else
                            ("forward pass (block lists derived from the mask in the kernel)" if dp.blockmap is not None
                             else "forward pass"), "parallelism": "single GPU",
                    "warmup_run": {"steps": nwarm, "seconds": round(twarm, 3)},

@@ -31,6 +31,7 @@ class DeviceProblem:
     blockmap: Optional[torch.Tensor]  # the block map, or the variable-length workspace
     keep: tuple  # device tensors the mask / fp8 structs point to
     cu_seqlens: Optional[torch.Tensor] = None  # packed variable-length batch
+    compact_map: bool = False  # the block map in its compact form (no class and list sections)
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -38,7 +39,9 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 
 def to_device(p: Problem, device="cuda", pv_mode: int = L.ATTN_PV_F16,
-              qk_mode: int = L.ATTN_QK_BF16) -> DeviceProblem:
+              qk_mode: int = L.ATTN_QK_BF16, compact_map: bool = False) -> DeviceProblem:
+    """compact_map: allocate and build the block map in its compact form (every call takes
+    either form; packed batches always use it)."""
     if p.dtype == "bf16":
         q, k, v = (_dev(x.view(np.int16), device).view(torch.bfloat16) for x in (p.q, p.k, p.v))
         dtype, fp8, keep = L.ATTN_BF16, None, ()
@@ -59,18 +62,19 @@ def to_device(p: Problem, device="cuda", pv_mode: int = L.ATTN_PV_F16,
         cu = _dev(p.cu_seqlens, device)
         nbytes = L.attn_varlen_workspace_bytes(p.N, mask)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        return DeviceProblem(p, q, k, v, o, lse, dtype, mask, fp8, ws, keep, cu)
+        return DeviceProblem(p, q, k, v, o, lse, dtype, mask, fp8, ws, keep, cu, compact_map=True)
     if p.flags & L.POSITIONAL:
-        nbytes = L.attn_blockmap_bytes(p.B, p.N, mask)
+        nbytes = (L.attn_blockmap_compact_bytes if compact_map else L.attn_blockmap_bytes)(p.B, p.N, mask)
         blockmap = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return DeviceProblem(p, q, k, v, o, lse, dtype, mask, fp8, blockmap, keep)
+    return DeviceProblem(p, q, k, v, o, lse, dtype, mask, fp8, blockmap, keep, compact_map=compact_map)
 
 
 def build_map(dp: DeviceProblem, stream=None) -> None:
     if dp.cu_seqlens is not None:
         L.attn_varlen_prepare(dp.cu_seqlens, dp.p.N, dp.mask, dp.blockmap, stream)
     elif dp.blockmap is not None:
-        L.attn_blockmap_build(dp.p.B, dp.p.N, dp.mask, dp.blockmap, stream)
+        build = L.attn_blockmap_build_compact if dp.compact_map else L.attn_blockmap_build
+        build(dp.p.B, dp.p.N, dp.mask, dp.blockmap, stream)
 
 
 def needs_map(dp: DeviceProblem) -> bool:
