@@ -72,3 +72,26 @@ def test_compact_map_sections_and_passes(case, N):
     assert not torch.isnan(o1).any() and _same_bits(o1, o2) and _same_bits(l1, l2)
     for a, b in zip(g1, g2):
         assert not torch.isnan(a.float()).any() and _same_bits(a, b)
+
+
+@pytest.mark.parametrize("case", ["doc_causal", "doc_window_softcap"])
+def test_compact_map_fp8_forward(case):
+    """The fp8 forward pass (e4m3 inputs with block scales) with the compact map equals
+    the pass with the general map bit for bit."""
+    kw = CASES[case]
+    p = W.make_problem(2, 4, 700, 128, dtype="fp8", n_outliers=4, seed=(41, sorted(CASES).index(case)), H_kv=2,
+                       doc_len_range=(1, 300), **kw)
+    print("CASE compact map fp8", case, flush=True)
+    dp = WD.to_device(p)
+    WD.build_map(dp)
+    comp = torch.empty(L.attn_blockmap_compact_bytes(p.B, p.N, dp.mask), dtype=torch.uint8, device="cuda")
+    L.attn_blockmap_build_compact(p.B, p.N, dp.mask, comp)
+    res = []
+    for mp in (dp.blockmap, comp):
+        o, lse = torch.full_like(dp.o, float("nan")), torch.full_like(dp.lse, float("nan"))
+        L.attn_fwd_gqa(dp.q, dp.k, dp.v, o, lse, scale=p.scale, dtype=dp.dtype, mask=dp.mask, blockmap=mp,
+                       fp8=dp.fp8)
+        res.append((o, lse))
+    torch.cuda.synchronize()
+    (o1, l1), (o2, l2) = res
+    assert not torch.isnan(o1).any() and _same_bits(o1, o2) and _same_bits(l1, l2)
