@@ -14,8 +14,8 @@
 
 namespace attn119 {
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
-                           const int32_t* doc_id, const int32_t* cu, int nseq, bool compact, hipStream_t stream);
-hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t* doc, hipStream_t stream);
+                           const int32_t* doc_id, const int32_t* cu, int nseq, int32_t* ids, bool compact,
+                           hipStream_t stream);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, float* delta, int B, int H, int Hkv, int N, int d, float scale,
                       uint32_t flags, int window, float softcap, const float* slopes, const void* map,
@@ -158,7 +158,8 @@ attn_status build_map(int32_t B, int32_t N, const attn_mask* mask, void* map, si
   const uint32_t flags = mask ? mask->flags : 0u;
   const int window = (mask && (flags & ATTN_WINDOW)) ? mask->window : 0;
   const int32_t* doc = (mask && (flags & ATTN_DOCUMENT)) ? mask->doc_id : nullptr;
-  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, compact, (hipStream_t)stream) !=
+  if (launch_blockmap((unsigned char*)map, B, N, flags, window, doc, nullptr, 0, nullptr, compact,
+                      (hipStream_t)stream) !=
       hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -455,9 +456,11 @@ attn_status attn_varlen_prepare(const int32_t* cu_seqlens, int32_t nseq, int32_t
   if (bytes != need) return ATTN_ERR_BAD_BLOCKMAP;
   const attn_mask m = varlen_mask(mask, workspace, total);
   const hipStream_t s = (hipStream_t)stream;
-  if (launch_varlen_doc_ids(cu_seqlens, nseq, total, (int32_t*)m.doc_id, s) != hipSuccess) return ATTN_ERR_HIP;
   const int window = (m.flags & ATTN_WINDOW) ? m.window : 0;
-  if (launch_blockmap((unsigned char*)workspace, 1, total, m.flags, window, m.doc_id, cu_seqlens, nseq, true, s) !=
+  // (the map kernel writes the sequence ids as it builds the map; the work order follows
+  // in a second launch)
+  if (launch_blockmap((unsigned char*)workspace, 1, total, m.flags, window, nullptr, cu_seqlens, nseq,
+                      (int32_t*)m.doc_id, true, s) !=
       hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;

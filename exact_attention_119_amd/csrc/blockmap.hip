@@ -22,6 +22,8 @@
 // intervals together cover [lo(r0), hi(r1)] without a gap (the non-empty key blocks are
 // those that meet it), and a key block is FULL exactly when it lies inside
 // [lo(r1), hi(r0)] with 128 keys and the query block has 128 rows.
+// For a packed batch the rows' sequences come from the offsets, and the kernel also
+// writes the sequence id of every token to the workspace.
 // A second launch, for document masks only, fills the work-order section: the
 // (batch row, query block) pairs heaviest-first by the work of their block lists (other
 // masks keep the identity order the first launch writes; their work is known from the
@@ -41,6 +43,7 @@ struct MapArgs {
   int window;
   const int32_t* cu;  // packed variable-length batch (B = 1): offsets [nseq + 1], else null
   int nseq;
+  int32_t* ids;       // packed batch: the sequence id of every token, written here
   int compact;        // 1: the compact form (no class and list sections)
 };
 
@@ -109,7 +112,25 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
   __shared__ int s_doc[kBlock + 1];
   __shared__ int s_run_f[4], s_run_g[4];
   int first0 = 0, last1 = N - 1, run_first = 0, run_last = 0;
-  if (a.flags & kDocument) {
+  // Packed batches: a row's sequence is the number of interior offsets cu[1..nseq-1] at
+  // or below it (a binary search; every read stays inside cu whatever the values), its
+  // bounds cu[id] and cu[id + 1] - 1; the ids go to the workspace from here.  Offsets out
+  // of order give wrong bounds, and the check below marks the batch row invalid.
+  int cu_ds = 0, cu_de = N - 1;
+  if (a.cu) {
+    if (tid < nrows) {
+      const int q = q0 + tid;
+      int lo = 1, hi = a.nseq;  // first index in [1, nseq) with cu[index] > q
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu[mid] <= q) lo = mid + 1; else hi = mid;
+      }
+      const int sq = lo - 1;
+      a.ids[q] = sq;
+      cu_ds = a.cu[sq];
+      cu_de = a.cu[sq + 1] - 1;
+    }
+  } else if (a.flags & kDocument) {
     const int32_t* drow = a.doc_id + (size_t)b * N;
     const int step0 = (N + 255) / 256;
     const int pv0 = tid * step0 < N ? drow[tid * step0] : 0;
@@ -158,9 +179,12 @@ __global__ void __launch_bounds__(256) blockmap_kernel(MapArgs a) {
         chi = min(chi, q + (a.window - 1));
       }
       if (a.flags & kDocument) {
-        if (q + 1 < N && s_doc[tid + 1] < s_doc[tid]) bad = 1;
-        const int ds = run_first == 0 ? first0 : q0 + run_first;
-        const int de = run_last == nrows - 1 ? last1 : q0 + run_last;
+        int ds = cu_ds, de = cu_de;
+        if (!a.cu) {
+          if (q + 1 < N && s_doc[tid + 1] < s_doc[tid]) bad = 1;
+          ds = run_first == 0 ? first0 : q0 + run_first;
+          de = run_last == nrows - 1 ? last1 : q0 + run_last;
+        }
         lo = max(lo, ds);
         hi = min(hi, de);
         clo = max(clo, ds);
@@ -306,31 +330,9 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* counts, int32
   if (e < M) order[rank] = e;
 }
 
-// Packed variable-length batch: token t belongs to sequence i when cu[i] <= t < cu[i+1].
-// The id is the number of interior boundaries cu[1..nseq-1] at or below t (a binary
-// search; cu[0] and cu[nseq] are not read here).  Every read stays inside cu[1..nseq-1]
-// whatever the values; the block-map kernel checks that the offsets are in order and
-// marks the batch row invalid when they are not.
-__global__ void __launch_bounds__(256) varlen_doc_ids_kernel(const int32_t* cu, int nseq, int total,
-                                                             int32_t* doc) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  int lo = 1, hi = nseq;  // first index in [1, nseq) with cu[index] > t
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid + 1; else hi = mid;
-  }
-  doc[t] = lo - 1;
-}
-
-hipError_t launch_varlen_doc_ids(const int32_t* cu, int nseq, int total, int32_t* doc, hipStream_t stream) {
-  hipLaunchKernelGGL(varlen_doc_ids_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, cu, nseq, total,
-                     doc);
-  return hipGetLastError();
-}
-
 hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int window,
-                           const int32_t* doc_id, const int32_t* cu, int nseq, bool compact, hipStream_t stream) {
+                           const int32_t* doc_id, const int32_t* cu, int nseq, int32_t* ids, bool compact,
+                           hipStream_t stream) {
   MapArgs a;
   a.map = map;
   a.lay = map_layout(B, N, compact);
@@ -343,6 +345,7 @@ hipError_t launch_blockmap(unsigned char* map, int B, int N, uint32_t flags, int
   a.window = window;
   a.cu = cu;
   a.nseq = nseq;
+  a.ids = ids;
   hipLaunchKernelGGL(blockmap_kernel, dim3(a.nb, B), dim3(256), 0, stream, a);
   if (a.flags & kDocument) {
     const int M = B * a.nb;
