@@ -262,3 +262,16 @@ def test_noalloc_backward_rejects_more_rows_than_its_scratch(L):
     assert st == L.ATTN_ERR_INVALID_ARG
     st = lib.attn_bwd_gqa_noalloc(P, P, P, P, P, None, P, P, P, 1, 4, 4, 300, 128, 0.1, None, None, 0, None)
     assert st == L.ATTN_ERR_INVALID_ARG
+
+
+def test_header_is_plain_c():
+    """include/attn119.h declares a C ABI: it compiles as C (and as C++) on its own."""
+    import shutil
+    import subprocess
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn119.h")
+    for cc, lang in (("gcc", "c"), ("g++", "c++")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not installed")
+        r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", "-x", lang, hdr],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
